@@ -1,0 +1,222 @@
+/*
+ * pa.h -- C ABI of a paged-KV-cache decode library for AMD Instinct MI355X (gfx950).
+ *
+ * Method (from the pages this library follows):
+ *   - "Paged Attention Explained: How LLMs Manage GPU Memory for Faster AI
+ *     Inference", section "How Paged Attention Works", Steps 1-5: the KV cache
+ *     is cut into fixed-size blocks of token slots, blocks are allocated on
+ *     demand, a per-request block table maps logical blocks to physical ones,
+ *     the attention kernel gathers K/V through that table, and finished
+ *     requests return their blocks.  Section "Why Does the KV Cache Consume So
+ *     Much Memory?" gives the size 2 * L * T * H_KV * D_head * B.
+ *   - "PagedAttention: paging the KV cache like an OS pages memory", section
+ *     "How it works": attention itself is standard causal attention (only the
+ *     storage layout changes); blocks are reference-counted and shared across
+ *     requests or decode branches, with block-granular copy-on-write.
+ *
+ * Conventions
+ *   - Every function returns PA_OK (0) or a negative pa_status unless noted;
+ *     pa_last_error() then holds a message (thread-local).  No C++ exception
+ *     crosses this boundary.
+ *   - Device buffers are owned by the caller (e.g. allocated by PyTorch); the
+ *     library never allocates or frees device memory.  "device" below means a
+ *     pointer into GPU memory, "host" a pointer into CPU memory.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  All
+ *     device work is enqueued asynchronously; nothing synchronises implicitly.
+ *   - A pool handle is not thread-safe: one thread at a time.
+ *   - Setting the environment variable PA_DEBUG=1 makes pa_write_kv and
+ *     pa_decode copy their index arguments to the host and validate them
+ *     (synchronising the stream) before launching.
+ *
+ * Pool layout in device memory (this library's own design; the pages fix
+ * only fixed-size blocks addressed through a table).  Element order, outer to
+ * inner:
+ *      [layer][block][kv_head][K, V][block_size x head_dim tile]
+ * so each (layer, block, kv_head) owns one contiguous run of
+ * 2 * block_size * head_dim elements, K tile first.  A tile is a sequence of
+ * 16-token sub-tiles: token slot t of a block lies in sub-tile t / 16 at row
+ * r = t % 16.  With E = 16 / sizeof(element) (8 for f16/bf16, 4 for f32),
+ * element (r, d) of a sub-tile is at
+ *      K:  ((d / 4E) * 64 + r + 16 * ((d % 4E) / E)) * E + d % E
+ *      V:  (((d / 16) / (E/4) * 64 + d % 16 + 16 * (r / 4)) * (E/4)
+ *            + (d / 16) % (E/4)) * 4 + r % 4
+ * This places every 16-byte chunk that one 64-lane wavefront loads for a
+ * Q.K^T or P.V step side by side (1 KiB per load instruction).  Token
+ * position p of a sequence with block table `tbl` is slot p % block_size of
+ * physical block tbl[p / block_size]; its global slot number (used by
+ * slot_mapping) is tbl[p / block_size] * block_size + p % block_size.
+ *
+ * Supported shapes: block_size a positive multiple of 16 (up to 256),
+ * head_dim 64 or 128, dtypes F32 / F16 / BF16, query heads per KV head
+ * G = num_q_heads / num_kv_heads with 1 <= G <= 16 (F32: G in {1, 2, 4, 8}).
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PA_OK = 0,
+  PA_ERR_INVALID_ARG = -1,      /* bad argument or precondition violated */
+  PA_ERR_OUT_OF_BLOCKS = -2,    /* pool exhausted; state left unchanged  */
+  PA_ERR_BUFFER_TOO_SMALL = -3, /* caller buffer smaller than required   */
+  PA_ERR_UNSUPPORTED = -4,      /* shape/dtype outside the list above    */
+  PA_ERR_HIP = -5               /* a HIP runtime call failed             */
+} pa_status;
+
+typedef enum { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 } pa_dtype;
+
+typedef struct {
+  int32_t num_layers;   /* L   */
+  int32_t num_blocks;   /* N   physical blocks per layer        */
+  int32_t block_size;   /* bs  token slots per block             */
+  int32_t num_kv_heads; /* H_KV */
+  int32_t head_dim;     /* D   */
+  int32_t dtype;        /* pa_dtype; B = 4 or 2 bytes per element */
+} pa_pool_desc;
+
+typedef struct pa_pool pa_pool;
+
+typedef struct {
+  int64_t num_blocks, free_blocks, used_blocks;
+  int64_t shared_blocks;  /* blocks with reference count > 1             */
+  int64_t cow_copies;     /* copy-on-write copies decided so far         */
+  int64_t live_seqs;
+  int64_t logical_tokens; /* sum of live sequence lengths                */
+  int64_t tail_slots;     /* sum over live sequences of blocks*bs - len  */
+} pa_stats;
+
+/* Library version string (static storage). */
+const char* pa_version(void);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char* pa_last_error(void);
+
+/* Bytes a pool needs: exactly 2 * L * (N * bs) * H_KV * D * B -- the KV-size
+ * estimate of "Why Does the KV Cache Consume So Much Memory?" with T = N * bs
+ * token slots.  Returns 0 for an invalid or unsupported descriptor. */
+size_t pa_pool_required_bytes(const pa_pool_desc* desc);
+
+/* Create a pool handle over caller-owned device memory `dev_buf` of
+ * `buf_bytes` (>= pa_pool_required_bytes, 256-byte aligned).  The library
+ * borrows the buffer for the handle's lifetime and does not touch its
+ * contents.  Host allocator state starts with every block free; blocks are
+ * handed out in the order `free_order[0], free_order[1], ...` (host array of
+ * N distinct ids, NULL = ascending ids).
+ * Errors: INVALID_ARG (NULL pointers, negative counts, block_size <= 0 --
+ * the error rules of the page's "Practical Example" -- misalignment, a
+ * free_order that is not a permutation), UNSUPPORTED, BUFFER_TOO_SMALL. */
+int pa_alloc_pool(const pa_pool_desc* desc, void* dev_buf, size_t buf_bytes,
+                  const int32_t* free_order, pa_pool** out);
+
+/* Destroy the handle and its host state.  Does not free dev_buf.  NULL is a
+ * no-op. */
+int pa_free(pa_pool* pool);
+
+/* Scatter new tokens' K and V rows into their cache slots ("cache updates",
+ * "Practical Example"; a new block only when the current one is full,
+ * "Real-World Consequences: Zero Fragmentation" of "PagedAttention and KV
+ * Cache Compression").
+ *   k, v          device [num_tokens, H_KV, D] contiguous, pool dtype
+ *   slot_mapping  device int32 [num_tokens]: global slot block*bs + offset,
+ *                 or -1 to skip the token.  Slots must be distinct; slots
+ *                 outside [0, N*bs) are skipped (reported under PA_DEBUG).
+ * Bit-exact copy.  Asynchronous on `stream`. */
+int pa_write_kv(pa_pool* pool, int layer, const void* k, const void* v,
+                const int32_t* slot_mapping, int num_tokens, void* stream);
+
+/* Device workspace bytes pa_decode needs for split-K partials (float32
+ * partial outputs plus running max and sum per query head and partition). */
+size_t pa_decode_workspace_bytes(const pa_pool* pool, int num_seqs, int num_q_heads,
+                                 int max_context_len, int partition_tokens);
+
+/* Single-token decode attention over the paged cache ("How Paged Attention
+ * Works", Step 4; standard attention per "How it works").  For sequence i,
+ * query head g and kv head h = g / (num_q_heads / H_KV):
+ *     out[i, g] = softmax_p(scale * q[i, g] . K_i[p, h]) . V_i[p, h],
+ *     p = 0 .. context_lens[i] - 1,
+ * where K_i/V_i are read through block_tables row i.  Contexts longer than
+ * `partition_tokens` are split into partitions whose softmax states are merged
+ * by log-sum-exp weighting.
+ *   q, out             device [num_seqs, num_q_heads, D], pool dtype,
+ *                      out written with round-to-nearest-even from float32
+ *   block_tables       device int32 [num_seqs, max_blocks_per_seq]; entries
+ *                      below ceil(ctx/bs) must be valid ids, later ones unread
+ *   context_lens       device int32 [num_seqs], 1 <= ctx <= max_blocks*bs
+ *   max_context_len    host value >= every context_lens[i] (sizes the grid)
+ *   scale              applied in float32 to the float32 dot products
+ *   partition_tokens   0 = automatic, else a multiple of block_size and of 16
+ *   workspace          device, >= pa_decode_workspace_bytes(...) bytes
+ * Asynchronous on `stream`; the result is ready when the stream reaches it. */
+int pa_decode(const pa_pool* pool, int layer, const void* q, int num_seqs, int num_q_heads,
+              const int32_t* block_tables, int max_blocks_per_seq,
+              const int32_t* context_lens, int max_context_len, float scale,
+              int partition_tokens, void* workspace, size_t ws_bytes, void* out,
+              void* stream);
+
+/* Copy whole blocks (every layer, head, K and V) for copy-on-write.
+ *   pairs  device int32 [n, 2] of (source, destination) block ids.
+ * Run it before the pa_write_kv that writes into the destinations.  Sources
+ * and destinations must be distinct. */
+int pa_copy_blocks(pa_pool* pool, const int32_t* pairs, int n, void* stream);
+
+/* ---- Host block manager ("KV-Cache Block Manager": allocates and releases
+ * blocks, tracks free memory, keeps logical-to-physical mappings).  Host only,
+ * synchronous, never touches device memory.  All-or-nothing: a call that fails
+ * leaves every table, count and the free stack unchanged. ---- */
+
+/* New empty sequence; ids are issued 0, 1, 2, ... and never reused. */
+int pa_seq_create(pa_pool* pool, int* seq);
+
+/* Reserve slots for the next n_tokens positions of `seq` (Step 2: a new block
+ * only when the last one is full).  If the last block is partially filled and
+ * shared (reference count > 1) it is first replaced by a fresh block and the
+ * pair (old, new) is reported for pa_copy_blocks (copy-on-write).
+ *   slots_out      host int32 [n_tokens] (may be NULL if n_tokens == 0)
+ *   cow_pairs_out  host int32 [2] (0 or 1 pair is produced per call)
+ *   n_cow          host, receives the number of pairs
+ * Errors: INVALID_ARG (unknown seq, n_tokens < 0), OUT_OF_BLOCKS. */
+int pa_seq_append(pa_pool* pool, int seq, int n_tokens, int32_t* slots_out,
+                  int32_t* cow_pairs_out, int* n_cow);
+
+/* Fork: the child shares every block of the parent (counts incremented in
+ * logical order) and has the parent's length. */
+int pa_seq_fork(pa_pool* pool, int parent, int* child);
+
+/* Release (Step 5): decrement each block of the table in logical order and
+ * push blocks whose count reaches zero on the free stack. */
+int pa_seq_release(pa_pool* pool, int seq);
+
+/* Copy a sequence's block table to host `out` (capacity `cap` entries);
+ * *n receives its length and *len_tokens (may be NULL) its token count. */
+int pa_seq_block_table(const pa_pool* pool, int seq, int32_t* out, int cap, int* n,
+                       int* len_tokens);
+
+/* Fill host tables [num_seqs, max_blocks] (-1 padded) and host lengths for a
+ * batch of sequences, ready to upload for pa_decode. */
+int pa_batch_tables(const pa_pool* pool, const int* seqs, int num_seqs, int max_blocks,
+                    int32_t* tables_out, int32_t* context_lens_out);
+
+/* Export the allocator state: reference counts [N] and the free stack,
+ * bottom to top, [*n_free] (host arrays of capacity N). */
+int pa_pool_state(const pa_pool* pool, int32_t* refcounts, int32_t* free_stack, int* n_free);
+
+int pa_pool_stats(const pa_pool* pool, pa_stats* stats);
+
+/* Host helper: global slot numbers for positions [pos_begin, pos_begin +
+ * n_tokens) of every sequence of a batch, written sequence-major into host
+ * `slots_out`.  tables: host int32 [num_seqs, max_blocks]; pos_begin and
+ * n_tokens: host int32 [num_seqs]; the total count is sum(n_tokens). */
+int pa_slots_for_positions(const int32_t* tables, int num_seqs, int max_blocks,
+                           int block_size, const int32_t* pos_begin, const int32_t* n_tokens,
+                           int32_t* slots_out);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PA_H */

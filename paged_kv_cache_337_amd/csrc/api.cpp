@@ -1,0 +1,416 @@
+// C ABI of the paged decode library (declared in include/pa.h): argument
+// validation, error reporting, the host block manager, and kernel launches.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
+#include <exception>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "allocator.hpp"
+#include "launch.hpp"
+#include "pa.h"
+
+struct pa_pool {
+  pa_pool_desc desc;
+  void* buf;
+  size_t bytes;
+  pa::BlockAllocator alloc;
+  pa_pool(const pa_pool_desc& d, void* b, size_t n)
+      : desc(d), buf(b), bytes(n), alloc(d.num_blocks, d.block_size) {}
+};
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const std::string& msg) {
+  g_err = msg;
+  return code;
+}
+
+int elem_bytes(int32_t dtype) { return dtype == PA_F32 ? 4 : (dtype == PA_F16 || dtype == PA_BF16) ? 2 : 0; }
+
+// Validates a descriptor; returns PA_OK or an error code (message set).
+int check_desc(const pa_pool_desc* d) {
+  if (!d) return fail(PA_ERR_INVALID_ARG, "descriptor is NULL");
+  if (d->num_layers < 0 || d->num_blocks < 0 || d->num_kv_heads < 0 || d->head_dim < 0)
+    return fail(PA_ERR_INVALID_ARG, "counts cannot be negative");
+  if (d->block_size <= 0) return fail(PA_ERR_INVALID_ARG, "block size must be positive");
+  if (d->num_layers == 0 || d->num_kv_heads == 0 || d->head_dim == 0)
+    return fail(PA_ERR_INVALID_ARG, "layers, kv heads and head_dim must be positive");
+  if (elem_bytes(d->dtype) == 0) return fail(PA_ERR_UNSUPPORTED, "unknown dtype");
+  if (d->block_size % 16 || d->block_size > 256)
+    return fail(PA_ERR_UNSUPPORTED, "block_size must be a multiple of 16, at most 256");
+  if (d->head_dim != 64 && d->head_dim != 128) return fail(PA_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+  if (static_cast<int64_t>(d->num_blocks) * d->block_size >= (int64_t{1} << 31))
+    return fail(PA_ERR_INVALID_ARG, "num_blocks * block_size must stay below 2^31 slots");
+  return PA_OK;
+}
+
+size_t required_bytes(const pa_pool_desc& d) {
+  // 2 * L * T * H_KV * D * B with T = N * bs.
+  return size_t{2} * static_cast<size_t>(d.num_layers) * static_cast<size_t>(d.num_blocks) *
+         static_cast<size_t>(d.block_size) * static_cast<size_t>(d.num_kv_heads) *
+         static_cast<size_t>(d.head_dim) * static_cast<size_t>(elem_bytes(d.dtype));
+}
+
+pa::PoolGeom geom_of(const pa_pool* p) {
+  pa::PoolGeom g;
+  g.base = p->buf;
+  g.L = p->desc.num_layers;
+  g.N = p->desc.num_blocks;
+  g.bs = p->desc.block_size;
+  g.H = p->desc.num_kv_heads;
+  g.D = p->desc.head_dim;
+  g.dtype = p->desc.dtype;
+  g.elem_bytes = elem_bytes(p->desc.dtype);
+  return g;
+}
+
+bool debug_enabled() {
+  static const bool on = [] {
+    const char* s = std::getenv("PA_DEBUG");
+    return s && *s && std::strcmp(s, "0") != 0;
+  }();
+  return on;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(PA_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+int auto_partition(int bs) {
+  // 512 tokens rounded to whole blocks.
+  int p = (512 / bs) * bs;
+  return p > 0 ? p : bs;
+}
+
+template <typename F>
+int guarded(F&& f) {
+  try {
+    return f();
+  } catch (const std::bad_alloc&) {
+    return fail(PA_ERR_INVALID_ARG, "host allocation failed");
+  } catch (const std::exception& e) {
+    return fail(PA_ERR_INVALID_ARG, e.what());
+  } catch (...) {
+    return fail(PA_ERR_INVALID_ARG, "unknown error");
+  }
+}
+
+int alloc_status(pa::AllocResult r, const std::string& msg) {
+  switch (r) {
+    case pa::AllocResult::Ok:
+      return PA_OK;
+    case pa::AllocResult::OutOfBlocks:
+      return fail(PA_ERR_OUT_OF_BLOCKS, msg);
+    default:
+      return fail(PA_ERR_INVALID_ARG, msg);
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pa_version(void) { return "pagedattn-mi355x 0.1.0 (gfx950)"; }
+
+const char* pa_last_error(void) { return g_err.c_str(); }
+
+size_t pa_pool_required_bytes(const pa_pool_desc* desc) {
+  if (check_desc(desc) != PA_OK) return 0;
+  return required_bytes(*desc);
+}
+
+int pa_alloc_pool(const pa_pool_desc* desc, void* dev_buf, size_t buf_bytes,
+                  const int32_t* free_order, pa_pool** out) {
+  return guarded([&]() -> int {
+    if (!out) return fail(PA_ERR_INVALID_ARG, "out is NULL");
+    *out = nullptr;
+    int rc = check_desc(desc);
+    if (rc != PA_OK) return rc;
+    if (!dev_buf) return fail(PA_ERR_INVALID_ARG, "device buffer is NULL");
+    if (reinterpret_cast<uintptr_t>(dev_buf) & 255u)
+      return fail(PA_ERR_INVALID_ARG, "device buffer must be 256-byte aligned");
+    const size_t need = required_bytes(*desc);
+    if (buf_bytes < need)
+      return fail(PA_ERR_BUFFER_TOO_SMALL, "buffer holds " + std::to_string(buf_bytes) + " bytes, pool needs " +
+                                               std::to_string(need));
+    pa_pool* p = new pa_pool(*desc, dev_buf, buf_bytes);
+    if (free_order) {
+      std::string err;
+      if (!p->alloc.set_free_order(free_order, desc->num_blocks, &err)) {
+        delete p;
+        return fail(PA_ERR_INVALID_ARG, err);
+      }
+    }
+    *out = p;
+    return PA_OK;
+  });
+}
+
+int pa_free(pa_pool* pool) {
+  delete pool;
+  return PA_OK;
+}
+
+int pa_write_kv(pa_pool* pool, int layer, const void* k, const void* v,
+                const int32_t* slot_mapping, int num_tokens, void* stream) {
+  return guarded([&]() -> int {
+    if (!pool) return fail(PA_ERR_INVALID_ARG, "pool is NULL");
+    if (layer < 0 || layer >= pool->desc.num_layers) return fail(PA_ERR_INVALID_ARG, "layer out of range");
+    if (num_tokens < 0) return fail(PA_ERR_INVALID_ARG, "token count cannot be negative");
+    if (num_tokens == 0) return PA_OK;
+    if (!k || !v || !slot_mapping) return fail(PA_ERR_INVALID_ARG, "NULL device pointer");
+    if (!aligned16(k) || !aligned16(v)) return fail(PA_ERR_INVALID_ARG, "k and v must be 16-byte aligned");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (debug_enabled()) {
+      std::vector<int32_t> h(num_tokens);
+      hipError_t e = hipMemcpyAsync(h.data(), slot_mapping, sizeof(int32_t) * num_tokens,
+                                    hipMemcpyDeviceToHost, s);
+      if (e == hipSuccess) e = hipStreamSynchronize(s);
+      if (e != hipSuccess) return hip_fail(e, "PA_DEBUG slot readback");
+      const int64_t nslots = static_cast<int64_t>(pool->desc.num_blocks) * pool->desc.block_size;
+      std::vector<int32_t> sorted;
+      for (int32_t x : h) {
+        if (x < -1 || x >= nslots) return fail(PA_ERR_INVALID_ARG, "slot " + std::to_string(x) + " out of range");
+        if (x >= 0) sorted.push_back(x);
+      }
+      std::sort(sorted.begin(), sorted.end());
+      if (std::adjacent_find(sorted.begin(), sorted.end()) != sorted.end())
+        return fail(PA_ERR_INVALID_ARG, "slot_mapping holds a repeated slot");
+    }
+    hipError_t e = pa::launch_write_kv(geom_of(pool), layer, k, v, slot_mapping, num_tokens, s);
+    return e == hipSuccess ? PA_OK : hip_fail(e, "write_kv launch");
+  });
+}
+
+size_t pa_decode_workspace_bytes(const pa_pool* pool, int num_seqs, int num_q_heads,
+                                 int max_context_len, int partition_tokens) {
+  if (!pool || num_seqs <= 0 || num_q_heads <= 0 || max_context_len <= 0) return 0;
+  const int P = partition_tokens > 0 ? partition_tokens : auto_partition(pool->desc.block_size);
+  const int64_t parts = (static_cast<int64_t>(max_context_len) + P - 1) / P;
+  if (parts <= 1) return 0;
+  return static_cast<size_t>(num_seqs) * num_q_heads * parts * (pool->desc.head_dim + 2) * sizeof(float);
+}
+
+int pa_decode(const pa_pool* pool, int layer, const void* q, int num_seqs, int num_q_heads,
+              const int32_t* block_tables, int max_blocks_per_seq, const int32_t* context_lens,
+              int max_context_len, float scale, int partition_tokens, void* workspace,
+              size_t ws_bytes, void* out, void* stream) {
+  return guarded([&]() -> int {
+    if (!pool) return fail(PA_ERR_INVALID_ARG, "pool is NULL");
+    const pa_pool_desc& d = pool->desc;
+    if (layer < 0 || layer >= d.num_layers) return fail(PA_ERR_INVALID_ARG, "layer out of range");
+    if (num_seqs < 0) return fail(PA_ERR_INVALID_ARG, "num_seqs cannot be negative");
+    if (num_seqs == 0) return PA_OK;
+    if (num_seqs > 65535) return fail(PA_ERR_UNSUPPORTED, "at most 65535 sequences per call");
+    if (num_q_heads <= 0 || num_q_heads % d.num_kv_heads)
+      return fail(PA_ERR_INVALID_ARG, "num_q_heads must be a positive multiple of num_kv_heads");
+    const int G = num_q_heads / d.num_kv_heads;
+    if (!pa::decode_supported(d.dtype, d.head_dim, G))
+      return fail(PA_ERR_UNSUPPORTED, "no kernel for G=" + std::to_string(G));
+    if (!q || !out || !block_tables || !context_lens) return fail(PA_ERR_INVALID_ARG, "NULL device pointer");
+    if (!aligned16(q) || !aligned16(out)) return fail(PA_ERR_INVALID_ARG, "q and out must be 16-byte aligned");
+    if (max_blocks_per_seq <= 0 || max_context_len <= 0)
+      return fail(PA_ERR_INVALID_ARG, "max_blocks_per_seq and max_context_len must be positive");
+    if (!std::isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "scale must be finite");
+    const int bs = d.block_size;
+    int P = partition_tokens;
+    if (P == 0) P = auto_partition(bs);
+    if (P < 0 || P % bs || P % 16) return fail(PA_ERR_INVALID_ARG, "partition_tokens must be a multiple of block_size");
+    const int64_t cap64 = std::min<int64_t>(max_context_len, static_cast<int64_t>(max_blocks_per_seq) * bs);
+    const int ctx_cap = static_cast<int>(cap64);
+    const int max_parts = static_cast<int>((cap64 + P - 1) / P);
+    const size_t need = max_parts > 1
+                            ? static_cast<size_t>(num_seqs) * num_q_heads * max_parts * (d.head_dim + 2) * sizeof(float)
+                            : 0;
+    if (need > 0 && (!workspace || ws_bytes < need))
+      return fail(PA_ERR_BUFFER_TOO_SMALL, "workspace needs " + std::to_string(need) + " bytes");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (debug_enabled()) {
+      std::vector<int32_t> hc(num_seqs), ht(static_cast<size_t>(num_seqs) * max_blocks_per_seq);
+      hipError_t e = hipMemcpyAsync(hc.data(), context_lens, sizeof(int32_t) * num_seqs, hipMemcpyDeviceToHost, s);
+      if (e == hipSuccess)
+        e = hipMemcpyAsync(ht.data(), block_tables, sizeof(int32_t) * ht.size(), hipMemcpyDeviceToHost, s);
+      if (e == hipSuccess) e = hipStreamSynchronize(s);
+      if (e != hipSuccess) return hip_fail(e, "PA_DEBUG readback");
+      for (int i = 0; i < num_seqs; ++i) {
+        if (hc[i] < 1 || hc[i] > ctx_cap)
+          return fail(PA_ERR_INVALID_ARG, "context_lens[" + std::to_string(i) + "] out of range");
+        const int nb = (hc[i] + bs - 1) / bs;
+        for (int b = 0; b < nb; ++b) {
+          const int32_t id = ht[static_cast<size_t>(i) * max_blocks_per_seq + b];
+          if (id < 0 || id >= d.num_blocks)
+            return fail(PA_ERR_INVALID_ARG, "block_tables[" + std::to_string(i) + "][" + std::to_string(b) + "] invalid");
+        }
+      }
+    }
+    pa::DecodeParams p{};
+    p.pool = pool->buf;
+    p.layer_off = static_cast<size_t>(layer) * d.num_blocks * d.num_kv_heads * 2 * static_cast<size_t>(bs) * d.head_dim;
+    p.N = d.num_blocks;
+    p.H = d.num_kv_heads;
+    p.bs = bs;
+    p.q = q;
+    p.out = out;
+    p.tables = block_tables;
+    p.max_blocks = max_blocks_per_seq;
+    p.ctx = context_lens;
+    p.S = num_seqs;
+    p.Hq = num_q_heads;
+    p.G = G;
+    p.ctx_cap = ctx_cap;
+    p.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
+    p.P = P;
+    p.max_parts = max_parts;
+    float* ws = static_cast<float*>(workspace);
+    const size_t parts_total = static_cast<size_t>(num_seqs) * num_q_heads * max_parts;
+    p.ws_o = need ? ws : nullptr;
+    p.ws_ml = need ? ws + parts_total * d.head_dim : nullptr;
+    hipError_t e = pa::launch_decode(p, d.dtype, d.head_dim, s);
+    return e == hipSuccess ? PA_OK : hip_fail(e, "decode launch");
+  });
+}
+
+int pa_copy_blocks(pa_pool* pool, const int32_t* pairs, int n, void* stream) {
+  return guarded([&]() -> int {
+    if (!pool) return fail(PA_ERR_INVALID_ARG, "pool is NULL");
+    if (n < 0) return fail(PA_ERR_INVALID_ARG, "pair count cannot be negative");
+    if (n == 0) return PA_OK;
+    if (!pairs) return fail(PA_ERR_INVALID_ARG, "pairs is NULL");
+    if (n > 65535) return fail(PA_ERR_UNSUPPORTED, "at most 65535 pairs per call");
+    hipError_t e = pa::launch_copy_blocks(geom_of(pool), pairs, n, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? PA_OK : hip_fail(e, "copy_blocks launch");
+  });
+}
+
+int pa_seq_create(pa_pool* pool, int* seq) {
+  return guarded([&]() -> int {
+    if (!pool || !seq) return fail(PA_ERR_INVALID_ARG, "NULL argument");
+    *seq = pool->alloc.create();
+    return PA_OK;
+  });
+}
+
+int pa_seq_append(pa_pool* pool, int seq, int n_tokens, int32_t* slots_out, int32_t* cow_pairs_out,
+                  int* n_cow) {
+  return guarded([&]() -> int {
+    if (!pool) return fail(PA_ERR_INVALID_ARG, "pool is NULL");
+    if (n_tokens > 0 && !slots_out) return fail(PA_ERR_INVALID_ARG, "slots_out is NULL");
+    std::string err;
+    return alloc_status(pool->alloc.append(seq, n_tokens, slots_out, cow_pairs_out, n_cow, &err), err);
+  });
+}
+
+int pa_seq_fork(pa_pool* pool, int parent, int* child) {
+  return guarded([&]() -> int {
+    if (!pool || !child) return fail(PA_ERR_INVALID_ARG, "NULL argument");
+    std::string err;
+    return alloc_status(pool->alloc.fork(parent, child, &err), err);
+  });
+}
+
+int pa_seq_release(pa_pool* pool, int seq) {
+  return guarded([&]() -> int {
+    if (!pool) return fail(PA_ERR_INVALID_ARG, "pool is NULL");
+    std::string err;
+    return alloc_status(pool->alloc.release(seq, &err), err);
+  });
+}
+
+int pa_seq_block_table(const pa_pool* pool, int seq, int32_t* out, int cap, int* n, int* len_tokens) {
+  return guarded([&]() -> int {
+    if (!pool || !n) return fail(PA_ERR_INVALID_ARG, "NULL argument");
+    if (!pool->alloc.live(seq)) return fail(PA_ERR_INVALID_ARG, "unknown or released sequence");
+    const auto& t = pool->alloc.table(seq);
+    *n = static_cast<int>(t.size());
+    if (len_tokens) *len_tokens = pool->alloc.length(seq);
+    if (static_cast<int>(t.size()) > cap) return fail(PA_ERR_BUFFER_TOO_SMALL, "table capacity too small");
+    if (!t.empty() && !out) return fail(PA_ERR_INVALID_ARG, "out is NULL");
+    std::copy(t.begin(), t.end(), out);
+    return PA_OK;
+  });
+}
+
+int pa_batch_tables(const pa_pool* pool, const int* seqs, int num_seqs, int max_blocks,
+                    int32_t* tables_out, int32_t* context_lens_out) {
+  return guarded([&]() -> int {
+    if (!pool || (num_seqs > 0 && (!seqs || !tables_out || !context_lens_out)))
+      return fail(PA_ERR_INVALID_ARG, "NULL argument");
+    if (num_seqs < 0 || max_blocks < 0) return fail(PA_ERR_INVALID_ARG, "negative size");
+    for (int i = 0; i < num_seqs; ++i) {
+      if (!pool->alloc.live(seqs[i])) return fail(PA_ERR_INVALID_ARG, "unknown or released sequence");
+      if (static_cast<int>(pool->alloc.table(seqs[i]).size()) > max_blocks)
+        return fail(PA_ERR_BUFFER_TOO_SMALL, "max_blocks too small");
+    }
+    for (int i = 0; i < num_seqs; ++i) {
+      const auto& t = pool->alloc.table(seqs[i]);
+      int32_t* row = tables_out + static_cast<size_t>(i) * max_blocks;
+      std::fill(row, row + max_blocks, -1);
+      std::copy(t.begin(), t.end(), row);
+      context_lens_out[i] = pool->alloc.length(seqs[i]);
+    }
+    return PA_OK;
+  });
+}
+
+int pa_pool_state(const pa_pool* pool, int32_t* refcounts, int32_t* free_stack, int* n_free) {
+  return guarded([&]() -> int {
+    if (!pool || !n_free) return fail(PA_ERR_INVALID_ARG, "NULL argument");
+    const auto& rc = pool->alloc.refcounts();
+    const auto& st = pool->alloc.free_stack();
+    if (refcounts) std::copy(rc.begin(), rc.end(), refcounts);
+    if (free_stack) std::copy(st.begin(), st.end(), free_stack);
+    *n_free = static_cast<int>(st.size());
+    return PA_OK;
+  });
+}
+
+int pa_pool_stats(const pa_pool* pool, pa_stats* s) {
+  return guarded([&]() -> int {
+    if (!pool || !s) return fail(PA_ERR_INVALID_ARG, "NULL argument");
+    const auto& a = pool->alloc;
+    s->num_blocks = a.num_blocks();
+    s->free_blocks = static_cast<int64_t>(a.free_stack().size());
+    s->used_blocks = s->num_blocks - s->free_blocks;
+    s->shared_blocks = a.shared_blocks();
+    s->cow_copies = a.cow_copies();
+    s->live_seqs = a.live_seqs();
+    s->logical_tokens = a.logical_tokens();
+    s->tail_slots = a.tail_slots();
+    return PA_OK;
+  });
+}
+
+int pa_slots_for_positions(const int32_t* tables, int num_seqs, int max_blocks, int block_size,
+                           const int32_t* pos_begin, const int32_t* n_tokens, int32_t* slots_out) {
+  return guarded([&]() -> int {
+    if (num_seqs < 0 || max_blocks < 0 || block_size <= 0) return fail(PA_ERR_INVALID_ARG, "bad size");
+    if (num_seqs > 0 && (!tables || !pos_begin || !n_tokens || !slots_out))
+      return fail(PA_ERR_INVALID_ARG, "NULL argument");
+    size_t o = 0;
+    for (int i = 0; i < num_seqs; ++i) {
+      if (pos_begin[i] < 0 || n_tokens[i] < 0) return fail(PA_ERR_INVALID_ARG, "negative position or count");
+      const int64_t end = static_cast<int64_t>(pos_begin[i]) + n_tokens[i];
+      if (end > static_cast<int64_t>(max_blocks) * block_size)
+        return fail(PA_ERR_INVALID_ARG, "position beyond the table of sequence " + std::to_string(i));
+      const int32_t* row = tables + static_cast<size_t>(i) * max_blocks;
+      for (int64_t pos = pos_begin[i]; pos < end; ++pos) {
+        const int32_t b = row[pos / block_size];
+        if (b < 0) return fail(PA_ERR_INVALID_ARG, "position maps to an empty table entry");
+        slots_out[o++] = b * block_size + static_cast<int32_t>(pos % block_size);
+      }
+    }
+    return PA_OK;
+  });
+}
+
+}  // extern "C"

@@ -1,0 +1,564 @@
+// Paged single-token decode attention for gfx950.
+//
+// What is computed ("Paged Attention Explained", "How Paged Attention Works",
+// Step 4; "PagedAttention: paging the KV cache like an OS pages memory", "How
+// it works"): for every sequence and query head, softmax attention of the new
+// token's query over the sequence's cached K/V, which the kernel gathers block
+// by block through the sequence's block table.  The softmax is evaluated
+// online (running max and sum, the technique the first page attributes to
+// FlashAttention) so K/V are read exactly once.
+//
+// Work decomposition: one workgroup of four wave64s per (partition of
+// `P` tokens, kv head, sequence).  The partition is cut into 16-token units
+// (a 16-token sub-tile of one block); wave w takes units w, w+4, ... with the
+// next unit's 16-byte loads in flight while the current one is computed.  The
+// four waves' softmax states are merged through LDS; a sequence with a single
+// partition writes its output directly, otherwise the partition's normalised
+// output, max and sum go to the workspace and `merge_kernel` combines them by
+// log-sum-exp weighting.
+//
+// Two inner paths read the same pool layout:
+//   * MFMA (G = query heads per kv head >= 3): S = K.Q^T with
+//     v_mfma_f32_16x16x32_{bf16,f16} (tokens x heads, head_dim reduced) and
+//     O += P.V with v_mfma_f32_16x16x16 (heads x head_dim, tokens reduced);
+//     float32 pools use v_mfma_f32_16x16x4_f32.  The 16x16 result layout of
+//     the first product is exactly the A-operand layout of the second, so P
+//     never leaves registers.
+//   * VALU (G <= 2, e.g. multi-head attention): packed dot2 for Q.K, wave
+//     shuffles for the per-token reduction and the block max, dot2/FMA for P.V.
+//
+// Memory safety: context lengths are clamped to the table capacity and block
+// ids outside [0, N) are skipped, so bad inputs give unspecified values but
+// never an out-of-bounds access.
+#include <cfloat>
+
+#include "../launch.hpp"
+#include "common.hpp"
+
+namespace pa {
+
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr float kNegInf = -__builtin_inff();
+
+struct UnitPtrs {
+  const char* k;  // K sub-tile base (bytes)
+  const char* v;  // V sub-tile base (bytes)
+  bool ok;
+};
+
+// Location of 16-token unit u of partition `start` of sequence `row`.
+template <int D, int kBytes>
+__device__ __forceinline__ UnitPtrs unit_ptrs(const DecodeParams& p, const int32_t* trow, int start,
+                                              int u, int h) {
+  const int p0 = start + u * 16;
+  const int lb = p0 / p.bs;
+  const int sub = (p0 - lb * p.bs) >> 4;
+  const int32_t b = trow[lb];
+  UnitPtrs r;
+  r.ok = (b >= 0) & (b < p.N);
+  const int32_t bb = r.ok ? b : 0;
+  const size_t region = p.layer_off + (static_cast<size_t>(bb) * p.H + h) * (2 * static_cast<size_t>(p.bs) * D);
+  const char* base = static_cast<const char*>(p.pool) + region * kBytes;
+  r.k = base + static_cast<size_t>(sub) * 16 * D * kBytes;
+  r.v = base + (static_cast<size_t>(p.bs) + static_cast<size_t>(sub) * 16) * D * kBytes;
+  return r;
+}
+
+// Per-thread view of one unit: NCH 16-byte chunks of K and of V.
+template <int NCH>
+struct Frag {
+  uint4 k[NCH];
+  uint4 v[NCH];
+};
+
+template <int NCH>
+__device__ __forceinline__ void load_frag(Frag<NCH>& f, const UnitPtrs& u, int lane) {
+  const uint4* kp = reinterpret_cast<const uint4*>(u.k) + lane;
+  const uint4* vp = reinterpret_cast<const uint4*>(u.v) + lane;
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) f.k[c] = load_stream16(kp + 64 * c);
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) f.v[c] = load_stream16(vp + 64 * c);
+}
+
+// Zero V elements of tokens >= valid (their slots may hold anything, and
+// 0 * NaN would poison the product).  Lane group `grp` holds tokens
+// 4*grp .. 4*grp+3 of the unit, token-inner.
+template <int kBytes, int NCH>
+__device__ __forceinline__ void mask_v_tail(Frag<NCH>& f, int grp, int valid) {
+  const int t0 = 4 * grp;
+  if constexpr (kBytes == 2) {
+    const uint32_t m01 = (t0 + 0 < valid ? 0x0000ffffu : 0u) | (t0 + 1 < valid ? 0xffff0000u : 0u);
+    const uint32_t m23 = (t0 + 2 < valid ? 0x0000ffffu : 0u) | (t0 + 3 < valid ? 0xffff0000u : 0u);
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      f.v[c].x &= m01;
+      f.v[c].y &= m23;
+      f.v[c].z &= m01;
+      f.v[c].w &= m23;
+    }
+  } else {
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      f.v[c].x = t0 + 0 < valid ? f.v[c].x : 0u;
+      f.v[c].y = t0 + 1 < valid ? f.v[c].y : 0u;
+      f.v[c].z = t0 + 2 < valid ? f.v[c].z : 0u;
+      f.v[c].w = t0 + 3 < valid ? f.v[c].w : 0u;
+    }
+  }
+}
+
+// LDS merge of the four waves' states, then either the final output or the
+// partition's workspace entry.  sm_o rows are query heads of this kv head.
+template <typename T, int D, int GMAX>
+struct MergeSmem {
+  float m[kWaves][GMAX];
+  float l[kWaves][GMAX];
+  float o[kWaves][GMAX][D];
+};
+
+template <typename T, int D, int GMAX>
+__device__ __forceinline__ void finish_partition(const DecodeParams& p, MergeSmem<T, D, GMAX>& sm,
+                                                 int i, int h, int j, bool single) {
+  __syncthreads();
+  const int G = p.G;
+  for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
+    const int g = idx / D, d = idx - g * D;
+    float M = sm.m[0][g];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, sm.m[w][g]);
+    float L = 0.f, O = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float mw = sm.m[w][g];
+      const float f = (mw == kNegInf) ? 0.f : fast_exp2(mw - M);
+      L += f * sm.l[w][g];
+      O += f * sm.o[w][g][d];
+    }
+    const int qh = h * G + g;
+    const float o = (L > 0.f) ? O / L : 0.f;
+    if (single) {
+      using B = typename T::bits;
+      B* out = static_cast<B*>(p.out);
+      out[(static_cast<size_t>(i) * p.Hq + qh) * D + d] = static_cast<B>(to_storage<T>(o));
+    } else {
+      const size_t e = (static_cast<size_t>(i) * p.Hq + qh) * p.max_parts + j;
+      p.ws_o[e * D + d] = o;
+      if (d == 0) {
+        p.ws_ml[2 * e] = M;
+        p.ws_ml[2 * e + 1] = L;
+      }
+    }
+  }
+}
+
+__device__ __forceinline__ int clamp_ctx(const DecodeParams& p, int i) {
+  int c = p.ctx[i];
+  c = c < 0 ? 0 : c;
+  return c > p.ctx_cap ? p.ctx_cap : c;
+}
+
+// ---------------------------------------------------------------------------
+// MFMA path: 3 <= G <= 16 query heads per kv head.
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
+  constexpr int kBytes = T::kBytes;
+  constexpr int E = 16 / kBytes;
+  constexpr int NCH = D / (4 * E);  // 16-byte chunks per lane per sub-tile
+  constexpr int NT = D / 16;        // 16-wide head_dim tiles of the output
+  __shared__ MergeSmem<T, D, 16> sm;
+
+  const int j = blockIdx.x, h = blockIdx.y, i = blockIdx.z;
+  const int ctx = clamp_ctx(p, i);
+  const int start = j * p.P;
+  if (start >= ctx && !(j == 0 && ctx == 0)) return;
+  const int ntok = ctx - start < p.P ? ctx - start : p.P;
+  const int nunits = (ntok + 15) >> 4;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int col = lane & 15, grp = lane >> 4;
+  const int G = p.G;
+  const int32_t* trow = p.tables + static_cast<size_t>(i) * p.max_blocks;
+
+  // Query rows as the B operand of S = K.Q^T: lane holds head `col`,
+  // the head_dim entries matching its K chunk entries.
+  const char* qbase = static_cast<const char*>(p.q) +
+                      (static_cast<size_t>(i) * p.Hq + static_cast<size_t>(h) * G + col) * D * kBytes;
+  uint4 qb[NCH];
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    qb[c] = (col < G) ? *reinterpret_cast<const uint4*>(qbase + ((c * 4 + grp) * E) * kBytes)
+                      : make_uint4(0, 0, 0, 0);
+  }
+
+  f32x4_t acc[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m_col = kNegInf, l_part = 0.f;
+  const float sl2 = p.scale_log2;
+
+  auto compute = [&](Frag<NCH>& f, int u, bool ok) {
+    const int valid = ntok - u * 16 < 16 ? ntok - u * 16 : 16;
+    if (!ok) return;
+    f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (kBytes == 2) {
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) s = mfma_k32<T>(f.k[c], qb[c], s);
+    } else {
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+        s = mfma_f32_k4(__uint_as_float(f.k[c].x), __uint_as_float(qb[c].x), s);
+        s = mfma_f32_k4(__uint_as_float(f.k[c].y), __uint_as_float(qb[c].y), s);
+        s = mfma_f32_k4(__uint_as_float(f.k[c].z), __uint_as_float(qb[c].z), s);
+        s = mfma_f32_k4(__uint_as_float(f.k[c].w), __uint_as_float(qb[c].w), s);
+      }
+    }
+    // s[r] = score of token 4*grp + r for query head col.
+    float sv[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sv[r] = (4 * grp + r < valid) ? s[r] * sl2 : kNegInf;
+    float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_col, mx);
+    const float alpha = fast_exp2(m_col - m_new);
+    m_col = m_new;
+    float pr[4];
+    uint32_t pbits[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float e = fast_exp2(sv[r] - m_new);
+      if constexpr (kBytes == 2) {
+        pbits[r] = to_storage<T>(e);
+        pr[r] = from_storage<T>(pbits[r]);
+      } else {
+        pr[r] = e;
+      }
+    }
+    l_part = l_part * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
+    // Output rows 4*grp + r belong to query heads whose alpha sits in lane 4*grp + r.
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float a = __shfl(alpha, 4 * grp + r);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) acc[t][r] *= a;
+    }
+    if (valid < 16) mask_v_tail<kBytes, NCH>(f, grp, valid);
+    if constexpr (kBytes == 2) {
+      const uint2 pa = make_uint2(pbits[0] | (pbits[1] << 16), pbits[2] | (pbits[3] << 16));
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const uint4 vc = f.v[t >> 1];
+        const uint2 vb = (t & 1) ? make_uint2(vc.z, vc.w) : make_uint2(vc.x, vc.y);
+        acc[t] = mfma_k16<T>(pa, vb, acc[t]);
+      }
+    } else {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        acc[t] = mfma_f32_k4(pr[0], __uint_as_float(f.v[t].x), acc[t]);
+        acc[t] = mfma_f32_k4(pr[1], __uint_as_float(f.v[t].y), acc[t]);
+        acc[t] = mfma_f32_k4(pr[2], __uint_as_float(f.v[t].z), acc[t]);
+        acc[t] = mfma_f32_k4(pr[3], __uint_as_float(f.v[t].w), acc[t]);
+      }
+    }
+  };
+
+  Frag<NCH> fa, fb;
+  int u = wave;
+  bool oka = false, okb = false;
+  if (u < nunits) {
+    const UnitPtrs up = unit_ptrs<D, kBytes>(p, trow, start, u, h);
+    oka = up.ok;
+    load_frag<NCH>(fa, up, lane);
+  }
+  while (u < nunits) {
+    if (u + kWaves < nunits) {
+      const UnitPtrs up = unit_ptrs<D, kBytes>(p, trow, start, u + kWaves, h);
+      okb = up.ok;
+      load_frag<NCH>(fb, up, lane);
+    }
+    compute(fa, u, oka);
+    u += kWaves;
+    if (u >= nunits) break;
+    if (u + kWaves < nunits) {
+      const UnitPtrs up = unit_ptrs<D, kBytes>(p, trow, start, u + kWaves, h);
+      oka = up.ok;
+      load_frag<NCH>(fa, up, lane);
+    }
+    compute(fb, u, okb);
+    u += kWaves;
+  }
+
+  // Column sums over the four lane groups.
+  float l_col = l_part + __shfl_xor(l_part, 16);
+  l_col += __shfl_xor(l_col, 32);
+  if (lane < 16) {
+    sm.m[wave][lane] = m_col;
+    sm.l[wave][lane] = l_col;
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int g = 4 * grp + r;
+    if (g < G) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) sm.o[wave][g][t * 16 + col] = acc[t][r];
+    }
+  }
+  finish_partition<T, D, 16>(p, sm, i, h, j, ctx <= p.P);
+}
+
+// ---------------------------------------------------------------------------
+// VALU path: NG (1 or 2) query heads per kv head.
+// ---------------------------------------------------------------------------
+template <typename T, int D, int NG>
+__global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeParams p) {
+  constexpr int kBytes = T::kBytes;
+  constexpr int E = 16 / kBytes;
+  constexpr int NCH = D / (4 * E);
+  constexpr int R = E / 4;          // 16-wide d tiles per V chunk
+  constexpr int NT = D / 16;        // d values per lane in P.V (d = t*16 + col)
+  __shared__ MergeSmem<T, D, NG> sm;
+
+  const int j = blockIdx.x, h = blockIdx.y, i = blockIdx.z;
+  const int ctx = clamp_ctx(p, i);
+  const int start = j * p.P;
+  if (start >= ctx && !(j == 0 && ctx == 0)) return;
+  const int ntok = ctx - start < p.P ? ctx - start : p.P;
+  const int nunits = (ntok + 15) >> 4;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int col = lane & 15, grp = lane >> 4;
+  const int32_t* trow = p.tables + static_cast<size_t>(i) * p.max_blocks;
+
+  // q entries matching this lane's K chunk entries: d = (c*4 + grp)*E + e.
+  uint4 qv[NG][NCH];
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    const char* qrow = static_cast<const char*>(p.q) +
+                       (static_cast<size_t>(i) * p.Hq + static_cast<size_t>(h) * NG + g) * D * kBytes;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) qv[g][c] = *reinterpret_cast<const uint4*>(qrow + ((c * 4 + grp) * E) * kBytes);
+  }
+
+  float acc[NG][NT];
+  float m_run[NG], l_run[NG];
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    m_run[g] = kNegInf;
+    l_run[g] = 0.f;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[g][t] = 0.f;
+  }
+  const float sl2 = p.scale_log2;
+
+  auto compute = [&](Frag<NCH>& f, int u, bool ok) {
+    const int valid = ntok - u * 16 < 16 ? ntok - u * 16 : 16;
+    if (!ok) return;
+    if (valid < 16) mask_v_tail<kBytes, NCH>(f, grp, valid);
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      // Partial dot over this lane's head_dim entries of token `col`.
+      float dot = 0.f;
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+        if constexpr (kBytes == 2) {
+          dot = dot2<T>(f.k[c].x, qv[g][c].x, dot);
+          dot = dot2<T>(f.k[c].y, qv[g][c].y, dot);
+          dot = dot2<T>(f.k[c].z, qv[g][c].z, dot);
+          dot = dot2<T>(f.k[c].w, qv[g][c].w, dot);
+        } else {
+          dot = fmaf(__uint_as_float(f.k[c].x), __uint_as_float(qv[g][c].x), dot);
+          dot = fmaf(__uint_as_float(f.k[c].y), __uint_as_float(qv[g][c].y), dot);
+          dot = fmaf(__uint_as_float(f.k[c].z), __uint_as_float(qv[g][c].z), dot);
+          dot = fmaf(__uint_as_float(f.k[c].w), __uint_as_float(qv[g][c].w), dot);
+        }
+      }
+      dot += __shfl_xor(dot, 16);
+      dot += __shfl_xor(dot, 32);
+      const float s = (col < valid) ? dot * sl2 : kNegInf;
+      float mx = fmaxf(s, __shfl_xor(s, 1));
+      mx = fmaxf(mx, __shfl_xor(mx, 2));
+      mx = fmaxf(mx, __shfl_xor(mx, 4));
+      mx = fmaxf(mx, __shfl_xor(mx, 8));
+      const float m_new = fmaxf(m_run[g], mx);
+      const float alpha = fast_exp2(m_run[g] - m_new);
+      m_run[g] = m_new;
+      const float e = fast_exp2(s - m_new);
+      uint32_t pb;
+      float pr;
+      if constexpr (kBytes == 2) {
+        pb = to_storage<T>(e);
+        pr = from_storage<T>(pb);
+      } else {
+        pb = __float_as_uint(e);
+        pr = e;
+      }
+      l_run[g] = l_run[g] * alpha + pr;  // token `col`'s weight; summed over lanes at the end
+      // Weights of tokens 4*grp .. 4*grp+3, the tokens this lane's V entries hold.
+      const uint32_t w0 = __shfl(pb, 4 * grp + 0), w1 = __shfl(pb, 4 * grp + 1);
+      const uint32_t w2 = __shfl(pb, 4 * grp + 2), w3 = __shfl(pb, 4 * grp + 3);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) acc[g][t] *= alpha;
+      if constexpr (kBytes == 2) {
+        const uint32_t p01 = w0 | (w1 << 16), p23 = w2 | (w3 << 16);
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+          // chunk c holds d tiles c*R + 0 (dwords x, y) and c*R + 1 (z, w)
+          acc[g][c * R + 0] = dot2<T>(f.v[c].x, p01, acc[g][c * R + 0]);
+          acc[g][c * R + 0] = dot2<T>(f.v[c].y, p23, acc[g][c * R + 0]);
+          acc[g][c * R + 1] = dot2<T>(f.v[c].z, p01, acc[g][c * R + 1]);
+          acc[g][c * R + 1] = dot2<T>(f.v[c].w, p23, acc[g][c * R + 1]);
+        }
+      } else {
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+          float a = acc[g][c];
+          a = fmaf(__uint_as_float(w0), __uint_as_float(f.v[c].x), a);
+          a = fmaf(__uint_as_float(w1), __uint_as_float(f.v[c].y), a);
+          a = fmaf(__uint_as_float(w2), __uint_as_float(f.v[c].z), a);
+          a = fmaf(__uint_as_float(w3), __uint_as_float(f.v[c].w), a);
+          acc[g][c] = a;
+        }
+      }
+    }
+  };
+
+  Frag<NCH> fa, fb;
+  int u = wave;
+  bool oka = false, okb = false;
+  if (u < nunits) {
+    const UnitPtrs up = unit_ptrs<D, kBytes>(p, trow, start, u, h);
+    oka = up.ok;
+    load_frag<NCH>(fa, up, lane);
+  }
+  while (u < nunits) {
+    if (u + kWaves < nunits) {
+      const UnitPtrs up = unit_ptrs<D, kBytes>(p, trow, start, u + kWaves, h);
+      okb = up.ok;
+      load_frag<NCH>(fb, up, lane);
+    }
+    compute(fa, u, oka);
+    u += kWaves;
+    if (u >= nunits) break;
+    if (u + kWaves < nunits) {
+      const UnitPtrs up = unit_ptrs<D, kBytes>(p, trow, start, u + kWaves, h);
+      oka = up.ok;
+      load_frag<NCH>(fa, up, lane);
+    }
+    compute(fb, u, okb);
+    u += kWaves;
+  }
+
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    float l = l_run[g];
+    l += __shfl_xor(l, 1);
+    l += __shfl_xor(l, 2);
+    l += __shfl_xor(l, 4);
+    l += __shfl_xor(l, 8);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      float a = acc[g][t];
+      a += __shfl_xor(a, 16);
+      a += __shfl_xor(a, 32);
+      acc[g][t] = a;
+    }
+    if (lane < 16) {
+      if (lane == 0) {
+        sm.m[wave][g] = m_run[g];
+        sm.l[wave][g] = l;
+      }
+#pragma unroll
+      for (int t = 0; t < NT; ++t) sm.o[wave][g][t * 16 + col] = acc[g][t];
+    }
+  }
+  finish_partition<T, D, NG>(p, sm, i, h, j, ctx <= p.P);
+}
+
+// ---------------------------------------------------------------------------
+// Log-sum-exp merge of partition states: one wave per (sequence, query head).
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void merge_kernel(DecodeParams p) {
+  const int lane = threadIdx.x & 63;
+  const int pair = blockIdx.x * kWaves + (threadIdx.x >> 6);
+  if (pair >= p.S * p.Hq) return;
+  const int i = pair / p.Hq;
+  const int ctx = clamp_ctx(p, i);
+  if (ctx <= p.P) return;  // written directly by the partition kernel
+  int np = (ctx + p.P - 1) / p.P;
+  np = np > p.max_parts ? p.max_parts : np;
+  const size_t e0 = static_cast<size_t>(pair) * p.max_parts;
+  const float* ml = p.ws_ml + 2 * e0;
+
+  float M = kNegInf;
+  for (int jj = lane; jj < np; jj += 64) M = fmaxf(M, ml[2 * jj]);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+  float L = 0.f;
+  for (int jj = lane; jj < np; jj += 64) L += ml[2 * jj + 1] * fast_exp2(ml[2 * jj] - M);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) L += __shfl_xor(L, o);
+
+  constexpr int PER = D / 64;
+  float acc[PER];
+#pragma unroll
+  for (int k = 0; k < PER; ++k) acc[k] = 0.f;
+  for (int jj = 0; jj < np; ++jj) {
+    const float w = ml[2 * jj + 1] * fast_exp2(ml[2 * jj] - M);
+    const float* o = p.ws_o + (e0 + jj) * D;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) acc[k] = fmaf(w, o[lane + 64 * k], acc[k]);
+  }
+  using B = typename T::bits;
+  B* out = static_cast<B*>(p.out);
+  const float inv = (L > 0.f) ? 1.f / L : 0.f;
+#pragma unroll
+  for (int k = 0; k < PER; ++k)
+    out[static_cast<size_t>(pair) * D + lane + 64 * k] = static_cast<B>(to_storage<T>(acc[k] * inv));
+}
+
+template <typename T, int D>
+hipError_t launch_typed(const DecodeParams& p, hipStream_t stream) {
+  const dim3 grid(p.max_parts > 0 ? p.max_parts : 1, p.H, p.S);
+  if (p.G >= 3) {
+    hipLaunchKernelGGL((decode_mfma_kernel<T, D>), grid, dim3(kThreads), 0, stream, p);
+  } else if (p.G == 2) {
+    hipLaunchKernelGGL((decode_valu_kernel<T, D, 2>), grid, dim3(kThreads), 0, stream, p);
+  } else {
+    hipLaunchKernelGGL((decode_valu_kernel<T, D, 1>), grid, dim3(kThreads), 0, stream, p);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.max_parts <= 1) return e;
+  const int pairs = p.S * p.Hq;
+  hipLaunchKernelGGL((merge_kernel<T, D>), dim3((pairs + kWaves - 1) / kWaves), dim3(kThreads), 0,
+                     stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool decode_supported(int dtype, int D, int G) {
+  if (D != 64 && D != 128) return false;
+  if (G < 1 || G > 16) return false;
+  return dtype == 0 || dtype == 1 || dtype == 2;
+}
+
+hipError_t launch_decode(const DecodeParams& p, int dtype, int D, hipStream_t stream) {
+  if (!decode_supported(dtype, D, p.G)) return hipErrorInvalidValue;
+  if (p.S <= 0) return hipSuccess;
+  switch (dtype) {
+    case 0:
+      return D == 64 ? launch_typed<F32, 64>(p, stream) : launch_typed<F32, 128>(p, stream);
+    case 1:
+      return D == 64 ? launch_typed<F16, 64>(p, stream) : launch_typed<F16, 128>(p, stream);
+    default:
+      return D == 64 ? launch_typed<BF16, 64>(p, stream) : launch_typed<BF16, 128>(p, stream);
+  }
+}
+
+}  // namespace pa

@@ -1,0 +1,45 @@
+// Host-side launch entry points of the device kernels (internal, not ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pa {
+
+struct PoolGeom {
+  void* base;           // device pool buffer
+  int32_t L, N, bs, H, D, dtype;
+  int32_t elem_bytes;
+  size_t layer_elems() const { return static_cast<size_t>(N) * H * 2 * bs * D; }
+};
+
+struct DecodeParams {
+  const void* pool;          // device pool base
+  size_t layer_off;          // element offset of the layer
+  int32_t N, H, bs;
+  const void* q;             // [S, Hq, D]
+  void* out;                 // [S, Hq, D]
+  const int32_t* tables;     // [S, max_blocks]
+  int32_t max_blocks;
+  const int32_t* ctx;        // [S]
+  int32_t S, Hq, G;
+  int32_t ctx_cap;           // min(max_context_len, max_blocks * bs)
+  float scale_log2;          // scale * log2(e)
+  int32_t P;                 // partition tokens
+  int32_t max_parts;         // ceil(ctx_cap / P)
+  float* ws_o;               // [S, Hq, max_parts, D]
+  float* ws_ml;              // [S, Hq, max_parts, 2] (max in log2 units, sum)
+};
+
+hipError_t launch_write_kv(const PoolGeom& g, int layer, const void* k, const void* v,
+                           const int32_t* slots, int num_tokens, hipStream_t stream);
+
+hipError_t launch_copy_blocks(const PoolGeom& g, const int32_t* pairs, int n, hipStream_t stream);
+
+// Returns hipErrorInvalidValue when no kernel variant covers (dtype, D, G).
+hipError_t launch_decode(const DecodeParams& p, int dtype, int D, hipStream_t stream);
+
+bool decode_supported(int dtype, int D, int G);
+
+}  // namespace pa
