@@ -1,0 +1,206 @@
+"""Paged decode benchmark on one MI355X.
+
+A step is one pass of the decode hot path over one batch: write the batch's
+new-token K/V rows into their cache slots (pa_write_kv), then decode attention
+for every sequence over its paged cache (pa_decode: partition kernel plus the
+log-sum-exp merge).  Default workload: Llama-3-8B-shaped GQA, bf16, 256
+sequences, 32 query / 8 KV heads, head_dim 128, block_size 16, context lengths
+lognormal (median 1024, sigma 0.8) clipped to [16, 8192], blocks placed by a
+seeded random permutation.  The pool holds `--layers` copies of the batch
+(one per layer slot) and consecutive steps use consecutive layers, so a step
+never finds the previous step's K/V in the 256 MB Infinity Cache.
+
+Prints one JSON line.  value = KV-read GB/s = algorithmic KV bytes of one step
+(valid tokens only: sum(ctx) * 2 * H_kv * D * 2 B) / wall time per step.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "paged decode KV-read GB/s (% of HBM peak) + seqs/s, Llama-3-8B-shaped GQA b=256"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="llama3_8b",
+                    choices=["tiny", "opt13b", "llama3_8b", "long_ctx"])
+    ap.add_argument("--layers", type=int, default=4)
+    ap.add_argument("--partition-tokens", type=int, default=-1,
+                    help="-1: the workload's own setting (0 = library default)")
+    ap.add_argument("--cpu-budget-s", type=float, default=20.0,
+                    help="wall-clock budget of the oracle baseline sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(w, budget_s):
+    """Time the CPU oracle as it stands (gather through the block table, then
+    float64 two-pass softmax) on the first sequences of the same batch, until
+    the wall-clock budget is spent."""
+    from oracle import attention as A
+    from oracle import layout as LY
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    g = LY.Geometry(1, w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim, w.dtype)
+    pool = np.zeros(g.num_elements, dtype=np.uint16 if w.dtype != "f32" else np.float32)
+    done, kv_bytes, t_total = 0, 0, 0.0
+    eb = 4 if w.dtype == "f32" else 2
+    for i in range(w.num_seqs):
+        K, V = w.seq_kv(i)
+        LY.scatter(pool, g, 0, w.block_tables[i], K, V)  # input staging, not timed
+        t0 = time.perf_counter()
+        A.paged_decode(pool, g, 0, w.q, w.block_tables, w.context_lens, w.scale, seqs=[i])
+        t_total += time.perf_counter() - t0
+        done += 1
+        kv_bytes += int(w.context_lens[i]) * 2 * w.num_kv_heads * w.head_dim * eb
+        if t_total >= budget_s:
+            break
+    return {
+        "value": round(kv_bytes / t_total / 1e9, 4),
+        "unit": "GB/s",
+        "seqs_per_s": round(done / t_total, 3),
+        "cores": int(threads),
+        "host_cpus": len(os.sched_getaffinity(0)),
+        "kind": "oracle",
+        "sample": f"first {done} of {w.num_seqs} sequences of the same batch "
+                  f"({int(w.context_lens[:done].sum())} tokens), {t_total:.1f} s of oracle time",
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(json.dumps({"error": "this library runs on a single GPU; use --gpus 1"}))
+        sys.exit(2)
+
+    import torch
+    import paged_kv_cache_337_amd as pa
+    import workloads as W
+    from paged_kv_cache_337_amd import staging as U
+
+    w = W.WORKLOADS[args.workload]()
+    P = w.partition_tokens if args.partition_tokens < 0 else args.partition_tokens
+    eb = pa.ELEM_BYTES[w.dtype]
+    L = max(1, args.layers)
+    log(f"[bench] workload={w.name} S={w.num_seqs} tokens={w.total_tokens} blocks={w.num_blocks} "
+        f"layers={L} P={P}")
+
+    t0 = time.time()
+    pool = U.make_pool(w, layers=L)
+    for layer in range(L):
+        U.fill_pool(pool, w, layer=layer)
+    log(f"[bench] pool filled ({pool.nbytes / 1e9:.2f} GB) in {time.time() - t0:.1f} s")
+
+    # new-token inputs: each sequence's last position (its current token)
+    last = w.context_lens - 1
+    kn = np.stack([w.seq_kv(i)[0][last[i]] for i in range(w.num_seqs)])
+    vn = np.stack([w.seq_kv(i)[1][last[i]] for i in range(w.num_seqs)])
+    slots_new = pa.slots_for_positions(w.block_tables, w.block_size, last, np.ones(w.num_seqs))
+    k_new, v_new = U.dev_tensor(kn, w.dtype), U.dev_tensor(vn, w.dtype)
+    slot_new = torch.from_numpy(slots_new).cuda()
+    q, tables, ctx = U.device_inputs(w)
+    out = torch.empty_like(q)
+    ws_bytes = pool.workspace_bytes(w.num_seqs, w.num_q_heads, w.max_context_len, P)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    max_ctx = w.max_context_len
+
+    def step(k, ev=None):
+        layer = k % L
+        pool.write_kv(layer, k_new, v_new, slot_new)
+        if ev is not None:
+            ev[0].record(stream)
+        pool.decode(layer, q, tables, ctx, max_ctx, w.scale, P, out=out, workspace=ws)
+        if ev is not None:
+            ev[1].record(stream)
+
+    for k in range(args.warmup):
+        step(k)
+    torch.cuda.synchronize()
+    if not torch.isfinite(out.float()).all():
+        raise RuntimeError("non-finite decode output")
+
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    e_all = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    e_all[0].record(stream)
+    for k in range(args.steps):
+        step(args.warmup + k, evs[k])
+    e_all[1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+
+    ms_per_step = wall * 1e3 / args.steps
+    ev_ms = e_all[0].elapsed_time(e_all[1]) / args.steps
+    dec_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    kv_bytes = int(w.context_lens.astype(np.int64).sum()) * 2 * w.num_kv_heads * w.head_dim * eb
+    nblk = int(sum(-(-int(c) // w.block_size) for c in w.context_lens))
+    qo_bytes = 2 * w.num_seqs * w.num_q_heads * w.head_dim * eb
+    alg_bytes = kv_bytes + qo_bytes + 4 * nblk + 4 * w.num_seqs
+    value = kv_bytes / (ms_per_step * 1e-3) / 1e9
+    achieved = alg_bytes / (dec_ms * 1e-3) / 1e9
+    res = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": f"{w.name}: paged decode layer, {w.num_seqs} seqs, {w.num_q_heads}q/{w.num_kv_heads}kv "
+                        f"heads, head_dim {w.head_dim}, block_size {w.block_size}",
+            "batch": w.num_seqs, "total_context_tokens": w.total_tokens,
+            "max_context_len": max_ctx, "partition_tokens": P or 512,
+            "layer_slots_rotated": L,
+            "step": "pa_write_kv (1 new token/seq) + pa_decode",
+        },
+        "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "seqs_per_s": round(w.num_seqs / (ms_per_step * 1e-3), 1),
+        "event_ms_per_step": round(ev_ms, 5),
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "pa_decode (partition kernel + merge)",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "alg_bytes_per_launch": alg_bytes,
+            "avg_launch_ms": round(dec_ms, 5),
+        },
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, args.cpu_budget_s)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

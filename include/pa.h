@@ -130,8 +130,10 @@ int pa_free(pa_pool* pool);
 int pa_write_kv(pa_pool* pool, int layer, const void* k, const void* v,
                 const int32_t* slot_mapping, int num_tokens, void* stream);
 
-/* Device workspace bytes pa_decode needs for split-K partials (float32
- * partial outputs plus running max and sum per query head and partition). */
+/* Device workspace bytes pa_decode needs: a work-item list (one entry per
+ * (sequence, partition) of up to max_context_len tokens) and, when contexts
+ * can span several partitions, float32 partial outputs plus running max and
+ * sum per query head and partition.  Always > 0 for valid arguments. */
 size_t pa_decode_workspace_bytes(const pa_pool* pool, int num_seqs, int num_q_heads,
                                  int max_context_len, int partition_tokens);
 
@@ -151,7 +153,8 @@ size_t pa_decode_workspace_bytes(const pa_pool* pool, int num_seqs, int num_q_he
  *   max_context_len    host value >= every context_lens[i] (sizes the grid)
  *   scale              applied in float32 to the float32 dot products
  *   partition_tokens   0 = automatic, else a multiple of block_size and of 16
- *   workspace          device, >= pa_decode_workspace_bytes(...) bytes
+ *   workspace          device, >= pa_decode_workspace_bytes(...) bytes,
+ *                      256-byte aligned; contents need no initialisation
  * Asynchronous on `stream`; the result is ready when the stream reaches it. */
 int pa_decode(const pa_pool* pool, int layer, const void* q, int num_seqs, int num_q_heads,
               const int32_t* block_tables, int max_blocks_per_seq,

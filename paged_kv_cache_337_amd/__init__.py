@@ -197,9 +197,9 @@ class Pool:
         S, Hq, _ = q.shape
         if out is None:
             out = torch.empty_like(q)
-        need = self.workspace_bytes(S, Hq, max_context_len, partition_tokens)
-        if workspace is None and need:
-            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        if workspace is None:
+            need = self.workspace_bytes(S, Hq, max_context_len, partition_tokens)
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
         wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
         _check(lib.pa_decode(self.handle, layer, _ptr(q), S, Hq, _ptr(block_tables),
                              int(block_tables.shape[1]), _ptr(context_lens), int(max_context_len),

@@ -197,8 +197,7 @@ size_t pa_decode_workspace_bytes(const pa_pool* pool, int num_seqs, int num_q_he
   if (!pool || num_seqs <= 0 || num_q_heads <= 0 || max_context_len <= 0) return 0;
   const int P = partition_tokens > 0 ? partition_tokens : auto_partition(pool->desc.block_size);
   const int64_t parts = (static_cast<int64_t>(max_context_len) + P - 1) / P;
-  if (parts <= 1) return 0;
-  return static_cast<size_t>(num_seqs) * num_q_heads * parts * (pool->desc.head_dim + 2) * sizeof(float);
+  return pa::decode_ws_layout(num_seqs, num_q_heads, static_cast<int>(parts), pool->desc.head_dim).total;
 }
 
 int pa_decode(const pa_pool* pool, int layer, const void* q, int num_seqs, int num_q_heads,
@@ -229,11 +228,11 @@ int pa_decode(const pa_pool* pool, int layer, const void* q, int num_seqs, int n
     const int64_t cap64 = std::min<int64_t>(max_context_len, static_cast<int64_t>(max_blocks_per_seq) * bs);
     const int ctx_cap = static_cast<int>(cap64);
     const int max_parts = static_cast<int>((cap64 + P - 1) / P);
-    const size_t need = max_parts > 1
-                            ? static_cast<size_t>(num_seqs) * num_q_heads * max_parts * (d.head_dim + 2) * sizeof(float)
-                            : 0;
-    if (need > 0 && (!workspace || ws_bytes < need))
-      return fail(PA_ERR_BUFFER_TOO_SMALL, "workspace needs " + std::to_string(need) + " bytes");
+    const pa::WsLayout wl = pa::decode_ws_layout(num_seqs, num_q_heads, max_parts, d.head_dim);
+    if (!workspace || ws_bytes < wl.total)
+      return fail(PA_ERR_BUFFER_TOO_SMALL, "workspace needs " + std::to_string(wl.total) + " bytes");
+    if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+      return fail(PA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (debug_enabled()) {
       std::vector<int32_t> hc(num_seqs), ht(static_cast<size_t>(num_seqs) * max_blocks_per_seq);
@@ -271,10 +270,11 @@ int pa_decode(const pa_pool* pool, int layer, const void* q, int num_seqs, int n
     p.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
     p.P = P;
     p.max_parts = max_parts;
-    float* ws = static_cast<float*>(workspace);
-    const size_t parts_total = static_cast<size_t>(num_seqs) * num_q_heads * max_parts;
-    p.ws_o = need ? ws : nullptr;
-    p.ws_ml = need ? ws + parts_total * d.head_dim : nullptr;
+    char* ws = static_cast<char*>(workspace);
+    p.header = reinterpret_cast<int32_t*>(ws + wl.header_off);
+    p.items = reinterpret_cast<int2*>(ws + wl.items_off);
+    p.ws_o = max_parts > 1 ? reinterpret_cast<float*>(ws + wl.o_off) : nullptr;
+    p.ws_ml = max_parts > 1 ? reinterpret_cast<float*>(ws + wl.ml_off) : nullptr;
     hipError_t e = pa::launch_decode(p, d.dtype, d.head_dim, s);
     return e == hipSuccess ? PA_OK : hip_fail(e, "decode launch");
   });

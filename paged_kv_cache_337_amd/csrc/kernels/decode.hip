@@ -8,14 +8,24 @@
 // online (running max and sum, the technique the first page attributes to
 // FlashAttention) so K/V are read exactly once.
 //
-// Work decomposition: one workgroup of four wave64s per (partition of
-// `P` tokens, kv head, sequence).  The partition is cut into 16-token units
-// (a 16-token sub-tile of one block); wave w takes units w, w+4, ... with the
-// next unit's 16-byte loads in flight while the current one is computed.  The
-// four waves' softmax states are merged through LDS; a sequence with a single
-// partition writes its output directly, otherwise the partition's normalised
-// output, max and sum go to the workspace and `merge_kernel` combines them by
-// log-sum-exp weighting.
+// Launch sequence of one pa_decode call:
+//   1. plan_kernel (one workgroup) cuts every context into partitions of P
+//      tokens and writes the list of (sequence, partition) work items, full
+//      partitions first and the partial ones by decreasing size, so the tail
+//      of the decode consists of the smallest items.
+//   2. the decode kernel is persistent: a grid sized to fill the GPU once;
+//      each workgroup (four wave64s) takes work items (item, kv head) from an
+//      atomic counter, fetching the next index while it works on the current
+//      one.  A sparse grid with one workgroup per possible partition spends
+//      most of its time dispatching empty workgroups; this one does not.
+//   3. merge_kernel combines the partition states of multi-partition
+//      sequences by log-sum-exp weighting.
+//
+// Inside an item the partition is cut into 16-token units (a 16-token
+// sub-tile of one block); wave w takes a contiguous run of units, loading the
+// next unit's K/V (16-byte loads, 1 KiB per instruction) while it computes the
+// current one.  The four waves' states are merged through LDS; single-
+// partition sequences write their output directly.
 //
 // Two inner paths read the same pool layout:
 //   * MFMA (G = query heads per kv head >= 3): S = K.Q^T with
@@ -27,10 +37,16 @@
 //   * VALU (G <= 2, e.g. multi-head attention): packed dot2 for Q.K, wave
 //     shuffles for the per-token reduction and the block max, dot2/FMA for P.V.
 //
+// Online softmax with a lazily moved reference: exponentials are taken
+// relative to a reference max that is raised only when a score exceeds it by
+// more than 2^8; the accumulators are rescaled only then.  The result is the
+// same softmax (the final division uses the same reference) while the common
+// unit needs no cross-lane max and no accumulator traffic.
+//
 // Memory safety: context lengths are clamped to the table capacity and block
 // ids outside [0, N) are skipped, so bad inputs give unspecified values but
 // never an out-of-bounds access.
-#include <cfloat>
+#include <mutex>
 
 #include "../launch.hpp"
 #include "common.hpp"
@@ -42,6 +58,9 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr float kNegInf = -__builtin_inff();
+constexpr float kRescaleLog2 = 8.0f;  // raise the reference only past 2^8
+constexpr int kPlanThreads = 1024;
+constexpr int kPlanBins = 1024;       // partial items sorted by 16-token units
 
 struct UnitPtrs {
   const char* k;  // K sub-tile base (bytes)
@@ -49,7 +68,7 @@ struct UnitPtrs {
   bool ok;
 };
 
-// Location of 16-token unit u of partition `start` of sequence `row`.
+// Location of 16-token unit u of the partition starting at token `start`.
 template <int D, int kBytes>
 __device__ __forceinline__ UnitPtrs unit_ptrs(const DecodeParams& p, const int32_t* trow, int start,
                                               int u, int h) {
@@ -112,16 +131,17 @@ __device__ __forceinline__ void mask_v_tail(Frag<NCH>& f, int grp, int valid) {
 }
 
 // LDS merge of the four waves' states, then either the final output or the
-// partition's workspace entry.  sm_o rows are query heads of this kv head.
-template <typename T, int D, int GMAX>
+// partition's workspace entry.  Rows are the query heads of this kv head.
+template <int D, int GMAX>
 struct MergeSmem {
   float m[kWaves][GMAX];
   float l[kWaves][GMAX];
   float o[kWaves][GMAX][D];
+  int next;
 };
 
 template <typename T, int D, int GMAX>
-__device__ __forceinline__ void finish_partition(const DecodeParams& p, MergeSmem<T, D, GMAX>& sm,
+__device__ __forceinline__ void finish_partition(const DecodeParams& p, MergeSmem<D, GMAX>& sm,
                                                  int i, int h, int j, bool single) {
   __syncthreads();
   const int G = p.G;
@@ -161,28 +181,100 @@ __device__ __forceinline__ int clamp_ctx(const DecodeParams& p, int i) {
   return c > p.ctx_cap ? p.ctx_cap : c;
 }
 
+// Wave-uniform "any lane" test.
+__device__ __forceinline__ bool wave_any(bool x) { return __builtin_amdgcn_ballot_w64(x) != 0; }
+
+// ---------------------------------------------------------------------------
+// Work items: plan kernel.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeParams p, int grid) {
+  __shared__ int cnt[kPlanBins];
+  __shared__ int off[kPlanBins];
+  const int P = p.P;
+  const int top = (P >> 4) - 1 < kPlanBins - 1 ? (P >> 4) - 1 : kPlanBins - 1;
+  for (int b = threadIdx.x; b < kPlanBins; b += kPlanThreads) cnt[b] = 0;
+  __syncthreads();
+  auto bin_of = [&](int ntok) {
+    const int units = (ntok + 15) >> 4;
+    const int b = units > 0 ? units - 1 : 0;
+    return b < top ? b : top;
+  };
+  for (int i = threadIdx.x; i < p.S; i += kPlanThreads) {
+    const int c = clamp_ctx(p, i);
+    const int nfull = c / P, rem = c - nfull * P;
+    if (nfull > 0) atomicAdd(&cnt[bin_of(P)], nfull);
+    if (rem > 0 || c == 0) atomicAdd(&cnt[bin_of(rem)], 1);
+  }
+  __syncthreads();
+  // Exclusive prefix over bins in descending size order: off[b] = sum_{b' > b} cnt[b'].
+  if (threadIdx.x == 0) {
+    int run = 0;
+    for (int b = kPlanBins - 1; b >= 0; --b) {
+      off[b] = run;
+      run += cnt[b];
+    }
+    p.header[0] = run;
+    p.header[1] = grid;  // indices below `grid` are taken by blockIdx at launch
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < p.S; i += kPlanThreads) {
+    const int c = clamp_ctx(p, i);
+    const int nfull = c / P, rem = c - nfull * P;
+    if (nfull > 0) {
+      const int base = atomicAdd(&off[bin_of(P)], nfull);
+      for (int j = 0; j < nfull; ++j) p.items[base + j] = make_int2(i, j);
+    }
+    if (rem > 0 || c == 0) p.items[atomicAdd(&off[bin_of(rem)], 1)] = make_int2(i, nfull);
+  }
+}
+
+// Persistent driver: the workgroup takes work index `cur` = item * H + head.
+template <typename Item>
+__device__ __forceinline__ void run_items(const DecodeParams& p, int& next_slot, Item&& item) {
+  const int total = p.header[0] * p.H;
+  int cur = blockIdx.x;
+  while (cur < total) {
+    int nxt = 0;
+    if (threadIdx.x == 0) nxt = atomicAdd(&p.header[1], 1);
+    const int it = cur / p.H;
+    const int2 sj = p.items[it];
+    item(sj.x, sj.y, cur - it * p.H);
+    if (threadIdx.x == 0) next_slot = nxt;
+    __syncthreads();
+    cur = next_slot;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // MFMA path: 3 <= G <= 16 query heads per kv head.
 // ---------------------------------------------------------------------------
 template <typename T, int D>
-__global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
+__device__ __forceinline__ void mfma_item(const DecodeParams& p, MergeSmem<D, 16>& sm, int i, int j, int h) {
   constexpr int kBytes = T::kBytes;
   constexpr int E = 16 / kBytes;
   constexpr int NCH = D / (4 * E);  // 16-byte chunks per lane per sub-tile
   constexpr int NT = D / 16;        // 16-wide head_dim tiles of the output
-  __shared__ MergeSmem<T, D, 16> sm;
 
-  const int j = blockIdx.x, h = blockIdx.y, i = blockIdx.z;
   const int ctx = clamp_ctx(p, i);
   const int start = j * p.P;
-  if (start >= ctx && !(j == 0 && ctx == 0)) return;
   const int ntok = ctx - start < p.P ? ctx - start : p.P;
-  const int nunits = (ntok + 15) >> 4;
+  const int nunits = ntok > 0 ? (ntok + 15) >> 4 : 0;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int col = lane & 15, grp = lane >> 4;
   const int G = p.G;
   const int32_t* trow = p.tables + static_cast<size_t>(i) * p.max_blocks;
+  const int per = (nunits + kWaves - 1) / kWaves;
+  const int u0 = wave * per;
+  const int u1 = u0 + per < nunits ? u0 + per : nunits;
+
+  Frag<NCH> fa, fb;
+  bool oka = false, okb = false;
+  if (u0 < u1) {
+    const UnitPtrs up = unit_ptrs<D, kBytes>(p, trow, start, u0, h);
+    oka = up.ok;
+    load_frag<NCH>(fa, up, lane);
+  }
 
   // Query rows as the B operand of S = K.Q^T: lane holds head `col`,
   // the head_dim entries matching its K chunk entries.
@@ -217,21 +309,31 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
         s = mfma_f32_k4(__uint_as_float(f.k[c].w), __uint_as_float(qb[c].w), s);
       }
     }
-    // s[r] = score of token 4*grp + r for query head col.
+    // s[r] = score of token 4*grp + r for query head col (log2 units).
     float sv[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) sv[r] = (4 * grp + r < valid) ? s[r] * sl2 : kNegInf;
-    float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_col, mx);
-    const float alpha = fast_exp2(m_col - m_new);
-    m_col = m_new;
+    const float mloc = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+    if (wave_any(mloc > m_col + kRescaleLog2)) {
+      float mx = fmaxf(mloc, __shfl_xor(mloc, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_new = fmaxf(m_col, mx);
+      const float alpha = fast_exp2(m_col - m_new);
+      m_col = m_new;
+      l_part *= alpha;
+      // Output rows 4*grp + r belong to query heads whose alpha sits in lane 4*grp + r.
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float a = __shfl(alpha, 4 * grp + r);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) acc[t][r] *= a;
+      }
+    }
     float pr[4];
     uint32_t pbits[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const float e = fast_exp2(sv[r] - m_new);
+      const float e = fast_exp2(sv[r] - m_col);
       if constexpr (kBytes == 2) {
         pbits[r] = to_storage<T>(e);
         pr[r] = from_storage<T>(pbits[r]);
@@ -239,14 +341,7 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
         pr[r] = e;
       }
     }
-    l_part = l_part * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
-    // Output rows 4*grp + r belong to query heads whose alpha sits in lane 4*grp + r.
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float a = __shfl(alpha, 4 * grp + r);
-#pragma unroll
-      for (int t = 0; t < NT; ++t) acc[t][r] *= a;
-    }
+    l_part += (pr[0] + pr[1]) + (pr[2] + pr[3]);
     if (valid < 16) mask_v_tail<kBytes, NCH>(f, grp, valid);
     if constexpr (kBytes == 2) {
       const uint2 pa = make_uint2(pbits[0] | (pbits[1] << 16), pbits[2] | (pbits[3] << 16));
@@ -267,30 +362,22 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
     }
   };
 
-  Frag<NCH> fa, fb;
-  int u = wave;
-  bool oka = false, okb = false;
-  if (u < nunits) {
-    const UnitPtrs up = unit_ptrs<D, kBytes>(p, trow, start, u, h);
-    oka = up.ok;
-    load_frag<NCH>(fa, up, lane);
-  }
-  while (u < nunits) {
-    if (u + kWaves < nunits) {
-      const UnitPtrs up = unit_ptrs<D, kBytes>(p, trow, start, u + kWaves, h);
+  int u = u0;
+  while (u < u1) {
+    if (u + 1 < u1) {
+      const UnitPtrs up = unit_ptrs<D, kBytes>(p, trow, start, u + 1, h);
       okb = up.ok;
       load_frag<NCH>(fb, up, lane);
     }
     compute(fa, u, oka);
-    u += kWaves;
-    if (u >= nunits) break;
-    if (u + kWaves < nunits) {
-      const UnitPtrs up = unit_ptrs<D, kBytes>(p, trow, start, u + kWaves, h);
+    if (++u >= u1) break;
+    if (u + 1 < u1) {
+      const UnitPtrs up = unit_ptrs<D, kBytes>(p, trow, start, u + 1, h);
       oka = up.ok;
       load_frag<NCH>(fa, up, lane);
     }
     compute(fb, u, okb);
-    u += kWaves;
+    ++u;
   }
 
   // Column sums over the four lane groups.
@@ -311,28 +398,42 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
   finish_partition<T, D, 16>(p, sm, i, h, j, ctx <= p.P);
 }
 
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
+  __shared__ MergeSmem<D, 16> sm;
+  run_items(p, sm.next, [&](int i, int j, int h) { mfma_item<T, D>(p, sm, i, j, h); });
+}
+
 // ---------------------------------------------------------------------------
 // VALU path: NG (1 or 2) query heads per kv head.
 // ---------------------------------------------------------------------------
 template <typename T, int D, int NG>
-__global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeParams p) {
+__device__ __forceinline__ void valu_item(const DecodeParams& p, MergeSmem<D, NG>& sm, int i, int j, int h) {
   constexpr int kBytes = T::kBytes;
   constexpr int E = 16 / kBytes;
   constexpr int NCH = D / (4 * E);
   constexpr int R = E / 4;          // 16-wide d tiles per V chunk
   constexpr int NT = D / 16;        // d values per lane in P.V (d = t*16 + col)
-  __shared__ MergeSmem<T, D, NG> sm;
 
-  const int j = blockIdx.x, h = blockIdx.y, i = blockIdx.z;
   const int ctx = clamp_ctx(p, i);
   const int start = j * p.P;
-  if (start >= ctx && !(j == 0 && ctx == 0)) return;
   const int ntok = ctx - start < p.P ? ctx - start : p.P;
-  const int nunits = (ntok + 15) >> 4;
+  const int nunits = ntok > 0 ? (ntok + 15) >> 4 : 0;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int col = lane & 15, grp = lane >> 4;
   const int32_t* trow = p.tables + static_cast<size_t>(i) * p.max_blocks;
+  const int per = (nunits + kWaves - 1) / kWaves;
+  const int u0 = wave * per;
+  const int u1 = u0 + per < nunits ? u0 + per : nunits;
+
+  Frag<NCH> fa, fb;
+  bool oka = false, okb = false;
+  if (u0 < u1) {
+    const UnitPtrs up = unit_ptrs<D, kBytes>(p, trow, start, u0, h);
+    oka = up.ok;
+    load_frag<NCH>(fa, up, lane);
+  }
 
   // q entries matching this lane's K chunk entries: d = (c*4 + grp)*E + e.
   uint4 qv[NG][NCH];
@@ -380,14 +481,19 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeParams p) {
       dot += __shfl_xor(dot, 16);
       dot += __shfl_xor(dot, 32);
       const float s = (col < valid) ? dot * sl2 : kNegInf;
-      float mx = fmaxf(s, __shfl_xor(s, 1));
-      mx = fmaxf(mx, __shfl_xor(mx, 2));
-      mx = fmaxf(mx, __shfl_xor(mx, 4));
-      mx = fmaxf(mx, __shfl_xor(mx, 8));
-      const float m_new = fmaxf(m_run[g], mx);
-      const float alpha = fast_exp2(m_run[g] - m_new);
-      m_run[g] = m_new;
-      const float e = fast_exp2(s - m_new);
+      if (wave_any(s > m_run[g] + kRescaleLog2)) {
+        float mx = fmaxf(s, __shfl_xor(s, 1));
+        mx = fmaxf(mx, __shfl_xor(mx, 2));
+        mx = fmaxf(mx, __shfl_xor(mx, 4));
+        mx = fmaxf(mx, __shfl_xor(mx, 8));
+        const float m_new = fmaxf(m_run[g], mx);
+        const float alpha = fast_exp2(m_run[g] - m_new);
+        m_run[g] = m_new;
+        l_run[g] *= alpha;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) acc[g][t] *= alpha;
+      }
+      const float e = fast_exp2(s - m_run[g]);
       uint32_t pb;
       float pr;
       if constexpr (kBytes == 2) {
@@ -397,12 +503,10 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeParams p) {
         pb = __float_as_uint(e);
         pr = e;
       }
-      l_run[g] = l_run[g] * alpha + pr;  // token `col`'s weight; summed over lanes at the end
+      l_run[g] += pr;  // token `col`'s weight; summed over lanes at the end
       // Weights of tokens 4*grp .. 4*grp+3, the tokens this lane's V entries hold.
       const uint32_t w0 = __shfl(pb, 4 * grp + 0), w1 = __shfl(pb, 4 * grp + 1);
       const uint32_t w2 = __shfl(pb, 4 * grp + 2), w3 = __shfl(pb, 4 * grp + 3);
-#pragma unroll
-      for (int t = 0; t < NT; ++t) acc[g][t] *= alpha;
       if constexpr (kBytes == 2) {
         const uint32_t p01 = w0 | (w1 << 16), p23 = w2 | (w3 << 16);
 #pragma unroll
@@ -427,30 +531,22 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeParams p) {
     }
   };
 
-  Frag<NCH> fa, fb;
-  int u = wave;
-  bool oka = false, okb = false;
-  if (u < nunits) {
-    const UnitPtrs up = unit_ptrs<D, kBytes>(p, trow, start, u, h);
-    oka = up.ok;
-    load_frag<NCH>(fa, up, lane);
-  }
-  while (u < nunits) {
-    if (u + kWaves < nunits) {
-      const UnitPtrs up = unit_ptrs<D, kBytes>(p, trow, start, u + kWaves, h);
+  int u = u0;
+  while (u < u1) {
+    if (u + 1 < u1) {
+      const UnitPtrs up = unit_ptrs<D, kBytes>(p, trow, start, u + 1, h);
       okb = up.ok;
       load_frag<NCH>(fb, up, lane);
     }
     compute(fa, u, oka);
-    u += kWaves;
-    if (u >= nunits) break;
-    if (u + kWaves < nunits) {
-      const UnitPtrs up = unit_ptrs<D, kBytes>(p, trow, start, u + kWaves, h);
+    if (++u >= u1) break;
+    if (u + 1 < u1) {
+      const UnitPtrs up = unit_ptrs<D, kBytes>(p, trow, start, u + 1, h);
       oka = up.ok;
       load_frag<NCH>(fa, up, lane);
     }
     compute(fb, u, okb);
-    u += kWaves;
+    ++u;
   }
 
 #pragma unroll
@@ -477,6 +573,12 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeParams p) {
     }
   }
   finish_partition<T, D, NG>(p, sm, i, h, j, ctx <= p.P);
+}
+
+template <typename T, int D, int NG>
+__global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeParams p) {
+  __shared__ MergeSmem<D, NG> sm;
+  run_items(p, sm.next, [&](int i, int j, int h) { valu_item<T, D, NG>(p, sm, i, j, h); });
 }
 
 // ---------------------------------------------------------------------------
@@ -522,17 +624,53 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(DecodeParams p) {
     out[static_cast<size_t>(pair) * D + lane + 64 * k] = static_cast<B>(to_storage<T>(acc[k] * inv));
 }
 
+// Persistent grid size: resident workgroups per CU x CUs, cached per kernel
+// and device.
+int persistent_grid(const void* kernel) {
+  static std::mutex mu;
+  static struct {
+    const void* k;
+    int dev, grid;
+  } cache[64];
+  static int n = 0;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  std::lock_guard<std::mutex> lock(mu);
+  for (int c = 0; c < n; ++c)
+    if (cache[c].k == kernel && cache[c].dev == dev) return cache[c].grid;
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kThreads, 0) != hipSuccess) return 0;
+  const int grid = (cus > 0 ? cus : 1) * (per_cu > 0 ? per_cu : 1);
+  if (n < 64) cache[n++] = {kernel, dev, grid};
+  return grid;
+}
+
 template <typename T, int D>
 hipError_t launch_typed(const DecodeParams& p, hipStream_t stream) {
-  const dim3 grid(p.max_parts > 0 ? p.max_parts : 1, p.H, p.S);
+  const void* kern;
   if (p.G >= 3) {
-    hipLaunchKernelGGL((decode_mfma_kernel<T, D>), grid, dim3(kThreads), 0, stream, p);
+    kern = reinterpret_cast<const void*>(&decode_mfma_kernel<T, D>);
   } else if (p.G == 2) {
-    hipLaunchKernelGGL((decode_valu_kernel<T, D, 2>), grid, dim3(kThreads), 0, stream, p);
+    kern = reinterpret_cast<const void*>(&decode_valu_kernel<T, D, 2>);
   } else {
-    hipLaunchKernelGGL((decode_valu_kernel<T, D, 1>), grid, dim3(kThreads), 0, stream, p);
+    kern = reinterpret_cast<const void*>(&decode_valu_kernel<T, D, 1>);
   }
+  const int64_t work_bound = static_cast<int64_t>(p.S) * p.max_parts * p.H;
+  int grid = persistent_grid(kern);
+  if (grid <= 0) return hipErrorInvalidValue;
+  if (grid > work_bound) grid = static_cast<int>(work_bound);
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, p, grid);
   hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (p.G >= 3) {
+    hipLaunchKernelGGL((decode_mfma_kernel<T, D>), dim3(grid), dim3(kThreads), 0, stream, p);
+  } else if (p.G == 2) {
+    hipLaunchKernelGGL((decode_valu_kernel<T, D, 2>), dim3(grid), dim3(kThreads), 0, stream, p);
+  } else {
+    hipLaunchKernelGGL((decode_valu_kernel<T, D, 1>), dim3(grid), dim3(kThreads), 0, stream, p);
+  }
+  e = hipGetLastError();
   if (e != hipSuccess || p.max_parts <= 1) return e;
   const int pairs = p.S * p.Hq;
   hipLaunchKernelGGL((merge_kernel<T, D>), dim3((pairs + kWaves - 1) / kWaves), dim3(kThreads), 0,

@@ -28,9 +28,29 @@ struct DecodeParams {
   float scale_log2;          // scale * log2(e)
   int32_t P;                 // partition tokens
   int32_t max_parts;         // ceil(ctx_cap / P)
+  int32_t* header;           // [0] work items, [1] next work index (device)
+  int2* items;               // [S * max_parts] (sequence, partition), longest first
   float* ws_o;               // [S, Hq, max_parts, D]
   float* ws_ml;              // [S, Hq, max_parts, 2] (max in log2 units, sum)
 };
+
+// Workspace of pa_decode: a small header, the work-item list, and (only when
+// some context spans several partitions) the float32 partition states.
+struct WsLayout {
+  size_t header_off, items_off, o_off, ml_off, total;
+};
+
+inline WsLayout decode_ws_layout(int S, int Hq, int max_parts, int D) {
+  auto align = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
+  WsLayout w;
+  w.header_off = 0;
+  w.items_off = 256;
+  w.o_off = align(w.items_off + static_cast<size_t>(S) * max_parts * sizeof(int2));
+  const size_t parts = max_parts > 1 ? static_cast<size_t>(S) * Hq * max_parts : 0;
+  w.ml_off = align(w.o_off + parts * D * sizeof(float));
+  w.total = align(w.ml_off + parts * 2 * sizeof(float));
+  return w;
+}
 
 hipError_t launch_write_kv(const PoolGeom& g, int layer, const void* k, const void* v,
                            const int32_t* slots, int num_tokens, hipStream_t stream);
