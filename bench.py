@@ -43,6 +43,9 @@ def parse():
     ap.add_argument("--cpu-budget-s", type=float, default=20.0,
                     help="wall-clock budget of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calib-blocks", type=int, default=0,
+                    help="after timing, copy this many whole blocks with pa_copy_blocks (a copy "
+                         "of known size for scaling hardware byte counters)")
     return ap.parse_args()
 
 
@@ -197,6 +200,14 @@ def main():
             "avg_launch_ms": round(dec_ms, 5),
         },
     }
+    if args.copy_calib_blocks > 0:
+        n = min(args.copy_calib_blocks, w.num_blocks // 2)
+        pairs = torch.stack([torch.arange(n), torch.arange(n) + n], dim=1).to(torch.int32).cuda()
+        pool.copy_blocks(pairs)
+        torch.cuda.synchronize()
+        nbytes = n * L * 2 * w.num_kv_heads * w.block_size * w.head_dim * eb
+        log(f"[bench] copy calibration: {n} blocks, {nbytes} bytes read and {nbytes} written")
+        res["copy_calibration_bytes"] = nbytes
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_budget_s)
     print(json.dumps(res), flush=True)

@@ -1,7 +1,8 @@
 """Build the gfx950 shared library libpa.so in-tree with hipcc.
 
-    python -m paged_kv_cache_337_amd.build
+    python paged_kv_cache_337_amd/build.py
 
+(run as a script: importing the package itself needs the library.)
 Every call recompiles (the objects are cheap); the result lands next to this
 file, where the Python binding loads it.
 """
