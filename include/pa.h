@@ -48,7 +48,7 @@
  *
  * Supported shapes: block_size a positive multiple of 16 (up to 256),
  * head_dim 64 or 128, dtypes F32 / F16 / BF16, query heads per KV head
- * G = num_q_heads / num_kv_heads with 1 <= G <= 16 (F32: G in {1, 2, 4, 8}).
+ * G = num_q_heads / num_kv_heads with 1 <= G <= 16.
  */
 #ifndef PA_H
 #define PA_H
@@ -133,7 +133,9 @@ int pa_write_kv(pa_pool* pool, int layer, const void* k, const void* v,
 /* Device workspace bytes pa_decode needs: a work-item list (one entry per
  * (sequence, partition) of up to max_context_len tokens) and, when contexts
  * can span several partitions, float32 partial outputs plus running max and
- * sum per query head and partition.  Always > 0 for valid arguments. */
+ * sum per query head and partition.  Always > 0 for valid arguments.
+ * pa_decode initialises what it needs itself; calls that share one workspace
+ * must not overlap. */
 size_t pa_decode_workspace_bytes(const pa_pool* pool, int num_seqs, int num_q_heads,
                                  int max_context_len, int partition_tokens);
 

@@ -223,7 +223,8 @@ int pa_decode(const pa_pool* pool, int layer, const void* q, int num_seqs, int n
     if (!std::isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "scale must be finite");
     const int bs = d.block_size;
     int P = partition_tokens;
-    if (P == 0) P = auto_partition(bs);
+    const bool automatic = P == 0;
+    if (automatic) P = auto_partition(bs);
     if (P < 0 || P % bs || P % 16) return fail(PA_ERR_INVALID_ARG, "partition_tokens must be a multiple of block_size");
     const int64_t cap64 = std::min<int64_t>(max_context_len, static_cast<int64_t>(max_blocks_per_seq) * bs);
     const int ctx_cap = static_cast<int>(cap64);
@@ -269,6 +270,7 @@ int pa_decode(const pa_pool* pool, int layer, const void* q, int num_seqs, int n
     p.ctx_cap = ctx_cap;
     p.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
     p.P = P;
+    p.auto_partition = automatic ? 1 : 0;
     p.max_parts = max_parts;
     char* ws = static_cast<char*>(workspace);
     p.header = reinterpret_cast<int32_t*>(ws + wl.header_off);

@@ -19,7 +19,11 @@
 //      one.  A sparse grid with one workgroup per possible partition spends
 //      most of its time dispatching empty workgroups; this one does not.
 //   3. merge_kernel combines the partition states of multi-partition
-//      sequences by log-sum-exp weighting.
+//      sequences by log-sum-exp weighting, one wave per (sequence, query head).
+//      (Merging inside the decode kernel, by the workgroup that finishes a
+//      sequence's last partition, needs either agent-scope fences -- a whole-L2
+//      writeback and invalidate per partition on gfx950 -- or a wait for
+//      device-coherent stores per partition; both cost more than this launch.)
 //
 // Inside an item the partition is cut into 16-token units (a 16-token
 // sub-tile of one block); wave w takes a contiguous run of units, loading the
@@ -61,30 +65,18 @@ constexpr float kNegInf = -__builtin_inff();
 constexpr float kRescaleLog2 = 8.0f;  // raise the reference only past 2^8
 constexpr int kPlanThreads = 1024;
 constexpr int kPlanBins = 1024;       // partial items sorted by 16-token units
+#ifndef PA_PREFETCH_UNITS
+#define PA_PREFETCH_UNITS 1
+#endif
+constexpr int kPrefetch = PA_PREFETCH_UNITS;  // units in flight ahead of the one computed
+#ifndef PA_ITEMS_PER_WG
+#define PA_ITEMS_PER_WG 4
+#endif
 
-struct UnitPtrs {
-  const char* k;  // K sub-tile base (bytes)
-  const char* v;  // V sub-tile base (bytes)
-  bool ok;
-};
-
-// Location of 16-token unit u of the partition starting at token `start`.
-template <int D, int kBytes>
-__device__ __forceinline__ UnitPtrs unit_ptrs(const DecodeParams& p, const int32_t* trow, int start,
-                                              int u, int h) {
-  const int p0 = start + u * 16;
-  const int lb = p0 / p.bs;
-  const int sub = (p0 - lb * p.bs) >> 4;
-  const int32_t b = trow[lb];
-  UnitPtrs r;
-  r.ok = (b >= 0) & (b < p.N);
-  const int32_t bb = r.ok ? b : 0;
-  const size_t region = p.layer_off + (static_cast<size_t>(bb) * p.H + h) * (2 * static_cast<size_t>(p.bs) * D);
-  const char* base = static_cast<const char*>(p.pool) + region * kBytes;
-  r.k = base + static_cast<size_t>(sub) * 16 * D * kBytes;
-  r.v = base + (static_cast<size_t>(p.bs) + static_cast<size_t>(sub) * 16) * D * kBytes;
-  return r;
-}
+// Target of the loads issued for units outside a wave's range or with an
+// invalid block id: every wave then issues the same loads per unit, so each
+// unit waits for its own loads only (8 KiB: the largest per-unit load span).
+__device__ __align__(256) uint4 g_dummy_unit[512];
 
 // Per-thread view of one unit: NCH 16-byte chunks of K and of V.
 template <int NCH>
@@ -93,14 +85,114 @@ struct Frag {
   uint4 v[NCH];
 };
 
-template <int NCH>
-__device__ __forceinline__ void load_frag(Frag<NCH>& f, const UnitPtrs& u, int lane) {
-  const uint4* kp = reinterpret_cast<const uint4*>(u.k) + lane;
-  const uint4* vp = reinterpret_cast<const uint4*>(u.v) + lane;
+// The 16-token units of one wave's run [u0, u1) of a partition, located in
+// issue order.  The run's block ids (at most 64 logical blocks) are held one
+// per lane and read out with v_readlane, so locating a unit is scalar
+// arithmetic with no memory access.
+template <int D, int kBytes>
+struct UnitStream {
+  const char* layer_base;  // pool base + layer offset (bytes)
+  const int32_t* trow;     // block-table row of the sequence
+  int max_blocks, bs, N, H, h;
+  int u1;                  // end of the run
+  int next;                // next unit to locate
+  int lb, sub;             // its logical block and 16-token sub-tile
+  int lb_base;             // logical block of ids lane 0
+  int32_t ids;
+
+  __device__ __forceinline__ void init(const DecodeParams& p, const int32_t* row, int start, int u0,
+                                       int u_end, int head, int lane) {
+    layer_base = static_cast<const char*>(p.pool) + p.layer_off * kBytes;
+    trow = row;
+    max_blocks = p.max_blocks;
+    bs = p.bs;
+    N = p.N;
+    H = p.H;
+    h = head;
+    u1 = u_end;
+    next = u0;
+    const int p0 = start + u0 * 16;
+    lb = p0 / bs;
+    sub = (p0 - lb * bs) >> 4;
+    load_ids(lane);
+  }
+
+  __device__ __forceinline__ void load_ids(int lane) {
+    lb_base = lb;
+    const int k = lb + lane;
+    ids = k < max_blocks ? trow[k] : -1;
+  }
+
+  // Bases of the K and V sub-tiles of unit `next`, then advance.  Returns
+  // false, with both bases at the dummy, past the run or for an invalid id.
+  __device__ __forceinline__ bool locate(const char*& kp, const char*& vp, int lane) {
+    kp = vp = reinterpret_cast<const char*>(g_dummy_unit);
+    if (next >= u1) return false;
+    const int32_t b = __builtin_amdgcn_readlane(ids, lb - lb_base);
+    const int s = sub;
+    ++next;
+    if (++sub * 16 == bs) {
+      sub = 0;
+      ++lb;
+    }
+    if (b < 0 || b >= N) return false;
+    const size_t region = (static_cast<size_t>(b) * H + h) * (2 * static_cast<size_t>(bs) * D);
+    kp = layer_base + (region + static_cast<size_t>(s) * 16 * D) * kBytes;
+    vp = layer_base + (region + static_cast<size_t>(bs) * D + static_cast<size_t>(s) * 16 * D) * kBytes;
+    return true;
+  }
+
+  template <int NCH>
+  __device__ __forceinline__ bool issue(Frag<NCH>& f, int lane) {
+    const char *kb, *vb;
+    const bool ok = locate(kb, vb, lane);
+    const uint4* kp = reinterpret_cast<const uint4*>(kb) + lane;
+    const uint4* vp = reinterpret_cast<const uint4*>(vb) + lane;
 #pragma unroll
-  for (int c = 0; c < NCH; ++c) f.k[c] = load_stream16(kp + 64 * c);
+    for (int c = 0; c < NCH; ++c) f.k[c] = load_stream16(kp + 64 * c);
 #pragma unroll
-  for (int c = 0; c < NCH; ++c) f.v[c] = load_stream16(vp + 64 * c);
+    for (int c = 0; c < NCH; ++c) f.v[c] = load_stream16(vp + 64 * c);
+    return ok;
+  }
+};
+
+// Runs compute(frag, u, ok) over units [u0, u1) with the loads of the next PF
+// units in flight.  Loads are issued unconditionally (past the run they read
+// the dummy), so the wait before each unit covers exactly that unit's loads.
+template <int PF, int NCH, typename Stream, typename Compute>
+__device__ __forceinline__ void stream_piece(Stream& st, int u0, int u1, int lane, Compute&& compute) {
+  constexpr int NB = PF + 1;
+  Frag<NCH> f[NB];
+  bool ok[NB];
+#pragma unroll
+  for (int s = 0; s < PF; ++s) ok[s] = st.template issue<NCH>(f[s], lane);
+  for (int u = u0; u < u1; u += NB) {
+#pragma unroll
+    for (int s = 0; s < NB; ++s) {
+      ok[(s + PF) % NB] = st.template issue<NCH>(f[(s + PF) % NB], lane);
+      if (u + s < u1) compute(f[s], u + s, ok[s]);
+    }
+  }
+}
+
+// First unit of the logical block 64 blocks after that of unit u: runs are
+// cut there, so that one load of block ids covers each piece.
+__device__ __forceinline__ int piece_end(int bs, int start, int u) {
+  const int p0 = start + u * 16;
+  return ((p0 / bs + 64) * bs - start) >> 4;
+}
+
+template <int PF, int NCH, int D, int kBytes, typename Compute>
+__device__ __forceinline__ void stream_units(const DecodeParams& p, const int32_t* trow, int start,
+                                             int u0, int u1, int h, int lane, Compute&& compute) {
+  UnitStream<D, kBytes> st;
+  for (int a = u0; a < u1;) {
+    int b = piece_end(p.bs, start, a);
+    b = b < u1 ? b : u1;
+    st.init(p, trow, start, a, b, h, lane);
+    stream_piece<PF, NCH>(st, a, b, lane, compute);
+    a = b;
+  }
 }
 
 // Zero V elements of tokens >= valid (their slots may hold anything, and
@@ -140,9 +232,15 @@ struct MergeSmem {
   int next;
 };
 
+template <typename T>
+__device__ __forceinline__ void store_out(const DecodeParams& p, size_t row, int d, int D, float o) {
+  using B = typename T::bits;
+  static_cast<B*>(p.out)[row * D + d] = static_cast<B>(to_storage<T>(o));
+}
+
 template <typename T, int D, int GMAX>
 __device__ __forceinline__ void finish_partition(const DecodeParams& p, MergeSmem<D, GMAX>& sm,
-                                                 int i, int h, int j, bool single) {
+                                                 int i, int h, int j, int np) {
   __syncthreads();
   const int G = p.G;
   for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
@@ -158,14 +256,12 @@ __device__ __forceinline__ void finish_partition(const DecodeParams& p, MergeSme
       L += f * sm.l[w][g];
       O += f * sm.o[w][g][d];
     }
-    const int qh = h * G + g;
+    const size_t row = static_cast<size_t>(i) * p.Hq + h * G + g;
     const float o = (L > 0.f) ? O / L : 0.f;
-    if (single) {
-      using B = typename T::bits;
-      B* out = static_cast<B*>(p.out);
-      out[(static_cast<size_t>(i) * p.Hq + qh) * D + d] = static_cast<B>(to_storage<T>(o));
+    if (np == 1) {
+      store_out<T>(p, row, d, D, o);
     } else {
-      const size_t e = (static_cast<size_t>(i) * p.Hq + qh) * p.max_parts + j;
+      const size_t e = row * p.max_parts + j;
       p.ws_o[e * D + d] = o;
       if (d == 0) {
         p.ws_ml[2 * e] = M;
@@ -175,10 +271,21 @@ __device__ __forceinline__ void finish_partition(const DecodeParams& p, MergeSme
   }
 }
 
+// Context length of sequence i clamped to [0, ctx_cap] (per lane).
 __device__ __forceinline__ int clamp_ctx(const DecodeParams& p, int i) {
   int c = p.ctx[i];
   c = c < 0 ? 0 : c;
   return c > p.ctx_cap ? p.ctx_cap : c;
+}
+
+// The same for a sequence index that is uniform across the wave.
+__device__ __forceinline__ int clamp_ctx_uniform(const DecodeParams& p, int i) {
+  return __builtin_amdgcn_readfirstlane(clamp_ctx(p, i));
+}
+
+// Partitions of a context of `ctx` tokens (one for an empty context).
+__device__ __forceinline__ int num_parts(int P, int ctx) {
+  return ctx > P ? (ctx + P - 1) / P : 1;
 }
 
 // Wave-uniform "any lane" test.
@@ -187,38 +294,91 @@ __device__ __forceinline__ bool wave_any(bool x) { return __builtin_amdgcn_ballo
 // ---------------------------------------------------------------------------
 // Work items: plan kernel.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeParams p, int grid) {
+// Partition size of an automatic decode: as large as keeps about
+// kItemsPerWorkgroup work items per workgroup of the persistent grid (fewer,
+// longer items cost fewer item starts and fewer partition merges), never
+// below the caller's minimum, at most kMaxAutoPartition tokens, a multiple of
+// the block size.
+constexpr int kItemsPerWorkgroup = PA_ITEMS_PER_WG;
+constexpr int kMaxAutoPartition = 4096;
+
+__global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeParams p) {
   __shared__ int cnt[kPlanBins];
   __shared__ int off[kPlanBins];
-  const int P = p.P;
-  const int top = (P >> 4) - 1 < kPlanBins - 1 ? (P >> 4) - 1 : kPlanBins - 1;
+  __shared__ int wsum[kPlanThreads / 64];
+  __shared__ long long wtok[kPlanThreads / 64];
+  __shared__ int sP;
+  constexpr int kCached = 4;  // context lengths kept in registers per thread
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int cc[kCached];
+  long long tok = 0;
+#pragma unroll
+  for (int k = 0; k < kCached; ++k) {
+    const int i = threadIdx.x + k * kPlanThreads;
+    cc[k] = i < p.S ? clamp_ctx(p, i) : 0;
+    tok += cc[k];
+  }
+  for (int i = threadIdx.x + kCached * kPlanThreads; i < p.S; i += kPlanThreads) tok += clamp_ctx(p, i);
+  auto ctx_of = [&](int k, int i) { return k < kCached ? cc[k] : clamp_ctx(p, i); };
   for (int b = threadIdx.x; b < kPlanBins; b += kPlanThreads) cnt[b] = 0;
+  if (p.auto_partition) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) tok += __shfl_xor(tok, o);
+    if (lane == 0) wtok[wave] = tok;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      long long total = 0;
+      for (int w = 0; w < kPlanThreads / 64; ++w) total += wtok[w];
+      total *= p.H;
+      const long long per = (total + static_cast<long long>(p.grid) * kItemsPerWorkgroup - 1) /
+                            (static_cast<long long>(p.grid) * kItemsPerWorkgroup);
+      long long P = (per + p.bs - 1) / p.bs * p.bs;
+      const int cap = kMaxAutoPartition / p.bs * p.bs;
+      P = P > cap ? cap : P;
+      sP = static_cast<int>(P < p.P ? p.P : P);
+    }
+  } else if (threadIdx.x == 0) {
+    sP = p.P;
+  }
   __syncthreads();
+  const int P = sP;
+  const int top = (P >> 4) - 1 < kPlanBins - 1 ? (P >> 4) - 1 : kPlanBins - 1;
   auto bin_of = [&](int ntok) {
     const int units = (ntok + 15) >> 4;
     const int b = units > 0 ? units - 1 : 0;
     return b < top ? b : top;
   };
-  for (int i = threadIdx.x; i < p.S; i += kPlanThreads) {
-    const int c = clamp_ctx(p, i);
+  for (int k = 0, i = threadIdx.x; i < p.S; ++k, i += kPlanThreads) {
+    const int c = ctx_of(k, i);
     const int nfull = c / P, rem = c - nfull * P;
     if (nfull > 0) atomicAdd(&cnt[bin_of(P)], nfull);
     if (rem > 0 || c == 0) atomicAdd(&cnt[bin_of(rem)], 1);
   }
   __syncthreads();
-  // Exclusive prefix over bins in descending size order: off[b] = sum_{b' > b} cnt[b'].
-  if (threadIdx.x == 0) {
-    int run = 0;
-    for (int b = kPlanBins - 1; b >= 0; --b) {
-      off[b] = run;
-      run += cnt[b];
-    }
-    p.header[0] = run;
-    p.header[1] = grid;  // indices below `grid` are taken by blockIdx at launch
+  // off[b] = sum of cnt[b'] over b' > b: an exclusive scan in descending bin
+  // order, thread t owning bin kPlanBins - 1 - t.
+  static_assert(kPlanBins == kPlanThreads, "one bin per thread");
+  const int bin = kPlanBins - 1 - threadIdx.x;
+  const int val = cnt[bin];
+  int x = val;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) wsum[wave] = x;
+  __syncthreads();
+  int before = 0;
+  for (int w = 0; w < wave; ++w) before += wsum[w];
+  off[bin] = before + x - val;
+  if (threadIdx.x == kPlanThreads - 1) {
+    p.header[0] = before + x;
+    p.header[1] = 0;
+    p.header[2] = P;
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < p.S; i += kPlanThreads) {
-    const int c = clamp_ctx(p, i);
+  for (int k = 0, i = threadIdx.x; i < p.S; ++k, i += kPlanThreads) {
+    const int c = ctx_of(k, i);
     const int nfull = c / P, rem = c - nfull * P;
     if (nfull > 0) {
       const int base = atomicAdd(&off[bin_of(P)], nfull);
@@ -228,36 +388,49 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeParams p, int 
   }
 }
 
-// Persistent driver: the workgroup takes work index `cur` = item * H + head.
+// Persistent driver: the workgroup takes work indices `cur` = item * H + head
+// from the counter until none is left, fetching the next index while it works
+// on the current one.  Workgroups that start after the work has run out exit
+// at once, so the grid may exceed what is resident.
 template <typename Item>
 __device__ __forceinline__ void run_items(const DecodeParams& p, int& next_slot, Item&& item) {
   const int total = p.header[0] * p.H;
-  int cur = blockIdx.x;
+  if (threadIdx.x == 0) next_slot = atomicAdd(&p.header[1], 1);
+  __syncthreads();
+  int cur = __builtin_amdgcn_readfirstlane(next_slot);
   while (cur < total) {
     int nxt = 0;
     if (threadIdx.x == 0) nxt = atomicAdd(&p.header[1], 1);
+#ifdef PA_HEAD_OUTER
+    const int nit = p.header[0];
+    const int hh = cur / nit;
+    const int it = cur - hh * nit;
+#else
     const int it = cur / p.H;
+    const int hh = cur - it * p.H;
+#endif
     const int2 sj = p.items[it];
-    item(sj.x, sj.y, cur - it * p.H);
+    item(__builtin_amdgcn_readfirstlane(sj.x), __builtin_amdgcn_readfirstlane(sj.y), hh);
     if (threadIdx.x == 0) next_slot = nxt;
     __syncthreads();
-    cur = next_slot;
+    cur = __builtin_amdgcn_readfirstlane(next_slot);
   }
 }
 
 // ---------------------------------------------------------------------------
 // MFMA path: 3 <= G <= 16 query heads per kv head.
 // ---------------------------------------------------------------------------
-template <typename T, int D>
-__device__ __forceinline__ void mfma_item(const DecodeParams& p, MergeSmem<D, 16>& sm, int i, int j, int h) {
+template <typename T, int D, int GM>
+__device__ __forceinline__ void mfma_item(const DecodeParams& p, int P, MergeSmem<D, GM>& sm, int i, int j,
+                                          int h) {
   constexpr int kBytes = T::kBytes;
   constexpr int E = 16 / kBytes;
   constexpr int NCH = D / (4 * E);  // 16-byte chunks per lane per sub-tile
   constexpr int NT = D / 16;        // 16-wide head_dim tiles of the output
 
-  const int ctx = clamp_ctx(p, i);
-  const int start = j * p.P;
-  const int ntok = ctx - start < p.P ? ctx - start : p.P;
+  const int ctx = clamp_ctx_uniform(p, i);
+  const int start = j * P;
+  const int ntok = ctx - start < P ? ctx - start : P;
   const int nunits = ntok > 0 ? (ntok + 15) >> 4 : 0;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -267,14 +440,6 @@ __device__ __forceinline__ void mfma_item(const DecodeParams& p, MergeSmem<D, 16
   const int per = (nunits + kWaves - 1) / kWaves;
   const int u0 = wave * per;
   const int u1 = u0 + per < nunits ? u0 + per : nunits;
-
-  Frag<NCH> fa, fb;
-  bool oka = false, okb = false;
-  if (u0 < u1) {
-    const UnitPtrs up = unit_ptrs<D, kBytes>(p, trow, start, u0, h);
-    oka = up.ok;
-    load_frag<NCH>(fa, up, lane);
-  }
 
   // Query rows as the B operand of S = K.Q^T: lane holds head `col`,
   // the head_dim entries matching its K chunk entries.
@@ -362,62 +527,49 @@ __device__ __forceinline__ void mfma_item(const DecodeParams& p, MergeSmem<D, 16
     }
   };
 
-  int u = u0;
-  while (u < u1) {
-    if (u + 1 < u1) {
-      const UnitPtrs up = unit_ptrs<D, kBytes>(p, trow, start, u + 1, h);
-      okb = up.ok;
-      load_frag<NCH>(fb, up, lane);
-    }
-    compute(fa, u, oka);
-    if (++u >= u1) break;
-    if (u + 1 < u1) {
-      const UnitPtrs up = unit_ptrs<D, kBytes>(p, trow, start, u + 1, h);
-      oka = up.ok;
-      load_frag<NCH>(fa, up, lane);
-    }
-    compute(fb, u, okb);
-    ++u;
-  }
+  stream_units<kPrefetch, NCH, D, kBytes>(p, trow, start, u0, u1, h, lane, compute);
 
   // Column sums over the four lane groups.
   float l_col = l_part + __shfl_xor(l_part, 16);
   l_col += __shfl_xor(l_col, 32);
-  if (lane < 16) {
+  if (lane < GM) {  // lane = query-head column
     sm.m[wave][lane] = m_col;
     sm.l[wave][lane] = l_col;
   }
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int g = 4 * grp + r;
-    if (g < G) {
+    if (g < GM && g < G) {
 #pragma unroll
       for (int t = 0; t < NT; ++t) sm.o[wave][g][t * 16 + col] = acc[t][r];
     }
   }
-  finish_partition<T, D, 16>(p, sm, i, h, j, ctx <= p.P);
+  finish_partition<T, D, GM>(p, sm, i, h, j, num_parts(P, ctx));
 }
 
-template <typename T, int D>
+// GM: query heads per kv head rounded up to 4, 8 or 16 (sizes the LDS merge).
+template <typename T, int D, int GM>
 __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
-  __shared__ MergeSmem<D, 16> sm;
-  run_items(p, sm.next, [&](int i, int j, int h) { mfma_item<T, D>(p, sm, i, j, h); });
+  __shared__ MergeSmem<D, GM> sm;
+  const int P = __builtin_amdgcn_readfirstlane(p.header[2]);
+  run_items(p, sm.next, [&](int i, int j, int h) { mfma_item<T, D, GM>(p, P, sm, i, j, h); });
 }
 
 // ---------------------------------------------------------------------------
 // VALU path: NG (1 or 2) query heads per kv head.
 // ---------------------------------------------------------------------------
 template <typename T, int D, int NG>
-__device__ __forceinline__ void valu_item(const DecodeParams& p, MergeSmem<D, NG>& sm, int i, int j, int h) {
+__device__ __forceinline__ void valu_item(const DecodeParams& p, int P, MergeSmem<D, NG>& sm, int i, int j,
+                                          int h) {
   constexpr int kBytes = T::kBytes;
   constexpr int E = 16 / kBytes;
   constexpr int NCH = D / (4 * E);
   constexpr int R = E / 4;          // 16-wide d tiles per V chunk
   constexpr int NT = D / 16;        // d values per lane in P.V (d = t*16 + col)
 
-  const int ctx = clamp_ctx(p, i);
-  const int start = j * p.P;
-  const int ntok = ctx - start < p.P ? ctx - start : p.P;
+  const int ctx = clamp_ctx_uniform(p, i);
+  const int start = j * P;
+  const int ntok = ctx - start < P ? ctx - start : P;
   const int nunits = ntok > 0 ? (ntok + 15) >> 4 : 0;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -426,14 +578,6 @@ __device__ __forceinline__ void valu_item(const DecodeParams& p, MergeSmem<D, NG
   const int per = (nunits + kWaves - 1) / kWaves;
   const int u0 = wave * per;
   const int u1 = u0 + per < nunits ? u0 + per : nunits;
-
-  Frag<NCH> fa, fb;
-  bool oka = false, okb = false;
-  if (u0 < u1) {
-    const UnitPtrs up = unit_ptrs<D, kBytes>(p, trow, start, u0, h);
-    oka = up.ok;
-    load_frag<NCH>(fa, up, lane);
-  }
 
   // q entries matching this lane's K chunk entries: d = (c*4 + grp)*E + e.
   uint4 qv[NG][NCH];
@@ -531,23 +675,7 @@ __device__ __forceinline__ void valu_item(const DecodeParams& p, MergeSmem<D, NG
     }
   };
 
-  int u = u0;
-  while (u < u1) {
-    if (u + 1 < u1) {
-      const UnitPtrs up = unit_ptrs<D, kBytes>(p, trow, start, u + 1, h);
-      okb = up.ok;
-      load_frag<NCH>(fb, up, lane);
-    }
-    compute(fa, u, oka);
-    if (++u >= u1) break;
-    if (u + 1 < u1) {
-      const UnitPtrs up = unit_ptrs<D, kBytes>(p, trow, start, u + 1, h);
-      oka = up.ok;
-      load_frag<NCH>(fa, up, lane);
-    }
-    compute(fb, u, okb);
-    ++u;
-  }
+  stream_units<kPrefetch, NCH, D, kBytes>(p, trow, start, u0, u1, h, lane, compute);
 
 #pragma unroll
   for (int g = 0; g < NG; ++g) {
@@ -572,13 +700,14 @@ __device__ __forceinline__ void valu_item(const DecodeParams& p, MergeSmem<D, NG
       for (int t = 0; t < NT; ++t) sm.o[wave][g][t * 16 + col] = acc[g][t];
     }
   }
-  finish_partition<T, D, NG>(p, sm, i, h, j, ctx <= p.P);
+  finish_partition<T, D, NG>(p, sm, i, h, j, num_parts(P, ctx));
 }
 
 template <typename T, int D, int NG>
 __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeParams p) {
   __shared__ MergeSmem<D, NG> sm;
-  run_items(p, sm.next, [&](int i, int j, int h) { valu_item<T, D, NG>(p, sm, i, j, h); });
+  const int P = __builtin_amdgcn_readfirstlane(p.header[2]);
+  run_items(p, sm.next, [&](int i, int j, int h) { valu_item<T, D, NG>(p, P, sm, i, j, h); });
 }
 
 // ---------------------------------------------------------------------------
@@ -589,33 +718,54 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(DecodeParams p) {
   const int lane = threadIdx.x & 63;
   const int pair = blockIdx.x * kWaves + (threadIdx.x >> 6);
   if (pair >= p.S * p.Hq) return;
-  const int i = pair / p.Hq;
-  const int ctx = clamp_ctx(p, i);
-  if (ctx <= p.P) return;  // written directly by the partition kernel
-  int np = (ctx + p.P - 1) / p.P;
+  const int P = __builtin_amdgcn_readfirstlane(p.header[2]);
+  const int ctx = clamp_ctx_uniform(p, pair / p.Hq);
+  if (ctx <= P) return;  // written directly by the partition kernel
+  int np = (ctx + P - 1) / P;
   np = np > p.max_parts ? p.max_parts : np;
   const size_t e0 = static_cast<size_t>(pair) * p.max_parts;
   const float* ml = p.ws_ml + 2 * e0;
 
+  // Partition states are held one per lane, 64 partitions at a time.
   float M = kNegInf;
-  for (int jj = lane; jj < np; jj += 64) M = fmaxf(M, ml[2 * jj]);
+  for (int c0 = 0; c0 < np; c0 += 64)
+    if (c0 + lane < np) M = fmaxf(M, ml[2 * (c0 + lane)]);
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
-  float L = 0.f;
-  for (int jj = lane; jj < np; jj += 64) L += ml[2 * jj + 1] * fast_exp2(ml[2 * jj] - M);
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) L += __shfl_xor(L, o);
 
-  constexpr int PER = D / 64;
+  constexpr int PER = D / 64;  // head_dim entries per lane
   float acc[PER];
 #pragma unroll
   for (int k = 0; k < PER; ++k) acc[k] = 0.f;
-  for (int jj = 0; jj < np; ++jj) {
-    const float w = ml[2 * jj + 1] * fast_exp2(ml[2 * jj] - M);
-    const float* o = p.ws_o + (e0 + jj) * D;
+  float L = 0.f;
+  for (int c0 = 0; c0 < np; c0 += 64) {
+    const int jj = c0 + lane;
+    const float mj = jj < np ? ml[2 * jj] : kNegInf;
+    const float wj = (mj == kNegInf) ? 0.f : ml[2 * jj + 1] * fast_exp2(mj - M);
+    L += wj;
+    const int n = np - c0 < 64 ? np - c0 : 64;
+    // Eight partitions per step, their loads issued together.
+    for (int t = 0; t < n; t += 8) {
+      float o[8][PER];
 #pragma unroll
-    for (int k = 0; k < PER; ++k) acc[k] = fmaf(w, o[lane + 64 * k], acc[k]);
+      for (int u = 0; u < 8; ++u) {
+        const int r = t + u < n ? t + u : n - 1;
+        const float* src = p.ws_o + (e0 + c0 + r) * D + lane;
+#pragma unroll
+        for (int k = 0; k < PER; ++k) o[u][k] = src[64 * k];
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const float w = t + u < n ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(
+                                                         __builtin_bit_cast(int, wj), t + u))
+                                  : 0.f;
+#pragma unroll
+        for (int k = 0; k < PER; ++k) acc[k] = fmaf(w, o[u][k], acc[k]);
+      }
+    }
   }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) L += __shfl_xor(L, o);
   using B = typename T::bits;
   B* out = static_cast<B*>(p.out);
   const float inv = (L > 0.f) ? 1.f / L : 0.f;
@@ -624,8 +774,9 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(DecodeParams p) {
     out[static_cast<size_t>(pair) * D + lane + 64 * k] = static_cast<B>(to_storage<T>(acc[k] * inv));
 }
 
-// Persistent grid size: resident workgroups per CU x CUs, cached per kernel
-// and device.
+// Persistent grid size: workgroups resident per CU (the runtime's occupancy
+// for this kernel's registers, accumulation registers and LDS) x CUs, cached
+// per kernel and device.
 int persistent_grid(const void* kernel) {
   static std::mutex mu;
   static struct {
@@ -641,36 +792,52 @@ int persistent_grid(const void* kernel) {
   int cus = 0, per_cu = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kThreads, 0) != hipSuccess) return 0;
+#ifdef PA_WG_PER_CU
+  per_cu = PA_WG_PER_CU;
+#endif
   const int grid = (cus > 0 ? cus : 1) * (per_cu > 0 ? per_cu : 1);
   if (n < 64) cache[n++] = {kernel, dev, grid};
   return grid;
 }
 
-template <typename T, int D>
-hipError_t launch_typed(const DecodeParams& p, hipStream_t stream) {
+template <typename T, int D, int GM>
+hipError_t launch_decode_kernel(DecodeParams p, hipStream_t stream) {
   const void* kern;
-  if (p.G >= 3) {
-    kern = reinterpret_cast<const void*>(&decode_mfma_kernel<T, D>);
-  } else if (p.G == 2) {
-    kern = reinterpret_cast<const void*>(&decode_valu_kernel<T, D, 2>);
+  if constexpr (GM == 1 || GM == 2) {
+    kern = reinterpret_cast<const void*>(&decode_valu_kernel<T, D, GM>);
   } else {
-    kern = reinterpret_cast<const void*>(&decode_valu_kernel<T, D, 1>);
+    kern = reinterpret_cast<const void*>(&decode_mfma_kernel<T, D, GM>);
   }
   const int64_t work_bound = static_cast<int64_t>(p.S) * p.max_parts * p.H;
   int grid = persistent_grid(kern);
   if (grid <= 0) return hipErrorInvalidValue;
   if (grid > work_bound) grid = static_cast<int>(work_bound);
-  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, p, grid);
+  p.grid = grid;
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (p.G >= 3) {
-    hipLaunchKernelGGL((decode_mfma_kernel<T, D>), dim3(grid), dim3(kThreads), 0, stream, p);
-  } else if (p.G == 2) {
-    hipLaunchKernelGGL((decode_valu_kernel<T, D, 2>), dim3(grid), dim3(kThreads), 0, stream, p);
+  if constexpr (GM == 1 || GM == 2) {
+    hipLaunchKernelGGL((decode_valu_kernel<T, D, GM>), dim3(grid), dim3(kThreads), 0, stream, p);
   } else {
-    hipLaunchKernelGGL((decode_valu_kernel<T, D, 1>), dim3(grid), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((decode_mfma_kernel<T, D, GM>), dim3(grid), dim3(kThreads), 0, stream, p);
   }
-  e = hipGetLastError();
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t launch_typed(const DecodeParams& p, hipStream_t stream) {
+  hipError_t e;
+  if (p.G == 1) {
+    e = launch_decode_kernel<T, D, 1>(p, stream);
+  } else if (p.G == 2) {
+    e = launch_decode_kernel<T, D, 2>(p, stream);
+  } else if (p.G <= 4) {
+    e = launch_decode_kernel<T, D, 4>(p, stream);
+  } else if (p.G <= 8) {
+    e = launch_decode_kernel<T, D, 8>(p, stream);
+  } else {
+    e = launch_decode_kernel<T, D, 16>(p, stream);
+  }
   if (e != hipSuccess || p.max_parts <= 1) return e;
   const int pairs = p.S * p.Hq;
   hipLaunchKernelGGL((merge_kernel<T, D>), dim3((pairs + kWaves - 1) / kWaves), dim3(kThreads), 0,

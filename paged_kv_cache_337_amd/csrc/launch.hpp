@@ -26,9 +26,11 @@ struct DecodeParams {
   int32_t S, Hq, G;
   int32_t ctx_cap;           // min(max_context_len, max_blocks * bs)
   float scale_log2;          // scale * log2(e)
-  int32_t P;                 // partition tokens
+  int32_t P;                 // partition tokens (the minimum when automatic)
+  int32_t auto_partition;    // 1: the plan kernel may raise P (header[2])
+  int32_t grid;              // workgroups of the decode kernel
   int32_t max_parts;         // ceil(ctx_cap / P)
-  int32_t* header;           // [0] work items, [1] next work index (device)
+  int32_t* header;           // [0] work items, [1] next work index, [2] P used (device)
   int2* items;               // [S * max_parts] (sequence, partition), longest first
   float* ws_o;               // [S, Hq, max_parts, D]
   float* ws_ml;              // [S, Hq, max_parts, 2] (max in log2 units, sum)
