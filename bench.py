@@ -53,6 +53,23 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+def counter_traffic(workload: str):
+    """HBM bytes per pa_decode call from the committed rocprofv3 counter record
+    of this workload (FETCH_SIZE + WRITE_SIZE, scaled by a copy of known size),
+    or None when the decode kernel source changed since it was taken."""
+    import hashlib
+    rec = os.path.join(ROOT, "profiles", "decode_llama3_8b_b256.traffic.json")
+    if not os.path.exists(rec):
+        return None
+    with open(rec) as f:
+        r = json.load(f)
+    with open(os.path.join(ROOT, r["kernel_source"]), "rb") as f:
+        sha = hashlib.sha256(f.read()).hexdigest()
+    if r.get("workload") != workload or r.get("source_sha256") != sha:
+        return None
+    return int(r["traffic_bytes_per_call"])
+
+
 def cpu_baseline(w, budget_s):
     """Time the CPU oracle as it stands (gather through the block table, then
     float64 two-pass softmax) on the first sequences of the same batch, until
@@ -190,12 +207,12 @@ def main():
         "event_ms_per_step": round(ev_ms, 5),
         "roofline": {
             "bound": "hbm",
-            "kernel": "pa_decode (partition kernel + merge)",
+            "kernel": "pa_decode call (plan_kernel + decode kernel + merge_kernel)",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": counter_traffic(w.name) if P == w.partition_tokens and L == 4 else None,
             "alg_bytes_per_launch": alg_bytes,
             "avg_launch_ms": round(dec_ms, 5),
         },

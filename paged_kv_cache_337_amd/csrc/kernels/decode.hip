@@ -65,18 +65,22 @@ constexpr float kNegInf = -__builtin_inff();
 constexpr float kRescaleLog2 = 8.0f;  // raise the reference only past 2^8
 constexpr int kPlanThreads = 1024;
 constexpr int kPlanBins = 1024;       // partial items sorted by 16-token units
+// Units whose loads are in flight ahead of the one being computed, and
+// decode workgroups per CU.  Measured on MI355X: one workgroup of four waves
+// per CU with two units (16 KiB) in flight per wave reads the paged cache
+// faster than two or three workgroups per CU with one or two units each --
+// fewer, deeper streams suit HBM3E here better than more, shallower ones.
 #ifndef PA_PREFETCH_UNITS
-#define PA_PREFETCH_UNITS 1
+#define PA_PREFETCH_UNITS 2
 #endif
-constexpr int kPrefetch = PA_PREFETCH_UNITS;  // units in flight ahead of the one computed
+#ifndef PA_WG_PER_CU
+#define PA_WG_PER_CU 1
+#endif
+constexpr int kPrefetch = PA_PREFETCH_UNITS;
+constexpr int kWorkgroupsPerCU = PA_WG_PER_CU;
 #ifndef PA_ITEMS_PER_WG
 #define PA_ITEMS_PER_WG 4
 #endif
-
-// Target of the loads issued for units outside a wave's range or with an
-// invalid block id: every wave then issues the same loads per unit, so each
-// unit waits for its own loads only (8 KiB: the largest per-unit load span).
-__device__ __align__(256) uint4 g_dummy_unit[512];
 
 // Per-thread view of one unit: NCH 16-byte chunks of K and of V.
 template <int NCH>
@@ -94,14 +98,12 @@ struct UnitStream {
   const char* layer_base;  // pool base + layer offset (bytes)
   const int32_t* trow;     // block-table row of the sequence
   int max_blocks, bs, N, H, h;
-  int u1;                  // end of the run
-  int next;                // next unit to locate
-  int lb, sub;             // its logical block and 16-token sub-tile
+  int lb, sub;             // logical block and 16-token sub-tile of the next unit
   int lb_base;             // logical block of ids lane 0
   int32_t ids;
 
   __device__ __forceinline__ void init(const DecodeParams& p, const int32_t* row, int start, int u0,
-                                       int u_end, int head, int lane) {
+                                       int head, int lane) {
     layer_base = static_cast<const char*>(p.pool) + p.layer_off * kBytes;
     trow = row;
     max_blocks = p.max_blocks;
@@ -109,8 +111,6 @@ struct UnitStream {
     N = p.N;
     H = p.H;
     h = head;
-    u1 = u_end;
-    next = u0;
     const int p0 = start + u0 * 16;
     lb = p0 / bs;
     sub = (p0 - lb * bs) >> 4;
@@ -123,31 +123,30 @@ struct UnitStream {
     ids = k < max_blocks ? trow[k] : -1;
   }
 
-  // Bases of the K and V sub-tiles of unit `next`, then advance.  Returns
-  // false, with both bases at the dummy, past the run or for an invalid id.
-  __device__ __forceinline__ bool locate(const char*& kp, const char*& vp, int lane) {
-    kp = vp = reinterpret_cast<const char*>(g_dummy_unit);
-    if (next >= u1) return false;
+  // Bases of the K and V sub-tiles of the next unit, then advance.  Returns
+  // false for an invalid block id (the bases then point at block 0 of the
+  // layer, a valid address; such a unit is not computed).
+  __device__ __forceinline__ bool locate(const char*& kp, const char*& vp) {
     const int32_t b = __builtin_amdgcn_readlane(ids, lb - lb_base);
     const int s = sub;
-    ++next;
     if (++sub * 16 == bs) {
       sub = 0;
       ++lb;
     }
-    if (b < 0 || b >= N) return false;
-    const size_t region = (static_cast<size_t>(b) * H + h) * (2 * static_cast<size_t>(bs) * D);
+    const bool ok = b >= 0 && b < N;
+    const size_t region = (static_cast<size_t>(ok ? b : 0) * H + h) * (2 * static_cast<size_t>(bs) * D);
     kp = layer_base + (region + static_cast<size_t>(s) * 16 * D) * kBytes;
     vp = layer_base + (region + static_cast<size_t>(bs) * D + static_cast<size_t>(s) * 16 * D) * kBytes;
-    return true;
+    return ok;
   }
 
   template <int NCH>
   __device__ __forceinline__ bool issue(Frag<NCH>& f, int lane) {
     const char *kb, *vb;
-    const bool ok = locate(kb, vb, lane);
-    const uint4* kp = reinterpret_cast<const uint4*>(kb) + lane;
-    const uint4* vp = reinterpret_cast<const uint4*>(vb) + lane;
+    const bool ok = locate(kb, vb);
+    const uint32_t lane_off = static_cast<uint32_t>(lane) * 16u;
+    const uint4* kp = reinterpret_cast<const uint4*>(kb + lane_off);
+    const uint4* vp = reinterpret_cast<const uint4*>(vb + lane_off);
 #pragma unroll
     for (int c = 0; c < NCH; ++c) f.k[c] = load_stream16(kp + 64 * c);
 #pragma unroll
@@ -157,19 +156,31 @@ struct UnitStream {
 };
 
 // Runs compute(frag, u, ok) over units [u0, u1) with the loads of the next PF
-// units in flight.  Loads are issued unconditionally (past the run they read
-// the dummy), so the wait before each unit covers exactly that unit's loads.
+// units in flight.  In the main loop every step issues one unit's loads, so
+// the wait before each unit covers exactly that unit's loads; the last steps
+// (fewer than PF + NB units) issue only what is left and drain.
 template <int PF, int NCH, typename Stream, typename Compute>
 __device__ __forceinline__ void stream_piece(Stream& st, int u0, int u1, int lane, Compute&& compute) {
   constexpr int NB = PF + 1;
   Frag<NCH> f[NB];
   bool ok[NB];
+  // A piece is never empty (u0 < u1): the first issue is unconditional, so
+  // every path into the loops below has waited for the block ids already.
 #pragma unroll
-  for (int s = 0; s < PF; ++s) ok[s] = st.template issue<NCH>(f[s], lane);
-  for (int u = u0; u < u1; u += NB) {
+  for (int s = 0; s < PF; ++s)
+    if (s == 0 || u0 + s < u1) ok[s] = st.template issue<NCH>(f[s], lane);
+  int u = u0;
+  for (; u + NB - 1 + PF < u1; u += NB) {
 #pragma unroll
     for (int s = 0; s < NB; ++s) {
       ok[(s + PF) % NB] = st.template issue<NCH>(f[(s + PF) % NB], lane);
+      compute(f[s], u + s, ok[s]);
+    }
+  }
+  for (; u < u1; u += NB) {
+#pragma unroll
+    for (int s = 0; s < NB; ++s) {
+      if (u + s + PF < u1) ok[(s + PF) % NB] = st.template issue<NCH>(f[(s + PF) % NB], lane);
       if (u + s < u1) compute(f[s], u + s, ok[s]);
     }
   }
@@ -189,7 +200,7 @@ __device__ __forceinline__ void stream_units(const DecodeParams& p, const int32_
   for (int a = u0; a < u1;) {
     int b = piece_end(p.bs, start, a);
     b = b < u1 ? b : u1;
-    st.init(p, trow, start, a, b, h, lane);
+    st.init(p, trow, start, a, h, lane);
     stream_piece<PF, NCH>(st, a, b, lane, compute);
     a = b;
   }
@@ -401,14 +412,8 @@ __device__ __forceinline__ void run_items(const DecodeParams& p, int& next_slot,
   while (cur < total) {
     int nxt = 0;
     if (threadIdx.x == 0) nxt = atomicAdd(&p.header[1], 1);
-#ifdef PA_HEAD_OUTER
-    const int nit = p.header[0];
-    const int hh = cur / nit;
-    const int it = cur - hh * nit;
-#else
     const int it = cur / p.H;
     const int hh = cur - it * p.H;
-#endif
     const int2 sj = p.items[it];
     item(__builtin_amdgcn_readfirstlane(sj.x), __builtin_amdgcn_readfirstlane(sj.y), hh);
     if (threadIdx.x == 0) next_slot = nxt;
@@ -459,8 +464,9 @@ __device__ __forceinline__ void mfma_item(const DecodeParams& p, int P, MergeSme
   const float sl2 = p.scale_log2;
 
   auto compute = [&](Frag<NCH>& f, int u, bool ok) {
-    const int valid = ntok - u * 16 < 16 ? ntok - u * 16 : 16;
-    if (!ok) return;
+    // A unit whose block id is invalid counts as having no valid token (its
+    // registers are still consumed, which keeps the load waits exact).
+    const int valid = !ok ? 0 : ntok - u * 16 < 16 ? ntok - u * 16 : 16;
     f32x4_t s = {0.f, 0.f, 0.f, 0.f};
     if constexpr (kBytes == 2) {
 #pragma unroll
@@ -498,7 +504,7 @@ __device__ __forceinline__ void mfma_item(const DecodeParams& p, int P, MergeSme
     uint32_t pbits[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const float e = fast_exp2(sv[r] - m_col);
+      const float e = sv[r] == kNegInf ? 0.f : fast_exp2(sv[r] - m_col);
       if constexpr (kBytes == 2) {
         pbits[r] = to_storage<T>(e);
         pr[r] = from_storage<T>(pbits[r]);
@@ -601,8 +607,9 @@ __device__ __forceinline__ void valu_item(const DecodeParams& p, int P, MergeSme
   const float sl2 = p.scale_log2;
 
   auto compute = [&](Frag<NCH>& f, int u, bool ok) {
-    const int valid = ntok - u * 16 < 16 ? ntok - u * 16 : 16;
-    if (!ok) return;
+    // A unit whose block id is invalid counts as having no valid token (its
+    // registers are still consumed, which keeps the load waits exact).
+    const int valid = !ok ? 0 : ntok - u * 16 < 16 ? ntok - u * 16 : 16;
     if (valid < 16) mask_v_tail<kBytes, NCH>(f, grp, valid);
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
@@ -637,7 +644,7 @@ __device__ __forceinline__ void valu_item(const DecodeParams& p, int P, MergeSme
 #pragma unroll
         for (int t = 0; t < NT; ++t) acc[g][t] *= alpha;
       }
-      const float e = fast_exp2(s - m_run[g]);
+      const float e = s == kNegInf ? 0.f : fast_exp2(s - m_run[g]);
       uint32_t pb;
       float pr;
       if constexpr (kBytes == 2) {
@@ -774,9 +781,8 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(DecodeParams p) {
     out[static_cast<size_t>(pair) * D + lane + 64 * k] = static_cast<B>(to_storage<T>(acc[k] * inv));
 }
 
-// Persistent grid size: workgroups resident per CU (the runtime's occupancy
-// for this kernel's registers, accumulation registers and LDS) x CUs, cached
-// per kernel and device.
+// Persistent grid: kWorkgroupsPerCU workgroups per CU (never more than the
+// kernel's occupancy allows), cached per device.
 int persistent_grid(const void* kernel) {
   static std::mutex mu;
   static struct {
@@ -789,13 +795,11 @@ int persistent_grid(const void* kernel) {
   std::lock_guard<std::mutex> lock(mu);
   for (int c = 0; c < n; ++c)
     if (cache[c].k == kernel && cache[c].dev == dev) return cache[c].grid;
-  int cus = 0, per_cu = 0;
+  int cus = 0, occ = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kThreads, 0) != hipSuccess) return 0;
-#ifdef PA_WG_PER_CU
-  per_cu = PA_WG_PER_CU;
-#endif
-  const int grid = (cus > 0 ? cus : 1) * (per_cu > 0 ? per_cu : 1);
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, kThreads, 0) != hipSuccess) return 0;
+  const int per_cu = occ > 0 && occ < kWorkgroupsPerCU ? occ : kWorkgroupsPerCU;
+  const int grid = (cus > 0 ? cus : 1) * per_cu;
   if (n < 64) cache[n++] = {kernel, dev, grid};
   return grid;
 }
