@@ -32,6 +32,9 @@ COMMON = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
     # packed fp32 instructions are kept out of generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # single-lane work-counter atomics stay as written: the atomic optimizer
+    # would read their result right away and so wait for every load in flight
+    "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
     "-Wall", "-Wno-unused-result",
 ]

@@ -274,7 +274,7 @@ int pa_decode(const pa_pool* pool, int layer, const void* q, int num_seqs, int n
     p.max_parts = max_parts;
     char* ws = static_cast<char*>(workspace);
     p.header = reinterpret_cast<int32_t*>(ws + wl.header_off);
-    p.items = reinterpret_cast<int2*>(ws + wl.items_off);
+    p.items = reinterpret_cast<int4*>(ws + wl.items_off);
     p.ws_o = max_parts > 1 ? reinterpret_cast<float*>(ws + wl.o_off) : nullptr;
     p.ws_ml = max_parts > 1 ? reinterpret_cast<float*>(ws + wl.ml_off) : nullptr;
     hipError_t e = pa::launch_decode(p, d.dtype, d.head_dim, s);

@@ -10,14 +10,19 @@
 //
 // Launch sequence of one pa_decode call:
 //   1. plan_kernel (one workgroup) cuts every context into partitions of P
-//      tokens and writes the list of (sequence, partition) work items, full
-//      partitions first and the partial ones by decreasing size, so the tail
-//      of the decode consists of the smallest items.
-//   2. the decode kernel is persistent: a grid sized to fill the GPU once;
-//      each workgroup (four wave64s) takes work items (item, kv head) from an
-//      atomic counter, fetching the next index while it works on the current
-//      one.  A sparse grid with one workgroup per possible partition spends
-//      most of its time dispatching empty workgroups; this one does not.
+//      tokens (P chosen from the total work when the caller asks for
+//      automatic partitioning) and writes the list of (sequence, partition,
+//      context) work items, full partitions first and the partial ones by
+//      decreasing size, so the tail of the decode consists of the smallest
+//      items.
+//   2. the decode kernel is persistent: one workgroup of four wave64s per CU
+//      takes work indices (item, kv head) from an atomic counter.  For many
+//      small items it runs two indices ahead and streams item after item:
+//      while it computes one item it reads the next item's record (scalar
+//      load), query rows and block ids, and it issues the next item's first
+//      K/V loads before merging the current item's four wave states.  For
+//      the few long items of an automatic partition size it takes one index
+//      at a time, which balances the end of the queue better.
 //   3. merge_kernel combines the partition states of multi-partition
 //      sequences by log-sum-exp weighting, one wave per (sequence, query head).
 //      (Merging inside the decode kernel, by the workgroup that finishes a
@@ -26,10 +31,9 @@
 //      device-coherent stores per partition; both cost more than this launch.)
 //
 // Inside an item the partition is cut into 16-token units (a 16-token
-// sub-tile of one block); wave w takes a contiguous run of units, loading the
-// next unit's K/V (16-byte loads, 1 KiB per instruction) while it computes the
-// current one.  The four waves' states are merged through LDS; single-
-// partition sequences write their output directly.
+// sub-tile of one block); wave w takes a contiguous run of units, keeping the
+// loads of the next units in flight (16-byte loads, 1 KiB per instruction)
+// while it computes the current one.
 //
 // Two inner paths read the same pool layout:
 //   * MFMA (G = query heads per kv head >= 3): S = K.Q^T with
@@ -47,9 +51,10 @@
 // same softmax (the final division uses the same reference) while the common
 // unit needs no cross-lane max and no accumulator traffic.
 //
-// Memory safety: context lengths are clamped to the table capacity and block
-// ids outside [0, N) are skipped, so bad inputs give unspecified values but
-// never an out-of-bounds access.
+// Memory safety: context lengths are clamped to the table capacity, table
+// reads stay inside the row, and block ids outside [0, N) are replaced by
+// block 0 and masked, so bad inputs give unspecified values but never an
+// out-of-bounds access.
 #include <mutex>
 
 #include "../launch.hpp"
@@ -59,12 +64,15 @@ namespace pa {
 
 namespace {
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 4;  // waves of a decode workgroup, sharing one work item
 constexpr int kThreads = 64 * kWaves;
+constexpr int kMergeWaves = 4;
+constexpr int kMergeThreads = 64 * kMergeWaves;
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kRescaleLog2 = 8.0f;  // raise the reference only past 2^8
 constexpr int kPlanThreads = 1024;
 constexpr int kPlanBins = 1024;       // partial items sorted by 16-token units
+
 // Units whose loads are in flight ahead of the one being computed, and
 // decode workgroups per CU.  Measured on MI355X: one workgroup of four waves
 // per CU with two units (16 KiB) in flight per wave reads the paged cache
@@ -82,6 +90,12 @@ constexpr int kWorkgroupsPerCU = PA_WG_PER_CU;
 #define PA_ITEMS_PER_WG 4
 #endif
 
+
+__device__ __forceinline__ int rfl(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// Wave-uniform "any lane" test.
+__device__ __forceinline__ bool wave_any(bool x) { return __builtin_amdgcn_ballot_w64(x) != 0; }
+
 // Per-thread view of one unit: NCH 16-byte chunks of K and of V.
 template <int NCH>
 struct Frag {
@@ -89,8 +103,47 @@ struct Frag {
   uint4 v[NCH];
 };
 
-// The 16-token units of one wave's run [u0, u1) of a partition, located in
-// issue order.  The run's block ids (at most 64 logical blocks) are held one
+// ---------------------------------------------------------------------------
+// Work items.
+// ---------------------------------------------------------------------------
+
+// One work item as one wave of the workgroup sees it (all values uniform).
+struct Item {
+  int i, j, h;     // sequence, partition, kv head
+  int ctx;         // context length (clamped)
+  int start;       // first token of the partition
+  int ntok;        // tokens in the partition
+  int u0, u1;      // this wave's run of 16-token units
+  int np;          // partitions of the sequence
+  const int32_t* trow;
+};
+
+// rec = (sequence, partition, clamped context, partitions of the sequence) as
+// written by plan_kernel.
+__device__ __forceinline__ Item make_item(const DecodeParams& p, int4 rec, int h, int P, int wave) {
+  Item it;
+  it.i = rfl(rec.x);
+  it.j = rfl(rec.y);
+  it.ctx = rfl(rec.z);
+  it.np = rfl(rec.w);
+  it.h = h;
+  it.start = it.j * P;
+  const int left = it.ctx - it.start;
+  it.ntok = left < P ? (left > 0 ? left : 0) : P;
+  const int nunits = (it.ntok + 15) >> 4;
+  const int per = (nunits + kWaves - 1) / kWaves;
+  it.u0 = wave * per;
+  it.u1 = it.u0 + per < nunits ? it.u0 + per : nunits;
+  it.trow = p.tables + static_cast<size_t>(it.i) * p.max_blocks;
+  return it;
+}
+
+// ---------------------------------------------------------------------------
+// Unit streaming.
+// ---------------------------------------------------------------------------
+
+// The 16-token units of one wave's run of a partition, located in issue order.
+// The block ids of a piece of the run (at most 64 logical blocks) are held one
 // per lane and read out with v_readlane, so locating a unit is scalar
 // arithmetic with no memory access.
 template <int D, int kBytes>
@@ -102,8 +155,8 @@ struct UnitStream {
   int lb_base;             // logical block of ids lane 0
   int32_t ids;
 
-  __device__ __forceinline__ void init(const DecodeParams& p, const int32_t* row, int start, int u0,
-                                       int head, int lane) {
+  // Position at unit u of the partition starting at token `start`.
+  __device__ __forceinline__ void begin(const DecodeParams& p, const int32_t* row, int start, int u, int head) {
     layer_base = static_cast<const char*>(p.pool) + p.layer_off * kBytes;
     trow = row;
     max_blocks = p.max_blocks;
@@ -111,21 +164,21 @@ struct UnitStream {
     N = p.N;
     H = p.H;
     h = head;
-    const int p0 = start + u0 * 16;
+    const int p0 = start + u * 16;
     lb = p0 / bs;
     sub = (p0 - lb * bs) >> 4;
-    load_ids(lane);
+    lb_base = lb;
   }
 
-  __device__ __forceinline__ void load_ids(int lane) {
-    lb_base = lb;
-    const int k = lb + lane;
-    ids = k < max_blocks ? trow[k] : -1;
+  // Block id of logical block lb_base + lane (-1 past the row).
+  __device__ __forceinline__ int32_t fetch_ids(int lane) const {
+    const int k = lb_base + lane;
+    return k < max_blocks ? trow[k] : -1;
   }
 
   // Bases of the K and V sub-tiles of the next unit, then advance.  Returns
   // false for an invalid block id (the bases then point at block 0 of the
-  // layer, a valid address; such a unit is not computed).
+  // layer, a valid address; such a unit is masked).
   __device__ __forceinline__ bool locate(const char*& kp, const char*& vp) {
     const int32_t b = __builtin_amdgcn_readlane(ids, lb - lb_base);
     const int s = sub;
@@ -155,20 +208,24 @@ struct UnitStream {
   }
 };
 
-// Runs compute(frag, u, ok) over units [u0, u1) with the loads of the next PF
-// units in flight.  In the main loop every step issues one unit's loads, so
-// the wait before each unit covers exactly that unit's loads; the last steps
-// (fewer than PF + NB units) issue only what is left and drain.
-template <int PF, int NCH, typename Stream, typename Compute>
-__device__ __forceinline__ void stream_piece(Stream& st, int u0, int u1, int lane, Compute&& compute) {
-  constexpr int NB = PF + 1;
-  Frag<NCH> f[NB];
-  bool ok[NB];
-  // A piece is never empty (u0 < u1): the first issue is unconditional, so
-  // every path into the loops below has waited for the block ids already.
+// Issues the first PF units of a piece into f[0 .. PF-1].  Always PF units:
+// units past the run only cost a wasted load of a valid address, and a fixed
+// count keeps the compiler's waits exact in every loop that follows.
+template <int PF, int NCH, typename Stream>
+__device__ __forceinline__ void prologue(Stream& st, Frag<NCH> (&f)[PF + 1], bool (&ok)[PF + 1], int lane) {
 #pragma unroll
-  for (int s = 0; s < PF; ++s)
-    if (s == 0 || u0 + s < u1) ok[s] = st.template issue<NCH>(f[s], lane);
+  for (int s = 0; s < PF; ++s) ok[s] = st.template issue<NCH>(f[s], lane);
+}
+
+// Runs compute(frag, u, ok) over the units [u0, u1) of one piece whose first
+// PF units are already in flight.  In the main loop every step issues one
+// unit's loads, so the wait before each unit covers exactly that unit's
+// loads; the last steps (fewer than PF + NB units) issue what is left and
+// drain.
+template <int PF, int NCH, typename Stream, typename Compute>
+__device__ __forceinline__ void stream_piece(Stream& st, Frag<NCH> (&f)[PF + 1], bool (&ok)[PF + 1],
+                                             int u0, int u1, int lane, Compute&& compute) {
+  constexpr int NB = PF + 1;
   int u = u0;
   for (; u + NB - 1 + PF < u1; u += NB) {
 #pragma unroll
@@ -193,16 +250,24 @@ __device__ __forceinline__ int piece_end(int bs, int start, int u) {
   return ((p0 / bs + 64) * bs - start) >> 4;
 }
 
+// The whole run of one item, its first piece's prologue already issued.
+// Runs longer than 64 blocks (partitions above 64 * block_size tokens) load
+// the ids of each further piece where it starts.
 template <int PF, int NCH, int D, int kBytes, typename Compute>
-__device__ __forceinline__ void stream_units(const DecodeParams& p, const int32_t* trow, int start,
-                                             int u0, int u1, int h, int lane, Compute&& compute) {
-  UnitStream<D, kBytes> st;
-  for (int a = u0; a < u1;) {
-    int b = piece_end(p.bs, start, a);
-    b = b < u1 ? b : u1;
-    st.init(p, trow, start, a, h, lane);
-    stream_piece<PF, NCH>(st, a, b, lane, compute);
-    a = b;
+__device__ __forceinline__ void stream_item(const DecodeParams& p, UnitStream<D, kBytes>& st,
+                                            Frag<NCH> (&f)[PF + 1], bool (&ok)[PF + 1], const Item& it,
+                                            int lane, Compute&& compute) {
+  int a = it.u0;
+  int b = piece_end(p.bs, it.start, a);
+  b = b < it.u1 ? b : it.u1;
+  stream_piece<PF, NCH>(st, f, ok, a, b, lane, compute);
+  for (a = b; a < it.u1; a = b) {
+    b = piece_end(p.bs, it.start, a);
+    b = b < it.u1 ? b : it.u1;
+    st.begin(p, it.trow, it.start, a, it.h);
+    st.ids = st.fetch_ids(lane);
+    prologue<PF, NCH>(st, f, ok, lane);
+    stream_piece<PF, NCH>(st, f, ok, a, b, lane, compute);
   }
 }
 
@@ -233,14 +298,20 @@ __device__ __forceinline__ void mask_v_tail(Frag<NCH>& f, int grp, int valid) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Merging the four waves' states of an item.
+// ---------------------------------------------------------------------------
+
 // LDS merge of the four waves' states, then either the final output or the
 // partition's workspace entry.  Rows are the query heads of this kv head.
+// `slot` carries work indices from thread 0 to the workgroup.
 template <int D, int GMAX>
 struct MergeSmem {
+  static constexpr int kRows = GMAX;
   float m[kWaves][GMAX];
   float l[kWaves][GMAX];
   float o[kWaves][GMAX][D];
-  int next;
+  int slot[4];
 };
 
 template <typename T>
@@ -250,8 +321,7 @@ __device__ __forceinline__ void store_out(const DecodeParams& p, size_t row, int
 }
 
 template <typename T, int D, int GMAX>
-__device__ __forceinline__ void finish_partition(const DecodeParams& p, MergeSmem<D, GMAX>& sm,
-                                                 int i, int h, int j, int np) {
+__device__ __forceinline__ void finish_partition(const DecodeParams& p, MergeSmem<D, GMAX>& sm, const Item& it) {
   __syncthreads();
   const int G = p.G;
   for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
@@ -267,12 +337,12 @@ __device__ __forceinline__ void finish_partition(const DecodeParams& p, MergeSme
       L += f * sm.l[w][g];
       O += f * sm.o[w][g][d];
     }
-    const size_t row = static_cast<size_t>(i) * p.Hq + h * G + g;
+    const size_t row = static_cast<size_t>(it.i) * p.Hq + it.h * G + g;
     const float o = (L > 0.f) ? O / L : 0.f;
-    if (np == 1) {
+    if (it.np == 1) {
       store_out<T>(p, row, d, D, o);
     } else {
-      const size_t e = row * p.max_parts + j;
+      const size_t e = row * p.max_parts + it.j;
       p.ws_o[e * D + d] = o;
       if (d == 0) {
         p.ws_ml[2 * e] = M;
@@ -289,22 +359,10 @@ __device__ __forceinline__ int clamp_ctx(const DecodeParams& p, int i) {
   return c > p.ctx_cap ? p.ctx_cap : c;
 }
 
-// The same for a sequence index that is uniform across the wave.
-__device__ __forceinline__ int clamp_ctx_uniform(const DecodeParams& p, int i) {
-  return __builtin_amdgcn_readfirstlane(clamp_ctx(p, i));
-}
-
-// Partitions of a context of `ctx` tokens (one for an empty context).
-__device__ __forceinline__ int num_parts(int P, int ctx) {
-  return ctx > P ? (ctx + P - 1) / P : 1;
-}
-
-// Wave-uniform "any lane" test.
-__device__ __forceinline__ bool wave_any(bool x) { return __builtin_amdgcn_ballot_w64(x) != 0; }
-
 // ---------------------------------------------------------------------------
 // Work items: plan kernel.
 // ---------------------------------------------------------------------------
+
 // Partition size of an automatic decode: as large as keeps about
 // kItemsPerWorkgroup work items per workgroup of the persistent grid (fewer,
 // longer items cost fewer item starts and fewer partition merges), never
@@ -391,93 +449,68 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeParams p) {
   for (int k = 0, i = threadIdx.x; i < p.S; ++k, i += kPlanThreads) {
     const int c = ctx_of(k, i);
     const int nfull = c / P, rem = c - nfull * P;
+    const int np = nfull + (rem > 0 || c == 0 ? 1 : 0);
     if (nfull > 0) {
       const int base = atomicAdd(&off[bin_of(P)], nfull);
-      for (int j = 0; j < nfull; ++j) p.items[base + j] = make_int2(i, j);
+      for (int j = 0; j < nfull; ++j) p.items[base + j] = make_int4(i, j, c, np);
     }
-    if (rem > 0 || c == 0) p.items[atomicAdd(&off[bin_of(rem)], 1)] = make_int2(i, nfull);
-  }
-}
-
-// Persistent driver: the workgroup takes work indices `cur` = item * H + head
-// from the counter until none is left, fetching the next index while it works
-// on the current one.  Workgroups that start after the work has run out exit
-// at once, so the grid may exceed what is resident.
-template <typename Item>
-__device__ __forceinline__ void run_items(const DecodeParams& p, int& next_slot, Item&& item) {
-  const int total = p.header[0] * p.H;
-  if (threadIdx.x == 0) next_slot = atomicAdd(&p.header[1], 1);
-  __syncthreads();
-  int cur = __builtin_amdgcn_readfirstlane(next_slot);
-  while (cur < total) {
-    int nxt = 0;
-    if (threadIdx.x == 0) nxt = atomicAdd(&p.header[1], 1);
-    const int it = cur / p.H;
-    const int hh = cur - it * p.H;
-    const int2 sj = p.items[it];
-    item(__builtin_amdgcn_readfirstlane(sj.x), __builtin_amdgcn_readfirstlane(sj.y), hh);
-    if (threadIdx.x == 0) next_slot = nxt;
-    __syncthreads();
-    cur = __builtin_amdgcn_readfirstlane(next_slot);
+    if (rem > 0 || c == 0) p.items[atomicAdd(&off[bin_of(rem)], 1)] = make_int4(i, nfull, c, np);
   }
 }
 
 // ---------------------------------------------------------------------------
-// MFMA path: 3 <= G <= 16 query heads per kv head.
+// MFMA path: 3 <= G <= 16 query heads per kv head (GM = G rounded up to 4, 8
+// or 16 sizes the LDS merge).
 // ---------------------------------------------------------------------------
 template <typename T, int D, int GM>
-__device__ __forceinline__ void mfma_item(const DecodeParams& p, int P, MergeSmem<D, GM>& sm, int i, int j,
-                                          int h) {
-  constexpr int kBytes = T::kBytes;
-  constexpr int E = 16 / kBytes;
-  constexpr int NCH = D / (4 * E);  // 16-byte chunks per lane per sub-tile
-  constexpr int NT = D / 16;        // 16-wide head_dim tiles of the output
+struct MfmaPath {
+  static constexpr int kBytes = T::kBytes;
+  static constexpr int E = 16 / kBytes;
+  static constexpr int NCH = D / (4 * E);  // 16-byte chunks per lane per sub-tile
+  static constexpr int NT = D / 16;        // 16-wide head_dim tiles of the output
+  using Smem = MergeSmem<D, GM>;
 
-  const int ctx = clamp_ctx_uniform(p, i);
-  const int start = j * P;
-  const int ntok = ctx - start < P ? ctx - start : P;
-  const int nunits = ntok > 0 ? (ntok + 15) >> 4 : 0;
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int col = lane & 15, grp = lane >> 4;
-  const int G = p.G;
-  const int32_t* trow = p.tables + static_cast<size_t>(i) * p.max_blocks;
-  const int per = (nunits + kWaves - 1) / kWaves;
-  const int u0 = wave * per;
-  const int u1 = u0 + per < nunits ? u0 + per : nunits;
+  // Query rows as the B operand of S = K.Q^T: lane holds head `col`, the
+  // head_dim entries matching its K chunk entries.
+  struct Q {
+    uint4 b[NCH];
+  };
+  struct State {
+    f32x4_t acc[NT];
+    float m_col, l_part;
+  };
 
-  // Query rows as the B operand of S = K.Q^T: lane holds head `col`,
-  // the head_dim entries matching its K chunk entries.
-  const char* qbase = static_cast<const char*>(p.q) +
-                      (static_cast<size_t>(i) * p.Hq + static_cast<size_t>(h) * G + col) * D * kBytes;
-  uint4 qb[NCH];
+  __device__ static void load_q(Q& q, const DecodeParams& p, const Item& it, int lane) {
+    const int col = lane & 15, grp = lane >> 4;
+    const int G = p.G;
+    const char* qbase = static_cast<const char*>(p.q) +
+                        (static_cast<size_t>(it.i) * p.Hq + static_cast<size_t>(it.h) * G + col) * D * kBytes;
 #pragma unroll
-  for (int c = 0; c < NCH; ++c) {
-    qb[c] = (col < G) ? *reinterpret_cast<const uint4*>(qbase + ((c * 4 + grp) * E) * kBytes)
-                      : make_uint4(0, 0, 0, 0);
+    for (int c = 0; c < NCH; ++c)
+      q.b[c] = (col < G) ? *reinterpret_cast<const uint4*>(qbase + ((c * 4 + grp) * E) * kBytes)
+                         : make_uint4(0, 0, 0, 0);
   }
 
-  f32x4_t acc[NT];
+  __device__ static void reset(State& s) {
 #pragma unroll
-  for (int t = 0; t < NT; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float m_col = kNegInf, l_part = 0.f;
-  const float sl2 = p.scale_log2;
+    for (int t = 0; t < NT; ++t) s.acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    s.m_col = kNegInf;
+    s.l_part = 0.f;
+  }
 
-  auto compute = [&](Frag<NCH>& f, int u, bool ok) {
-    // A unit whose block id is invalid counts as having no valid token (its
-    // registers are still consumed, which keeps the load waits exact).
-    const int valid = !ok ? 0 : ntok - u * 16 < 16 ? ntok - u * 16 : 16;
+  __device__ static void compute(State& st, const Q& q, Frag<NCH>& f, int valid, int lane, float sl2) {
+    const int grp = lane >> 4;
     f32x4_t s = {0.f, 0.f, 0.f, 0.f};
     if constexpr (kBytes == 2) {
 #pragma unroll
-      for (int c = 0; c < NCH; ++c) s = mfma_k32<T>(f.k[c], qb[c], s);
+      for (int c = 0; c < NCH; ++c) s = mfma_k32<T>(f.k[c], q.b[c], s);
     } else {
 #pragma unroll
       for (int c = 0; c < NCH; ++c) {
-        s = mfma_f32_k4(__uint_as_float(f.k[c].x), __uint_as_float(qb[c].x), s);
-        s = mfma_f32_k4(__uint_as_float(f.k[c].y), __uint_as_float(qb[c].y), s);
-        s = mfma_f32_k4(__uint_as_float(f.k[c].z), __uint_as_float(qb[c].z), s);
-        s = mfma_f32_k4(__uint_as_float(f.k[c].w), __uint_as_float(qb[c].w), s);
+        s = mfma_f32_k4(__uint_as_float(f.k[c].x), __uint_as_float(q.b[c].x), s);
+        s = mfma_f32_k4(__uint_as_float(f.k[c].y), __uint_as_float(q.b[c].y), s);
+        s = mfma_f32_k4(__uint_as_float(f.k[c].z), __uint_as_float(q.b[c].z), s);
+        s = mfma_f32_k4(__uint_as_float(f.k[c].w), __uint_as_float(q.b[c].w), s);
       }
     }
     // s[r] = score of token 4*grp + r for query head col (log2 units).
@@ -485,26 +518,26 @@ __device__ __forceinline__ void mfma_item(const DecodeParams& p, int P, MergeSme
 #pragma unroll
     for (int r = 0; r < 4; ++r) sv[r] = (4 * grp + r < valid) ? s[r] * sl2 : kNegInf;
     const float mloc = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-    if (wave_any(mloc > m_col + kRescaleLog2)) {
+    if (wave_any(mloc > st.m_col + kRescaleLog2)) {
       float mx = fmaxf(mloc, __shfl_xor(mloc, 16));
       mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_col, mx);
-      const float alpha = fast_exp2(m_col - m_new);
-      m_col = m_new;
-      l_part *= alpha;
+      const float m_new = fmaxf(st.m_col, mx);
+      const float alpha = fast_exp2(st.m_col - m_new);
+      st.m_col = m_new;
+      st.l_part *= alpha;
       // Output rows 4*grp + r belong to query heads whose alpha sits in lane 4*grp + r.
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float a = __shfl(alpha, 4 * grp + r);
 #pragma unroll
-        for (int t = 0; t < NT; ++t) acc[t][r] *= a;
+        for (int t = 0; t < NT; ++t) st.acc[t][r] *= a;
       }
     }
     float pr[4];
     uint32_t pbits[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const float e = sv[r] == kNegInf ? 0.f : fast_exp2(sv[r] - m_col);
+      const float e = sv[r] == kNegInf ? 0.f : fast_exp2(sv[r] - st.m_col);
       if constexpr (kBytes == 2) {
         pbits[r] = to_storage<T>(e);
         pr[r] = from_storage<T>(pbits[r]);
@@ -512,7 +545,7 @@ __device__ __forceinline__ void mfma_item(const DecodeParams& p, int P, MergeSme
         pr[r] = e;
       }
     }
-    l_part += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+    st.l_part += (pr[0] + pr[1]) + (pr[2] + pr[3]);
     if (valid < 16) mask_v_tail<kBytes, NCH>(f, grp, valid);
     if constexpr (kBytes == 2) {
       const uint2 pa = make_uint2(pbits[0] | (pbits[1] << 16), pbits[2] | (pbits[3] << 16));
@@ -520,96 +553,84 @@ __device__ __forceinline__ void mfma_item(const DecodeParams& p, int P, MergeSme
       for (int t = 0; t < NT; ++t) {
         const uint4 vc = f.v[t >> 1];
         const uint2 vb = (t & 1) ? make_uint2(vc.z, vc.w) : make_uint2(vc.x, vc.y);
-        acc[t] = mfma_k16<T>(pa, vb, acc[t]);
+        st.acc[t] = mfma_k16<T>(pa, vb, st.acc[t]);
       }
     } else {
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
-        acc[t] = mfma_f32_k4(pr[0], __uint_as_float(f.v[t].x), acc[t]);
-        acc[t] = mfma_f32_k4(pr[1], __uint_as_float(f.v[t].y), acc[t]);
-        acc[t] = mfma_f32_k4(pr[2], __uint_as_float(f.v[t].z), acc[t]);
-        acc[t] = mfma_f32_k4(pr[3], __uint_as_float(f.v[t].w), acc[t]);
+        st.acc[t] = mfma_f32_k4(pr[0], __uint_as_float(f.v[t].x), st.acc[t]);
+        st.acc[t] = mfma_f32_k4(pr[1], __uint_as_float(f.v[t].y), st.acc[t]);
+        st.acc[t] = mfma_f32_k4(pr[2], __uint_as_float(f.v[t].z), st.acc[t]);
+        st.acc[t] = mfma_f32_k4(pr[3], __uint_as_float(f.v[t].w), st.acc[t]);
       }
     }
-  };
-
-  stream_units<kPrefetch, NCH, D, kBytes>(p, trow, start, u0, u1, h, lane, compute);
-
-  // Column sums over the four lane groups.
-  float l_col = l_part + __shfl_xor(l_part, 16);
-  l_col += __shfl_xor(l_col, 32);
-  if (lane < GM) {  // lane = query-head column
-    sm.m[wave][lane] = m_col;
-    sm.l[wave][lane] = l_col;
   }
+
+  // This wave's (max, sum, weighted V) per query head into LDS.
+  __device__ static void to_lds(const State& st, Smem& sm, int wave, int lane, int G) {
+    const int col = lane & 15, grp = lane >> 4;
+    // Column sums over the four lane groups.
+    float l_col = st.l_part + __shfl_xor(st.l_part, 16);
+    l_col += __shfl_xor(l_col, 32);
+    if (lane < GM) {  // lane = query-head column
+      sm.m[wave][lane] = st.m_col;
+      sm.l[wave][lane] = l_col;
+    }
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int g = 4 * grp + r;
-    if (g < GM && g < G) {
+    for (int r = 0; r < 4; ++r) {
+      const int g = 4 * grp + r;
+      if (g < GM && g < G) {
 #pragma unroll
-      for (int t = 0; t < NT; ++t) sm.o[wave][g][t * 16 + col] = acc[t][r];
+        for (int t = 0; t < NT; ++t) sm.o[wave][g][t * 16 + col] = st.acc[t][r];
+      }
     }
   }
-  finish_partition<T, D, GM>(p, sm, i, h, j, num_parts(P, ctx));
-}
-
-// GM: query heads per kv head rounded up to 4, 8 or 16 (sizes the LDS merge).
-template <typename T, int D, int GM>
-__global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
-  __shared__ MergeSmem<D, GM> sm;
-  const int P = __builtin_amdgcn_readfirstlane(p.header[2]);
-  run_items(p, sm.next, [&](int i, int j, int h) { mfma_item<T, D, GM>(p, P, sm, i, j, h); });
-}
+};
 
 // ---------------------------------------------------------------------------
 // VALU path: NG (1 or 2) query heads per kv head.
 // ---------------------------------------------------------------------------
 template <typename T, int D, int NG>
-__device__ __forceinline__ void valu_item(const DecodeParams& p, int P, MergeSmem<D, NG>& sm, int i, int j,
-                                          int h) {
-  constexpr int kBytes = T::kBytes;
-  constexpr int E = 16 / kBytes;
-  constexpr int NCH = D / (4 * E);
-  constexpr int R = E / 4;          // 16-wide d tiles per V chunk
-  constexpr int NT = D / 16;        // d values per lane in P.V (d = t*16 + col)
-
-  const int ctx = clamp_ctx_uniform(p, i);
-  const int start = j * P;
-  const int ntok = ctx - start < P ? ctx - start : P;
-  const int nunits = ntok > 0 ? (ntok + 15) >> 4 : 0;
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int col = lane & 15, grp = lane >> 4;
-  const int32_t* trow = p.tables + static_cast<size_t>(i) * p.max_blocks;
-  const int per = (nunits + kWaves - 1) / kWaves;
-  const int u0 = wave * per;
-  const int u1 = u0 + per < nunits ? u0 + per : nunits;
+struct ValuPath {
+  static constexpr int kBytes = T::kBytes;
+  static constexpr int E = 16 / kBytes;
+  static constexpr int NCH = D / (4 * E);
+  static constexpr int R = E / 4;    // 16-wide d tiles per V chunk
+  static constexpr int NT = D / 16;  // d values per lane in P.V (d = t*16 + col)
+  using Smem = MergeSmem<D, NG>;
 
   // q entries matching this lane's K chunk entries: d = (c*4 + grp)*E + e.
-  uint4 qv[NG][NCH];
+  struct Q {
+    uint4 v[NG][NCH];
+  };
+  struct State {
+    float acc[NG][NT];
+    float m_run[NG], l_run[NG];
+  };
+
+  __device__ static void load_q(Q& q, const DecodeParams& p, const Item& it, int lane) {
+    const int grp = lane >> 4;
 #pragma unroll
-  for (int g = 0; g < NG; ++g) {
-    const char* qrow = static_cast<const char*>(p.q) +
-                       (static_cast<size_t>(i) * p.Hq + static_cast<size_t>(h) * NG + g) * D * kBytes;
+    for (int g = 0; g < NG; ++g) {
+      const char* qrow = static_cast<const char*>(p.q) +
+                         (static_cast<size_t>(it.i) * p.Hq + static_cast<size_t>(it.h) * NG + g) * D * kBytes;
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) qv[g][c] = *reinterpret_cast<const uint4*>(qrow + ((c * 4 + grp) * E) * kBytes);
+      for (int c = 0; c < NCH; ++c) q.v[g][c] = *reinterpret_cast<const uint4*>(qrow + ((c * 4 + grp) * E) * kBytes);
+    }
   }
 
-  float acc[NG][NT];
-  float m_run[NG], l_run[NG];
+  __device__ static void reset(State& s) {
 #pragma unroll
-  for (int g = 0; g < NG; ++g) {
-    m_run[g] = kNegInf;
-    l_run[g] = 0.f;
+    for (int g = 0; g < NG; ++g) {
+      s.m_run[g] = kNegInf;
+      s.l_run[g] = 0.f;
 #pragma unroll
-    for (int t = 0; t < NT; ++t) acc[g][t] = 0.f;
+      for (int t = 0; t < NT; ++t) s.acc[g][t] = 0.f;
+    }
   }
-  const float sl2 = p.scale_log2;
 
-  auto compute = [&](Frag<NCH>& f, int u, bool ok) {
-    // A unit whose block id is invalid counts as having no valid token (its
-    // registers are still consumed, which keeps the load waits exact).
-    const int valid = !ok ? 0 : ntok - u * 16 < 16 ? ntok - u * 16 : 16;
+  __device__ static void compute(State& st, const Q& q, Frag<NCH>& f, int valid, int lane, float sl2) {
+    const int col = lane & 15, grp = lane >> 4;
     if (valid < 16) mask_v_tail<kBytes, NCH>(f, grp, valid);
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
@@ -618,33 +639,33 @@ __device__ __forceinline__ void valu_item(const DecodeParams& p, int P, MergeSme
 #pragma unroll
       for (int c = 0; c < NCH; ++c) {
         if constexpr (kBytes == 2) {
-          dot = dot2<T>(f.k[c].x, qv[g][c].x, dot);
-          dot = dot2<T>(f.k[c].y, qv[g][c].y, dot);
-          dot = dot2<T>(f.k[c].z, qv[g][c].z, dot);
-          dot = dot2<T>(f.k[c].w, qv[g][c].w, dot);
+          dot = dot2<T>(f.k[c].x, q.v[g][c].x, dot);
+          dot = dot2<T>(f.k[c].y, q.v[g][c].y, dot);
+          dot = dot2<T>(f.k[c].z, q.v[g][c].z, dot);
+          dot = dot2<T>(f.k[c].w, q.v[g][c].w, dot);
         } else {
-          dot = fmaf(__uint_as_float(f.k[c].x), __uint_as_float(qv[g][c].x), dot);
-          dot = fmaf(__uint_as_float(f.k[c].y), __uint_as_float(qv[g][c].y), dot);
-          dot = fmaf(__uint_as_float(f.k[c].z), __uint_as_float(qv[g][c].z), dot);
-          dot = fmaf(__uint_as_float(f.k[c].w), __uint_as_float(qv[g][c].w), dot);
+          dot = fmaf(__uint_as_float(f.k[c].x), __uint_as_float(q.v[g][c].x), dot);
+          dot = fmaf(__uint_as_float(f.k[c].y), __uint_as_float(q.v[g][c].y), dot);
+          dot = fmaf(__uint_as_float(f.k[c].z), __uint_as_float(q.v[g][c].z), dot);
+          dot = fmaf(__uint_as_float(f.k[c].w), __uint_as_float(q.v[g][c].w), dot);
         }
       }
       dot += __shfl_xor(dot, 16);
       dot += __shfl_xor(dot, 32);
       const float s = (col < valid) ? dot * sl2 : kNegInf;
-      if (wave_any(s > m_run[g] + kRescaleLog2)) {
+      if (wave_any(s > st.m_run[g] + kRescaleLog2)) {
         float mx = fmaxf(s, __shfl_xor(s, 1));
         mx = fmaxf(mx, __shfl_xor(mx, 2));
         mx = fmaxf(mx, __shfl_xor(mx, 4));
         mx = fmaxf(mx, __shfl_xor(mx, 8));
-        const float m_new = fmaxf(m_run[g], mx);
-        const float alpha = fast_exp2(m_run[g] - m_new);
-        m_run[g] = m_new;
-        l_run[g] *= alpha;
+        const float m_new = fmaxf(st.m_run[g], mx);
+        const float alpha = fast_exp2(st.m_run[g] - m_new);
+        st.m_run[g] = m_new;
+        st.l_run[g] *= alpha;
 #pragma unroll
-        for (int t = 0; t < NT; ++t) acc[g][t] *= alpha;
+        for (int t = 0; t < NT; ++t) st.acc[g][t] *= alpha;
       }
-      const float e = s == kNegInf ? 0.f : fast_exp2(s - m_run[g]);
+      const float e = s == kNegInf ? 0.f : fast_exp2(s - st.m_run[g]);
       uint32_t pb;
       float pr;
       if constexpr (kBytes == 2) {
@@ -654,7 +675,7 @@ __device__ __forceinline__ void valu_item(const DecodeParams& p, int P, MergeSme
         pb = __float_as_uint(e);
         pr = e;
       }
-      l_run[g] += pr;  // token `col`'s weight; summed over lanes at the end
+      st.l_run[g] += pr;  // token `col`'s weight; summed over lanes at the end
       // Weights of tokens 4*grp .. 4*grp+3, the tokens this lane's V entries hold.
       const uint32_t w0 = __shfl(pb, 4 * grp + 0), w1 = __shfl(pb, 4 * grp + 1);
       const uint32_t w2 = __shfl(pb, 4 * grp + 2), w3 = __shfl(pb, 4 * grp + 3);
@@ -663,70 +684,176 @@ __device__ __forceinline__ void valu_item(const DecodeParams& p, int P, MergeSme
 #pragma unroll
         for (int c = 0; c < NCH; ++c) {
           // chunk c holds d tiles c*R + 0 (dwords x, y) and c*R + 1 (z, w)
-          acc[g][c * R + 0] = dot2<T>(f.v[c].x, p01, acc[g][c * R + 0]);
-          acc[g][c * R + 0] = dot2<T>(f.v[c].y, p23, acc[g][c * R + 0]);
-          acc[g][c * R + 1] = dot2<T>(f.v[c].z, p01, acc[g][c * R + 1]);
-          acc[g][c * R + 1] = dot2<T>(f.v[c].w, p23, acc[g][c * R + 1]);
+          st.acc[g][c * R + 0] = dot2<T>(f.v[c].x, p01, st.acc[g][c * R + 0]);
+          st.acc[g][c * R + 0] = dot2<T>(f.v[c].y, p23, st.acc[g][c * R + 0]);
+          st.acc[g][c * R + 1] = dot2<T>(f.v[c].z, p01, st.acc[g][c * R + 1]);
+          st.acc[g][c * R + 1] = dot2<T>(f.v[c].w, p23, st.acc[g][c * R + 1]);
         }
       } else {
 #pragma unroll
         for (int c = 0; c < NCH; ++c) {
-          float a = acc[g][c];
+          float a = st.acc[g][c];
           a = fmaf(__uint_as_float(w0), __uint_as_float(f.v[c].x), a);
           a = fmaf(__uint_as_float(w1), __uint_as_float(f.v[c].y), a);
           a = fmaf(__uint_as_float(w2), __uint_as_float(f.v[c].z), a);
           a = fmaf(__uint_as_float(w3), __uint_as_float(f.v[c].w), a);
-          acc[g][c] = a;
+          st.acc[g][c] = a;
         }
       }
     }
-  };
+  }
 
-  stream_units<kPrefetch, NCH, D, kBytes>(p, trow, start, u0, u1, h, lane, compute);
-
+  __device__ static void to_lds(State& st, Smem& sm, int wave, int lane, int) {
+    const int col = lane & 15;
 #pragma unroll
-  for (int g = 0; g < NG; ++g) {
-    float l = l_run[g];
-    l += __shfl_xor(l, 1);
-    l += __shfl_xor(l, 2);
-    l += __shfl_xor(l, 4);
-    l += __shfl_xor(l, 8);
+    for (int g = 0; g < NG; ++g) {
+      float l = st.l_run[g];
+      l += __shfl_xor(l, 1);
+      l += __shfl_xor(l, 2);
+      l += __shfl_xor(l, 4);
+      l += __shfl_xor(l, 8);
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      float a = acc[g][t];
-      a += __shfl_xor(a, 16);
-      a += __shfl_xor(a, 32);
-      acc[g][t] = a;
-    }
-    if (lane < 16) {
-      if (lane == 0) {
-        sm.m[wave][g] = m_run[g];
-        sm.l[wave][g] = l;
+      for (int t = 0; t < NT; ++t) {
+        float a = st.acc[g][t];
+        a += __shfl_xor(a, 16);
+        a += __shfl_xor(a, 32);
+        st.acc[g][t] = a;
       }
+      if (lane < 16) {
+        if (lane == 0) {
+          sm.m[wave][g] = st.m_run[g];
+          sm.l[wave][g] = l;
+        }
 #pragma unroll
-      for (int t = 0; t < NT; ++t) sm.o[wave][g][t * 16 + col] = acc[g][t];
+        for (int t = 0; t < NT; ++t) sm.o[wave][g][t * 16 + col] = st.acc[g][t];
+      }
     }
   }
-  finish_partition<T, D, NG>(p, sm, i, h, j, num_parts(P, ctx));
-}
+};
 
-template <typename T, int D, int NG>
-__global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeParams p) {
-  __shared__ MergeSmem<D, NG> sm;
-  const int P = __builtin_amdgcn_readfirstlane(p.header[2]);
-  run_items(p, sm.next, [&](int i, int j, int h) { valu_item<T, D, NG>(p, P, sm, i, j, h); });
+// ---------------------------------------------------------------------------
+// Persistent decode kernel, in two schedules.
+//
+// Deep (kDeep = true), for many small items (an explicit small partition
+// size): work indices run two ahead of the item being computed.  Timeline of
+// one workgroup for item k:
+//   - thread 0 fetches the index of item k+2 from the counter;
+//   - every wave reads item k+1's record (a scalar load through the
+//     __restrict__ items argument, which does not disturb the vector-load
+//     waits), then loads item k+1's query rows and this wave's block ids;
+//   - the waves stream and compute item k's units;
+//   - thread 0 posts item k+2's index; the waves issue item k+1's first units;
+//   - the four wave states of item k are merged through LDS and written while
+//     those loads are in flight.
+// Shallow (kDeep = false), for the few long items of an automatic partition
+// size: one index ahead, so the last items of the queue stay free for
+// whichever workgroup finishes first (measured: holding two indices per
+// workgroup costs more in the tail than it saves between items there).
+// ---------------------------------------------------------------------------
+template <typename Path, typename T, int D, bool kDeep>
+__global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p, const int4* __restrict__ items) {
+  constexpr int kBytes = T::kBytes;
+  constexpr int NCH = Path::NCH;
+  constexpr int PF = kPrefetch;
+  using Smem = typename Path::Smem;
+  __shared__ Smem sm;
+  const int lane = threadIdx.x & 63;
+  const int wave = rfl(threadIdx.x >> 6);
+  const int H = p.H;
+  const int P = rfl(p.header[2]);
+  const int total = rfl(p.header[0]) * H;
+  const float sl2 = p.scale_log2;
+
+  if (threadIdx.x == 0) {
+    sm.slot[2] = atomicAdd(&p.header[1], 1);
+    if constexpr (kDeep) sm.slot[3] = atomicAdd(&p.header[1], 1);
+  }
+  __syncthreads();
+  int cur = rfl(sm.slot[2]);
+  int nxt = kDeep ? rfl(sm.slot[3]) : 0;
+  if (cur >= total) return;
+
+  Item it = make_item(p, items[cur / H], cur % H, P, wave);
+  typename Path::Q q;
+  Path::load_q(q, p, it, lane);
+  UnitStream<D, kBytes> st;
+  Frag<NCH> f[PF + 1];
+  bool ok[PF + 1];
+  st.begin(p, it.trow, it.start, it.u0, it.h);
+  st.ids = st.fetch_ids(lane);
+  prologue<PF, NCH>(st, f, ok, lane);
+
+  auto run_item = [&](typename Path::State& s) {
+    Path::reset(s);
+    stream_item<PF, NCH>(p, st, f, ok, it, lane, [&](Frag<NCH>& fr, int u, bool okk) {
+      // A unit whose block id is invalid counts as having no valid token (its
+      // registers are still consumed, which keeps the load waits exact).
+      const int valid = !okk ? 0 : it.ntok - u * 16 < 16 ? it.ntok - u * 16 : 16;
+      Path::compute(s, q, fr, valid, lane, sl2);
+    });
+  };
+
+  for (int k = 0;; ++k) {
+    int nn = 0;
+    if (threadIdx.x == 0) nn = atomicAdd(&p.header[1], 1);
+    if constexpr (kDeep) {
+      // The next item (the current one again after the last: the loads below
+      // are then harmless repeats, and always issuing them keeps the waits in
+      // the stream exact).
+      const bool has_next = nxt < total;
+      const Item nit = make_item(p, items[(has_next ? nxt : cur) / H], (has_next ? nxt : cur) % H, P, wave);
+      typename Path::Q qn;
+      Path::load_q(qn, p, nit, lane);
+      int32_t ids_n;
+      {
+        const int kk = (nit.start + nit.u0 * 16) / p.bs + lane;
+        ids_n = kk < p.max_blocks ? nit.trow[kk] : -1;
+      }
+      typename Path::State s;
+      run_item(s);
+      if (threadIdx.x == 0) sm.slot[k & 1] = nn;
+      // The next item's first units go out before this item's merge.  After
+      // the last item every id reads as invalid, so these loads all hit block
+      // 0 (a cached address); issuing them regardless keeps the waits exact.
+      st.begin(p, nit.trow, nit.start, nit.u0, nit.h);
+      st.ids = has_next ? ids_n : -1;
+      prologue<PF, NCH>(st, f, ok, lane);
+      Path::to_lds(s, sm, wave, lane, p.G);
+      finish_partition<T, D, Smem::kRows>(p, sm, it);
+      __syncthreads();
+      if (!has_next) break;
+      cur = nxt;
+      nxt = rfl(sm.slot[k & 1]);
+      it = nit;
+      q = qn;
+    } else {
+      typename Path::State s;
+      run_item(s);
+      if (threadIdx.x == 0) sm.slot[k & 1] = nn;
+      Path::to_lds(s, sm, wave, lane, p.G);
+      finish_partition<T, D, Smem::kRows>(p, sm, it);
+      __syncthreads();
+      cur = rfl(sm.slot[k & 1]);
+      if (cur >= total) break;
+      it = make_item(p, items[cur / H], cur % H, P, wave);
+      Path::load_q(q, p, it, lane);
+      st.begin(p, it.trow, it.start, it.u0, it.h);
+      st.ids = st.fetch_ids(lane);
+      prologue<PF, NCH>(st, f, ok, lane);
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
 // Log-sum-exp merge of partition states: one wave per (sequence, query head).
 // ---------------------------------------------------------------------------
 template <typename T, int D>
-__global__ __launch_bounds__(kThreads) void merge_kernel(DecodeParams p) {
+__global__ __launch_bounds__(kMergeThreads) void merge_kernel(DecodeParams p) {
   const int lane = threadIdx.x & 63;
-  const int pair = blockIdx.x * kWaves + (threadIdx.x >> 6);
+  const int pair = blockIdx.x * kMergeWaves + (threadIdx.x >> 6);
   if (pair >= p.S * p.Hq) return;
-  const int P = __builtin_amdgcn_readfirstlane(p.header[2]);
-  const int ctx = clamp_ctx_uniform(p, pair / p.Hq);
+  const int P = rfl(p.header[2]);
+  const int ctx = rfl(clamp_ctx(p, pair / p.Hq));
   if (ctx <= P) return;  // written directly by the partition kernel
   int np = (ctx + P - 1) / P;
   np = np > p.max_parts ? p.max_parts : np;
@@ -804,26 +931,30 @@ int persistent_grid(const void* kernel) {
   return grid;
 }
 
-template <typename T, int D, int GM>
+// Items per workgroup from which the deep schedule pays (an upper bound
+// from the host's view: every sequence at the maximum context length).
+constexpr int kDeepItemsPerWorkgroup = 16;
+
+template <typename Path, typename T, int D>
 hipError_t launch_decode_kernel(DecodeParams p, hipStream_t stream) {
-  const void* kern;
-  if constexpr (GM == 1 || GM == 2) {
-    kern = reinterpret_cast<const void*>(&decode_valu_kernel<T, D, GM>);
-  } else {
-    kern = reinterpret_cast<const void*>(&decode_mfma_kernel<T, D, GM>);
-  }
   const int64_t work_bound = static_cast<int64_t>(p.S) * p.max_parts * p.H;
-  int grid = persistent_grid(kern);
+  const void* k_shallow = reinterpret_cast<const void*>(&decode_kernel<Path, T, D, false>);
+  const void* k_deep = reinterpret_cast<const void*>(&decode_kernel<Path, T, D, true>);
+  int grid = persistent_grid(k_shallow);
+  if (grid <= 0) return hipErrorInvalidValue;
+  const bool deep = !p.auto_partition && work_bound >= static_cast<int64_t>(kDeepItemsPerWorkgroup) * grid;
+  if (deep) grid = persistent_grid(k_deep);
   if (grid <= 0) return hipErrorInvalidValue;
   if (grid > work_bound) grid = static_cast<int>(work_bound);
   p.grid = grid;
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if constexpr (GM == 1 || GM == 2) {
-    hipLaunchKernelGGL((decode_valu_kernel<T, D, GM>), dim3(grid), dim3(kThreads), 0, stream, p);
+  const int4* items = static_cast<const int4*>(p.items);
+  if (deep) {
+    hipLaunchKernelGGL((decode_kernel<Path, T, D, true>), dim3(grid), dim3(kThreads), 0, stream, p, items);
   } else {
-    hipLaunchKernelGGL((decode_mfma_kernel<T, D, GM>), dim3(grid), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((decode_kernel<Path, T, D, false>), dim3(grid), dim3(kThreads), 0, stream, p, items);
   }
   return hipGetLastError();
 }
@@ -832,20 +963,20 @@ template <typename T, int D>
 hipError_t launch_typed(const DecodeParams& p, hipStream_t stream) {
   hipError_t e;
   if (p.G == 1) {
-    e = launch_decode_kernel<T, D, 1>(p, stream);
+    e = launch_decode_kernel<ValuPath<T, D, 1>, T, D>(p, stream);
   } else if (p.G == 2) {
-    e = launch_decode_kernel<T, D, 2>(p, stream);
+    e = launch_decode_kernel<ValuPath<T, D, 2>, T, D>(p, stream);
   } else if (p.G <= 4) {
-    e = launch_decode_kernel<T, D, 4>(p, stream);
+    e = launch_decode_kernel<MfmaPath<T, D, 4>, T, D>(p, stream);
   } else if (p.G <= 8) {
-    e = launch_decode_kernel<T, D, 8>(p, stream);
+    e = launch_decode_kernel<MfmaPath<T, D, 8>, T, D>(p, stream);
   } else {
-    e = launch_decode_kernel<T, D, 16>(p, stream);
+    e = launch_decode_kernel<MfmaPath<T, D, 16>, T, D>(p, stream);
   }
   if (e != hipSuccess || p.max_parts <= 1) return e;
   const int pairs = p.S * p.Hq;
-  hipLaunchKernelGGL((merge_kernel<T, D>), dim3((pairs + kWaves - 1) / kWaves), dim3(kThreads), 0,
-                     stream, p);
+  hipLaunchKernelGGL((merge_kernel<T, D>), dim3((pairs + kMergeWaves - 1) / kMergeWaves), dim3(kMergeThreads),
+                     0, stream, p);
   return hipGetLastError();
 }
 

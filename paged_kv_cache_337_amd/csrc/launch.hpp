@@ -31,7 +31,7 @@ struct DecodeParams {
   int32_t grid;              // workgroups of the decode kernel
   int32_t max_parts;         // ceil(ctx_cap / P)
   int32_t* header;           // [0] work items, [1] next work index, [2] P used (device)
-  int2* items;               // [S * max_parts] (sequence, partition), longest first
+  int4* items;               // [S * max_parts] (sequence, partition, context, partitions), longest first
   float* ws_o;               // [S, Hq, max_parts, D]
   float* ws_ml;              // [S, Hq, max_parts, 2] (max in log2 units, sum)
 };
@@ -47,7 +47,7 @@ inline WsLayout decode_ws_layout(int S, int Hq, int max_parts, int D) {
   WsLayout w;
   w.header_off = 0;
   w.items_off = 256;
-  w.o_off = align(w.items_off + static_cast<size_t>(S) * max_parts * sizeof(int2));
+  w.o_off = align(w.items_off + static_cast<size_t>(S) * max_parts * sizeof(int4));
   const size_t parts = max_parts > 1 ? static_cast<size_t>(S) * Hq * max_parts : 0;
   w.ml_off = align(w.o_off + parts * D * sizeof(float));
   w.total = align(w.ml_off + parts * 2 * sizeof(float));

@@ -81,6 +81,22 @@ def test_split_k_any_partition_matches_oracle(P):
     U.check_close(U.out_f64(out), U.oracle_rows(w, range(w.num_seqs)), "bf16", f"P={P}")
 
 
+@pytest.mark.parametrize("dtype,hq,hkv,bs,P", [("bf16", 32, 8, 16, 64), ("f16", 16, 16, 16, 32),
+                                                ("bf16", 64, 8, 32, 128)])
+def test_many_small_partitions_match_oracle(dtype, hq, hkv, bs, P):
+    """An explicit small partition size gives each workgroup dozens of items:
+    the schedule that runs two work indices ahead and overlaps one item's
+    merge with the next item's first loads."""
+    ctx = np.random.default_rng(81).integers(600, 2000, 64, endpoint=True).tolist()
+    w = W.custom("deep", 82, dtype, ctx, hq, hkv, 128, bs, partition_tokens=P)
+    U.log(f"[deep] {dtype} Hq={hq} Hkv={hkv} bs={bs} P={P} items~{sum(-(-c // P) for c in ctx) * hkv}")
+    pool = U.make_pool(w)
+    U.fill_pool(pool, w)
+    q, t, c = U.device_inputs(w)
+    out = U.run_decode(pool, w, q, t, c)
+    U.check_close(U.out_f64(out), U.oracle_rows(w, range(w.num_seqs)), dtype, f"deep P={P}")
+
+
 @pytest.mark.parametrize("dtype,hq,hkv,d", [("bf16", 32, 8, 128), ("f16", 8, 8, 128), ("f32", 4, 4, 64),
                                              ("f32", 8, 2, 128), ("bf16", 4, 2, 64)])
 def test_single_token_context_returns_v_exactly(dtype, hq, hkv, d):
