@@ -36,7 +36,10 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="llama3_8b",
-                    choices=["tiny", "opt13b", "llama3_8b", "long_ctx"])
+                    choices=["tiny", "opt13b", "llama3_8b", "long_ctx", "shared", "shared_cow"])
+    ap.add_argument("--contiguous", action="store_true",
+                    help="place every sequence's blocks side by side in logical order (a "
+                         "contiguous-cache control for the same kernel)")
     ap.add_argument("--layers", type=int, default=4)
     ap.add_argument("--partition-tokens", type=int, default=-1,
                     help="-1: the workload's own setting (0 = library default)")
@@ -70,7 +73,7 @@ def counter_traffic(workload: str):
     return int(r["traffic_bytes_per_call"])
 
 
-def cpu_baseline(w, budget_s):
+def cpu_baseline(w, budget_s, tables, ctx):
     """Time the CPU oracle as it stands (gather through the block table, then
     float64 two-pass softmax) on the first sequences of the same batch, until
     the wall-clock budget is spent."""
@@ -87,12 +90,12 @@ def cpu_baseline(w, budget_s):
     eb = 4 if w.dtype == "f32" else 2
     for i in range(w.num_seqs):
         K, V = w.seq_kv(i)
-        LY.scatter(pool, g, 0, w.block_tables[i], K, V)  # input staging, not timed
+        LY.scatter(pool, g, 0, tables[i], K, V)  # input staging, not timed
         t0 = time.perf_counter()
-        A.paged_decode(pool, g, 0, w.q, w.block_tables, w.context_lens, w.scale, seqs=[i])
+        A.paged_decode(pool, g, 0, w.q, tables, ctx, w.scale, seqs=[i])
         t_total += time.perf_counter() - t0
         done += 1
-        kv_bytes += int(w.context_lens[i]) * 2 * w.num_kv_heads * w.head_dim * eb
+        kv_bytes += int(ctx[i]) * 2 * w.num_kv_heads * w.head_dim * eb
         if t_total >= budget_s:
             break
     return {
@@ -103,7 +106,7 @@ def cpu_baseline(w, budget_s):
         "host_cpus": len(os.sched_getaffinity(0)),
         "kind": "oracle",
         "sample": f"first {done} of {w.num_seqs} sequences of the same batch "
-                  f"({int(w.context_lens[:done].sum())} tokens), {t_total:.1f} s of oracle time",
+                  f"({int(ctx[:done].sum())} tokens), {t_total:.1f} s of oracle time",
     }
 
 
@@ -126,19 +129,31 @@ def main():
         f"layers={L} P={P}")
 
     t0 = time.time()
-    pool = U.make_pool(w, layers=L)
-    for layer in range(L):
-        U.fill_pool(pool, w, layer=layer)
+    shared = w.script is not None
+    if shared:
+        # prefix sharing through the block manager (fork, append, copy-on-write)
+        pool = pa.Pool(L, w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim, w.dtype,
+                       free_order=w.script["free_order"])
+        U.poison(pool)
+        U.run_shared_script(pool, w, W.shared_prefix_kv, W.private_kv, layers=range(L))
+        width = max(len(pool.seq_block_table(s)[0]) for s in range(w.num_seqs))
+        host_tables, host_ctx = pool.batch_tables(list(range(w.num_seqs)), width)
+    else:
+        host_tables = U.contiguous_tables(w) if args.contiguous else w.block_tables
+        host_ctx = w.context_lens
+        pool = U.make_pool(w, layers=L)
+        for layer in range(L):
+            U.fill_pool(pool, w, layer=layer, tables=host_tables)
     log(f"[bench] pool filled ({pool.nbytes / 1e9:.2f} GB) in {time.time() - t0:.1f} s")
 
     # new-token inputs: each sequence's last position (its current token)
-    last = w.context_lens - 1
+    last = host_ctx - 1
     kn = np.stack([w.seq_kv(i)[0][last[i]] for i in range(w.num_seqs)])
     vn = np.stack([w.seq_kv(i)[1][last[i]] for i in range(w.num_seqs)])
-    slots_new = pa.slots_for_positions(w.block_tables, w.block_size, last, np.ones(w.num_seqs))
+    slots_new = pa.slots_for_positions(host_tables, w.block_size, last, np.ones(w.num_seqs))
     k_new, v_new = U.dev_tensor(kn, w.dtype), U.dev_tensor(vn, w.dtype)
     slot_new = torch.from_numpy(slots_new).cuda()
-    q, tables, ctx = U.device_inputs(w)
+    q, tables, ctx = U.device_inputs(w, tables=host_tables, ctx=host_ctx)
     out = torch.empty_like(q)
     ws_bytes = pool.workspace_bytes(w.num_seqs, w.num_q_heads, w.max_context_len, P)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
@@ -175,8 +190,16 @@ def main():
     ms_per_step = wall * 1e3 / args.steps
     ev_ms = e_all[0].elapsed_time(e_all[1]) / args.steps
     dec_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
-    kv_bytes = int(w.context_lens.astype(np.int64).sum()) * 2 * w.num_kv_heads * w.head_dim * eb
-    nblk = int(sum(-(-int(c) // w.block_size) for c in w.context_lens))
+    tok_bytes = 2 * w.num_kv_heads * w.head_dim * eb
+    kv_bytes = int(host_ctx.astype(np.int64).sum()) * tok_bytes
+    nblk = int(sum(-(-int(c) // w.block_size) for c in host_ctx))
+    # distinct cache slots the batch reads (below the logical count when blocks are shared)
+    slots_read = set()
+    for i in range(w.num_seqs):
+        pos = np.arange(int(host_ctx[i]))
+        slots_read.update((host_tables[i][pos // w.block_size].astype(np.int64) * w.block_size
+                           + pos % w.block_size).tolist())
+    unique_kv_bytes = len(slots_read) * tok_bytes
     qo_bytes = 2 * w.num_seqs * w.num_q_heads * w.head_dim * eb
     alg_bytes = kv_bytes + qo_bytes + 4 * nblk + 4 * w.num_seqs
     value = kv_bytes / (ms_per_step * 1e-3) / 1e9
@@ -196,13 +219,17 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": f"{w.name}: paged decode layer, {w.num_seqs} seqs, {w.num_q_heads}q/{w.num_kv_heads}kv "
-                        f"heads, head_dim {w.head_dim}, block_size {w.block_size}",
+                        f"heads, head_dim {w.head_dim}, block_size {w.block_size}"
+                        + (", contiguous block placement" if args.contiguous and not shared else ""),
             "batch": w.num_seqs, "total_context_tokens": w.total_tokens,
             "max_context_len": max_ctx, "partition_tokens": P or 512,
             "layer_slots_rotated": L,
             "step": "pa_write_kv (1 new token/seq) + pa_decode",
         },
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "kv_bytes_logical": kv_bytes,
+        "kv_bytes_unique": unique_kv_bytes,
+        "unique_kv_gbs": round(unique_kv_bytes / (ms_per_step * 1e-3) / 1e9, 2),
         "seqs_per_s": round(w.num_seqs / (ms_per_step * 1e-3), 1),
         "event_ms_per_step": round(ev_ms, 5),
         "roofline": {
@@ -212,7 +239,8 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": counter_traffic(w.name) if P == w.partition_tokens and L == 4 else None,
+            "traffic": (counter_traffic(w.name)
+                        if P == w.partition_tokens and L == 4 and not args.contiguous else None),
             "alg_bytes_per_launch": alg_bytes,
             "avg_launch_ms": round(dec_ms, 5),
         },
@@ -226,7 +254,7 @@ def main():
         log(f"[bench] copy calibration: {n} blocks, {nbytes} bytes read and {nbytes} written")
         res["copy_calibration_bytes"] = nbytes
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(w, args.cpu_budget_s)
+        res["cpu_baseline"] = cpu_baseline(w, args.cpu_budget_s, host_tables, host_ctx)
     print(json.dumps(res), flush=True)
 
 

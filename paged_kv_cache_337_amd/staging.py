@@ -4,7 +4,9 @@ Uploads numpy arrays in a storage dtype (bf16 as uint16 bits) to device
 tensors, poisons a pool with quiet NaNs, and fills a pool with a batch's cached
 tokens through pa_write_kv, with slots from the library's table translation.
 Works with any batch object exposing ``num_seqs``, ``dtype``, ``block_size``,
-``block_tables``, ``context_lens``, ``q`` and ``seq_kv(i)``.
+``block_tables``, ``context_lens``, ``q`` and ``seq_kv(i)``.  Prefix-sharing
+batches (``script`` set) are built through the library's block manager:
+fork, append, copy-on-write copies and token writes, one decode step at a time.
 """
 from __future__ import annotations
 
@@ -78,3 +80,61 @@ def device_inputs(batch, tables=None, ctx=None, device="cuda"):
 
 def pool_bits(pool: Pool) -> np.ndarray:
     return pool.buf.view(TORCH_BITS[pool.dtype]).cpu().numpy().view(BITS[pool.dtype])
+
+
+def contiguous_tables(batch) -> np.ndarray:
+    """Block tables that place every sequence's blocks side by side in logical
+    order (blocks 0.. for the first sequence, then the next, ...)."""
+    bs = batch.block_size
+    nb = [-(-int(c) // bs) for c in batch.context_lens]
+    tables = np.full((batch.num_seqs, max(nb)), -1, dtype=np.int32)
+    off = 0
+    for i, n in enumerate(nb):
+        tables[i, :n] = np.arange(off, off + n, dtype=np.int32)
+        off += n
+    return tables
+
+
+def run_shared_script(pool: Pool, w, prefix_kv, private_kv, layers=(0,), device="cuda"):
+    """Build a prefix-sharing batch in ``pool`` through the library's block
+    manager: per group the prefix is appended to one sequence and written,
+    then the other branches are forked from it; the private tokens are then
+    appended one decode step at a time, every sequence in ascending id order,
+    with the copy-on-write pairs of a step copied before its tokens are
+    written.  Every listed layer receives the same tokens.  ``prefix_kv(w, g)``
+    and ``private_kv(w, s)`` give a group's prefix rows and a sequence's
+    private rows.  Returns the copy pairs in order."""
+    sc = w.script
+    B, P, X = sc["branches"], sc["prefix"], sc["private"]
+    copies = []
+    for grp in range(sc["groups"]):
+        s0 = pool.seq_create()
+        slots, pairs = pool.seq_append(s0, P)
+        assert not pairs
+        pk, pv = prefix_kv(w, grp)
+        kd, vd = dev_tensor(pk, w.dtype, device), dev_tensor(pv, w.dtype, device)
+        sd = torch.from_numpy(slots).to(device)
+        for layer in layers:
+            pool.write_kv(layer, kd, vd, sd)
+        for _ in range(B - 1):
+            pool.seq_fork(s0)
+    priv = [private_kv(w, s) for s in range(w.num_seqs)]
+    pk_all = np.stack([p[0] for p in priv], axis=1)  # [X, S, H, D]
+    pv_all = np.stack([p[1] for p in priv], axis=1)
+    for step in range(X):
+        slots = np.empty(w.num_seqs, dtype=np.int32)
+        step_pairs = []
+        for s in range(w.num_seqs):
+            sl, pairs = pool.seq_append(s, 1)
+            slots[s] = sl[0]
+            step_pairs += pairs
+        if step_pairs:
+            pool.copy_blocks(torch.tensor(step_pairs, dtype=torch.int32).to(device))
+            copies += step_pairs
+        kd = dev_tensor(pk_all[step], w.dtype, device)
+        vd = dev_tensor(pv_all[step], w.dtype, device)
+        sd = torch.from_numpy(slots).to(device)
+        for layer in layers:
+            pool.write_kv(layer, kd, vd, sd)
+    torch.cuda.synchronize()
+    return copies

@@ -23,6 +23,7 @@ pytestmark = pytest.mark.gpu
 import workloads as W  # noqa: E402
 from tests import gpu_util as U  # noqa: E402
 from tests.shared_script import oracle_shared_run  # noqa: E402
+from paged_kv_cache_337_amd import staging as S  # noqa: E402
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -34,37 +35,10 @@ def _gpu():
 
 def _run_script_on_device(w, layers, layer):
     import paged_kv_cache_337_amd as pa
-    sc = w.script
     pool = pa.Pool(layers, w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim, w.dtype,
-                   free_order=sc["free_order"])
+                   free_order=w.script["free_order"])
     U.poison(pool)
-    B, P, X = sc["branches"], sc["prefix"], sc["private"]
-    copies = []
-    for grp in range(sc["groups"]):
-        s0 = pool.seq_create()
-        slots, pairs = pool.seq_append(s0, P)
-        assert not pairs
-        pk, pv = W.shared_prefix_kv(w, grp)
-        pool.write_kv(layer, U.dev_tensor(pk, w.dtype), U.dev_tensor(pv, w.dtype),
-                      torch.from_numpy(slots).cuda())
-        for _ in range(B - 1):
-            pool.seq_fork(s0)
-    priv = [W.private_kv(w, s) for s in range(w.num_seqs)]
-    pk_all = np.stack([p[0] for p in priv], axis=1)  # [X, S, H, D]
-    pv_all = np.stack([p[1] for p in priv], axis=1)
-    for step in range(X):
-        slots = np.empty(w.num_seqs, dtype=np.int32)
-        step_pairs = []
-        for s in range(w.num_seqs):
-            sl, pairs = pool.seq_append(s, 1)
-            slots[s] = sl[0]
-            step_pairs += pairs
-        if step_pairs:
-            pool.copy_blocks(torch.tensor(step_pairs, dtype=torch.int32).cuda())
-            copies += step_pairs
-        pool.write_kv(layer, U.dev_tensor(pk_all[step], w.dtype), U.dev_tensor(pv_all[step], w.dtype),
-                      torch.from_numpy(slots).cuda())
-    torch.cuda.synchronize()
+    copies = S.run_shared_script(pool, w, W.shared_prefix_kv, W.private_kv, layers=(layer,))
     return pool, copies
 
 
