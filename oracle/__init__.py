@@ -1,4 +1,4 @@
-"""CPU oracle for paged single-token decode attention -- TEST INFRASTRUCTURE ONLY.
+"""CPU oracle for paged decode and prefill attention -- TEST INFRASTRUCTURE ONLY.
 
 Plain, slow, float64 NumPy code that defines what the HIP path must compute.
 Only the test suite, the smoke check and the CPU-baseline leg of the benchmark
@@ -10,7 +10,7 @@ Modules
   layout     pool element index formula, scatter of logical K/V into a pool,
              gather of a sequence's K/V through its block table
   attention  two-pass softmax decode attention over gathered K/V, split-K with
-             log-sum-exp merge
+             log-sum-exp merge, causal prefill of a sequence's newest tokens
   allocator  reference model of the refcounted block allocator with
              copy-on-write
 

@@ -20,6 +20,14 @@ by log-sum-exp weighting (``split_decode``); in exact arithmetic this equals the
 unsplit result (the pages' FlashAttention comparison names online softmax as
 the standard technique; the partition scheme itself is this library's).
 
+Prefill of new tokens (``prefill_one``, ``paged_prefill``): a sequence whose
+context of T tokens ends with n new tokens, already written to the cache,
+attends from each new token to every cached token up to and including its own
+position -- standard causal attention ("PagedAttention: paging the KV cache
+like an OS pages memory", "How it works"; the blocks for the new tokens are
+allocated first, "Paged Attention Explained", "How Paged Attention Works",
+Step 2).  New token k (0-based) sits at position T - n + k.
+
 The scale is taken as the float32 value the device receives.  Inputs arrive in
 their storage dtype and are widened to float64 exactly.
 """
@@ -110,3 +118,39 @@ def paged_decode(pool: np.ndarray, g: layout.Geometry, layer: int, q: np.ndarray
         K, V = layout.gather(pool, g, layer, block_tables[i], int(context_lens[i]))
         out.append(decode_one(to_f64(q[i], g.dtype), to_f64(K, g.dtype), to_f64(V, g.dtype), scale))
     return np.stack(out)
+
+
+def prefill_one(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float, rows=None) -> np.ndarray:
+    """Causal attention of the n newest tokens of a T-token context.
+
+    q [n, Hq, D] are the new tokens' query rows; K, V [T, Hkv, D] hold every
+    cached token, the new ones included.  Row k is at position T - n + k and
+    attends to positions 0 .. T - n + k.  Returns [len(rows), Hq, D] for the
+    listed rows (all by default)."""
+    n = q.shape[0]
+    T = K.shape[0]
+    if n < 1 or n > T:
+        raise ValueError("need 1 <= new tokens <= context length")
+    rows = range(n) if rows is None else rows
+    out = []
+    for k in rows:
+        pos = T - n + int(k)
+        out.append(decode_one(q[k], K[:pos + 1], V[:pos + 1], scale))
+    return np.stack(out)
+
+
+def paged_prefill(pool: np.ndarray, g: layout.Geometry, layer: int, q: np.ndarray,
+                  query_start: np.ndarray, block_tables: np.ndarray, context_lens: np.ndarray,
+                  scale: float, seqs=None, rows=None) -> list:
+    """Per listed sequence (all by default), the [n_i, Hq, D] float64 outputs of
+    its new tokens q[query_start[i]:query_start[i+1]]: gather the sequence's
+    K/V through its table, then ``prefill_one`` (optionally only ``rows[i]``)."""
+    seqs = range(len(context_lens)) if seqs is None else seqs
+    out = []
+    for i in seqs:
+        a, b = int(query_start[i]), int(query_start[i + 1])
+        K, V = layout.gather(pool, g, layer, block_tables[i], int(context_lens[i]))
+        r = None if rows is None else rows[i]
+        out.append(prefill_one(to_f64(q[a:b], g.dtype), to_f64(K, g.dtype), to_f64(V, g.dtype),
+                               scale, rows=r))
+    return out

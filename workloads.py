@@ -21,6 +21,14 @@ Workloads (shapes from the pages' settings, values synthetic):
   * ``shared_cow`` the same with a 2040-token prefix, so the last shared block
                    is partial and the first append of a branch copies it.
 
+Prefill workloads (new tokens appended to a sequence and attended causally):
+  * ``prefill_tiny``       fp32, 4/2 heads, d=64: whole prompt, chunks, one token.
+  * ``prefill_llama3_8b``  16 whole Llama-3-8B-shaped prompts, bf16, lengths from
+                           the decode batch's lognormal.
+  * ``chunked_llama3_8b``  64 sequences, lognormal cached context + 256 new tokens.
+Their K/V rows are drawn per sequence exactly as for decode (the new tokens'
+rows are the last ones); their query rows are drawn after the placement.
+
 The pages' OPT-13B / Alpaca experiments are stood in for by these shapes only
 (no trace and no weights are used).
 
@@ -95,6 +103,20 @@ class PagedWorkload:
     num_layers: int = 1
     # shared-prefix workloads: description of the fork/append script
     script: dict | None = field(default=None)
+    # prefill workloads: new tokens per sequence (the last query_lens[i] of its
+    # context); q then holds their query rows, [sum(query_lens), Hq, D]
+    query_lens: np.ndarray | None = field(default=None)
+
+    @property
+    def query_start(self) -> np.ndarray:
+        """Offsets of each sequence's new tokens in q, int32 [S + 1]."""
+        qs = np.zeros(self.num_seqs + 1, dtype=np.int32)
+        qs[1:] = np.cumsum(self.query_lens)
+        return qs
+
+    @property
+    def max_query_len(self) -> int:
+        return int(self.query_lens.max())
 
     @property
     def max_blocks_per_seq(self) -> int:
@@ -240,6 +262,70 @@ def shared(seed: int = 5) -> PagedWorkload:
 
 def shared_cow(seed: int = 6) -> PagedWorkload:
     return _shared("shared_cow", seed, prefix=2040)
+
+
+def _prefill(name, seed, dtype, ctx, qlens, hq, hkv, d, bs, kv_std=1.0, width=None, extra_blocks=0):
+    """Prefill batch: sequence i has a context of ctx[i] tokens whose last
+    qlens[i] are new.  Draw order: perm, then the new tokens' query rows."""
+    rng = np.random.default_rng(seed)
+    ctx = np.asarray(ctx, dtype=np.int32)
+    qlens = np.asarray(qlens, dtype=np.int32)
+    if ctx.shape != qlens.shape or np.any(qlens < 1) or np.any(qlens > ctx):
+        raise ValueError("need 1 <= query_lens <= context_lens")
+    n = sum(_blocks_for(c, bs) for c in ctx) + extra_blocks
+    perm = rng.permutation(n).astype(np.int32)
+    tables = _place(ctx, perm, bs, width)
+    q = round_to_storage(rng.standard_normal((int(qlens.sum()), hq, d), dtype=np.float32), dtype)
+    return PagedWorkload(name=name, dtype=dtype, num_seqs=len(ctx), num_q_heads=hq,
+                         num_kv_heads=hkv, head_dim=d, block_size=bs, num_blocks=n,
+                         context_lens=ctx, block_tables=tables, q=q,
+                         scale=float(np.float32(1.0 / np.sqrt(d))), partition_tokens=0,
+                         kv_std=kv_std, seed=seed, query_lens=qlens)
+
+
+def _lognormal_lengths(rng, count, median=1024.0, sigma=0.8, lo=16, hi=8192):
+    z = rng.standard_normal(count)
+    return np.clip(np.rint(np.exp(np.log(median) + sigma * z)), lo, hi).astype(np.int64)
+
+
+def prefill_tiny(seed: int = 7) -> PagedWorkload:
+    """fp32, 4/2 heads, d=64: a whole 7-token prompt, chunks of 5 and 20 new
+    tokens after cached ones, and a single new token."""
+    return _prefill("prefill_tiny", seed, "f32", [7, 16, 33, 50], [7, 5, 1, 20], 4, 2, 64, 16,
+                    extra_blocks=3)
+
+
+def prefill_llama3_8b(seed: int = 8) -> PagedWorkload:
+    """Llama-3-8B-shaped GQA prompts, bf16: 16 whole prompts whose lengths
+    follow the decode batch's distribution (lognormal, median 1024, sigma 0.8,
+    clipped to [16, 8192])."""
+    rng = np.random.default_rng([seed, 0])
+    ctx = _lognormal_lengths(rng, 16)
+    return _prefill("prefill_llama3_8b", seed, "bf16", ctx, ctx, 32, 8, 128, 16, width=8192 // 16)
+
+
+def chunked_llama3_8b(seed: int = 9) -> PagedWorkload:
+    """Chunked prefill, Llama-3-8B-shaped GQA, bf16: 64 sequences, each with a
+    cached context (lognormal, median 1024, sigma 0.8, clipped to [16, 8192])
+    followed by a chunk of 256 new tokens."""
+    rng = np.random.default_rng([seed, 0])
+    ctx = _lognormal_lengths(rng, 64) + 256
+    return _prefill("chunked_llama3_8b", seed, "bf16", ctx, np.full(64, 256), 32, 8, 128, 16,
+                    width=(8192 + 256) // 16)
+
+
+def custom_prefill(name: str, seed: int, dtype: str, ctx, qlens, hq: int, hkv: int, d: int,
+                   bs: int, kv_std: float = 1.0, extra_blocks: int = 0) -> PagedWorkload:
+    """A prefill workload of any shape."""
+    return _prefill(name, seed, dtype, ctx, qlens, hq, hkv, d, bs, kv_std=kv_std,
+                    extra_blocks=extra_blocks)
+
+
+PREFILL_WORKLOADS = {
+    "prefill_tiny": prefill_tiny,
+    "prefill_llama3_8b": prefill_llama3_8b,
+    "chunked_llama3_8b": chunked_llama3_8b,
+}
 
 
 WORKLOADS = {
