@@ -24,9 +24,9 @@
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  All
  *     device work is enqueued asynchronously; nothing synchronises implicitly.
  *   - A pool handle is not thread-safe: one thread at a time.
- *   - Setting the environment variable PA_DEBUG=1 makes pa_write_kv and
- *     pa_decode copy their index arguments to the host and validate them
- *     (synchronising the stream) before launching.
+ *   - Setting the environment variable PA_DEBUG=1 makes pa_write_kv,
+ *     pa_decode and pa_prefill copy their index arguments to the host and
+ *     validate them (synchronising the stream) before launching.
  *
  * Pool layout in device memory (this library's own design; the pages fix
  * only fixed-size blocks addressed through a table).  Element order, outer to
@@ -163,6 +163,29 @@ int pa_decode(const pa_pool* pool, int layer, const void* q, int num_seqs, int n
               const int32_t* context_lens, int max_context_len, float scale,
               int partition_tokens, void* workspace, size_t ws_bytes, void* out,
               void* stream);
+
+/* Causal prefill attention of each sequence's newest tokens over the paged
+ * cache (standard causal attention per "How it works"; the new tokens' blocks
+ * are reserved and written first, "How Paged Attention Works", Steps 2-3).
+ * Sequence i owns new tokens query_start[i] .. query_start[i+1] - 1 of q,
+ * n_i of them; they are the last n_i positions of its context, already
+ * written with pa_write_kv.  New token k (position P = ctx_i - n_i + k) and
+ * query head g (kv head h = g / (num_q_heads / H_KV)) give
+ *     out[query_start[i] + k, g] = softmax_p(scale * q[., g] . K_i[p, h]) . V_i[p, h],
+ *     p = 0 .. P.
+ *   q, out             device [num_query_tokens, num_q_heads, D], pool dtype,
+ *                      16-byte aligned; out rows of no sequence are untouched
+ *   query_start        device int32 [num_seqs + 1], query_start[0] = 0,
+ *                      non-decreasing, last entry <= num_query_tokens
+ *   max_query_len      host value >= every n_i (sizes the grid)
+ *   block_tables, context_lens, max_context_len, scale: as for pa_decode,
+ *                      with n_i <= context_lens[i]
+ * No workspace.  Asynchronous on `stream`.  Errors: INVALID_ARG, UNSUPPORTED
+ * (shape, or max_query_len beyond the grid limit given in the message). */
+int pa_prefill(const pa_pool* pool, int layer, const void* q, int num_seqs, int num_q_heads,
+               const int32_t* query_start, int num_query_tokens, int max_query_len,
+               const int32_t* block_tables, int max_blocks_per_seq, const int32_t* context_lens,
+               int max_context_len, float scale, void* out, void* stream);
 
 /* Copy whole blocks (every layer, head, K and V) for copy-on-write.
  *   pairs  device int32 [n, 2] of (source, destination) block ids.

@@ -31,7 +31,7 @@ ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2}
 # Every symbol include/pa.h declares, in declaration order.
 EXPORTS = [
     "pa_version", "pa_last_error", "pa_pool_required_bytes", "pa_alloc_pool", "pa_free",
-    "pa_write_kv", "pa_decode_workspace_bytes", "pa_decode", "pa_copy_blocks",
+    "pa_write_kv", "pa_decode_workspace_bytes", "pa_decode", "pa_prefill", "pa_copy_blocks",
     "pa_seq_create", "pa_seq_append", "pa_seq_fork", "pa_seq_release", "pa_seq_block_table",
     "pa_batch_tables", "pa_pool_state", "pa_pool_stats", "pa_slots_for_positions",
 ]
@@ -73,6 +73,8 @@ def _load():
         "pa_decode_workspace_bytes": (c_sz, [vp, c_int, c_int, c_int, c_int]),
         "pa_decode": (c_int, [vp, c_int, vp, c_int, c_int, vp, c_int, vp, c_int, ctypes.c_float,
                               c_int, vp, c_sz, vp, vp]),
+        "pa_prefill": (c_int, [vp, c_int, vp, c_int, c_int, vp, c_int, c_int, vp, c_int, vp, c_int,
+                               ctypes.c_float, vp, vp]),
         "pa_copy_blocks": (c_int, [vp, vp, c_int, vp]),
         "pa_seq_create": (c_int, [vp, intp]),
         "pa_seq_append": (c_int, [vp, c_int, c_int, i32p, i32p, intp]),
@@ -205,6 +207,21 @@ class Pool:
                              int(block_tables.shape[1]), _ptr(context_lens), int(max_context_len),
                              float(scale), int(partition_tokens), _ptr(workspace), wsb, _ptr(out),
                              _stream(stream)), "pa_decode")
+        return out
+
+    def prefill(self, layer: int, q: torch.Tensor, query_start: torch.Tensor, max_query_len: int,
+                block_tables: torch.Tensor, context_lens: torch.Tensor, max_context_len: int,
+                scale: float, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+        """Causal attention of each sequence's newest tokens (rows
+        query_start[i] .. query_start[i+1] - 1 of q) over its cached context."""
+        self._need_device()
+        T, Hq, _ = q.shape
+        if out is None:
+            out = torch.empty_like(q)
+        _check(lib.pa_prefill(self.handle, layer, _ptr(q), int(query_start.shape[0]) - 1, Hq,
+                              _ptr(query_start), T, int(max_query_len), _ptr(block_tables),
+                              int(block_tables.shape[1]), _ptr(context_lens), int(max_context_len),
+                              float(scale), _ptr(out), _stream(stream)), "pa_prefill")
         return out
 
     def copy_blocks(self, pairs: torch.Tensor, stream=None):

@@ -23,6 +23,7 @@ SOURCES = [
     os.path.join(CSRC, "allocator.cpp"),
     os.path.join(CSRC, "kernels", "cache_ops.hip"),
     os.path.join(CSRC, "kernels", "decode.hip"),
+    os.path.join(CSRC, "kernels", "prefill.hip"),
 ]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

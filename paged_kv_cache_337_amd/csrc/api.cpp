@@ -282,6 +282,85 @@ int pa_decode(const pa_pool* pool, int layer, const void* q, int num_seqs, int n
   });
 }
 
+int pa_prefill(const pa_pool* pool, int layer, const void* q, int num_seqs, int num_q_heads,
+               const int32_t* query_start, int num_query_tokens, int max_query_len,
+               const int32_t* block_tables, int max_blocks_per_seq, const int32_t* context_lens,
+               int max_context_len, float scale, void* out, void* stream) {
+  return guarded([&]() -> int {
+    if (!pool) return fail(PA_ERR_INVALID_ARG, "pool is NULL");
+    const pa_pool_desc& d = pool->desc;
+    if (layer < 0 || layer >= d.num_layers) return fail(PA_ERR_INVALID_ARG, "layer out of range");
+    if (num_seqs < 0 || num_query_tokens < 0 || max_query_len < 0)
+      return fail(PA_ERR_INVALID_ARG, "counts cannot be negative");
+    if (num_seqs == 0 || num_query_tokens == 0) return PA_OK;
+    if (num_q_heads <= 0 || num_q_heads % d.num_kv_heads)
+      return fail(PA_ERR_INVALID_ARG, "num_q_heads must be a positive multiple of num_kv_heads");
+    const int G = num_q_heads / d.num_kv_heads;
+    if (!pa::decode_supported(d.dtype, d.head_dim, G))
+      return fail(PA_ERR_UNSUPPORTED, "no kernel for G=" + std::to_string(G));
+    if (static_cast<int64_t>(num_seqs) * d.num_kv_heads > INT32_MAX)
+      return fail(PA_ERR_UNSUPPORTED, "num_seqs * num_kv_heads must fit in 31 bits");
+    if (max_query_len <= 0) return fail(PA_ERR_INVALID_ARG, "max_query_len must be positive");
+    if (max_query_len > pa::prefill_max_query_len(G))
+      return fail(PA_ERR_UNSUPPORTED, "max_query_len above " + std::to_string(pa::prefill_max_query_len(G)));
+    if (!q || !out || !query_start || !block_tables || !context_lens)
+      return fail(PA_ERR_INVALID_ARG, "NULL device pointer");
+    if (!aligned16(q) || !aligned16(out)) return fail(PA_ERR_INVALID_ARG, "q and out must be 16-byte aligned");
+    if (max_blocks_per_seq <= 0 || max_context_len <= 0)
+      return fail(PA_ERR_INVALID_ARG, "max_blocks_per_seq and max_context_len must be positive");
+    if (!std::isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "scale must be finite");
+    const int bs = d.block_size;
+    const int64_t cap64 = std::min<int64_t>(max_context_len, static_cast<int64_t>(max_blocks_per_seq) * bs);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (debug_enabled()) {
+      std::vector<int32_t> hc(num_seqs), hq(num_seqs + 1), ht(static_cast<size_t>(num_seqs) * max_blocks_per_seq);
+      hipError_t e = hipMemcpyAsync(hc.data(), context_lens, sizeof(int32_t) * num_seqs, hipMemcpyDeviceToHost, s);
+      if (e == hipSuccess)
+        e = hipMemcpyAsync(hq.data(), query_start, sizeof(int32_t) * (num_seqs + 1), hipMemcpyDeviceToHost, s);
+      if (e == hipSuccess)
+        e = hipMemcpyAsync(ht.data(), block_tables, sizeof(int32_t) * ht.size(), hipMemcpyDeviceToHost, s);
+      if (e == hipSuccess) e = hipStreamSynchronize(s);
+      if (e != hipSuccess) return hip_fail(e, "PA_DEBUG readback");
+      if (hq[0] != 0 || hq[num_seqs] > num_query_tokens)
+        return fail(PA_ERR_INVALID_ARG, "query_start must start at 0 and end within num_query_tokens");
+      for (int i = 0; i < num_seqs; ++i) {
+        const int n = hq[i + 1] - hq[i];
+        if (n < 0 || n > max_query_len || n > hc[i])
+          return fail(PA_ERR_INVALID_ARG, "new tokens of sequence " + std::to_string(i) + " out of range");
+        if (hc[i] < 1 || hc[i] > cap64)
+          return fail(PA_ERR_INVALID_ARG, "context_lens[" + std::to_string(i) + "] out of range");
+        const int nb = (hc[i] + bs - 1) / bs;
+        for (int b = 0; b < nb; ++b) {
+          const int32_t id = ht[static_cast<size_t>(i) * max_blocks_per_seq + b];
+          if (id < 0 || id >= d.num_blocks)
+            return fail(PA_ERR_INVALID_ARG, "block_tables[" + std::to_string(i) + "][" + std::to_string(b) + "] invalid");
+        }
+      }
+    }
+    pa::PrefillParams p{};
+    p.pool = pool->buf;
+    p.layer_off = static_cast<size_t>(layer) * d.num_blocks * d.num_kv_heads * 2 * static_cast<size_t>(bs) * d.head_dim;
+    p.N = d.num_blocks;
+    p.H = d.num_kv_heads;
+    p.bs = bs;
+    p.q = q;
+    p.out = out;
+    p.query_start = query_start;
+    p.num_q_tokens = num_query_tokens;
+    p.max_query_len = max_query_len;
+    p.tables = block_tables;
+    p.max_blocks = max_blocks_per_seq;
+    p.ctx = context_lens;
+    p.S = num_seqs;
+    p.Hq = num_q_heads;
+    p.G = G;
+    p.ctx_cap = static_cast<int>(cap64);
+    p.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
+    hipError_t e = pa::launch_prefill(p, d.dtype, d.head_dim, s);
+    return e == hipSuccess ? PA_OK : hip_fail(e, "prefill launch");
+  });
+}
+
 int pa_copy_blocks(pa_pool* pool, const int32_t* pairs, int n, void* stream) {
   return guarded([&]() -> int {
     if (!pool) return fail(PA_ERR_INVALID_ARG, "pool is NULL");

@@ -36,6 +36,23 @@ struct DecodeParams {
   float* ws_ml;              // [S, Hq, max_parts, 2] (max in log2 units, sum)
 };
 
+struct PrefillParams {
+  const void* pool;            // device pool base
+  size_t layer_off;            // element offset of the layer
+  int32_t N, H, bs;
+  const void* q;               // [num_q_tokens, Hq, D]
+  void* out;                   // [num_q_tokens, Hq, D]
+  const int32_t* query_start;  // [S + 1] offsets of each sequence's new tokens
+  int32_t num_q_tokens;        // rows of q and out
+  int32_t max_query_len;       // bound on new tokens per sequence (sizes the grid)
+  const int32_t* tables;       // [S, max_blocks]
+  int32_t max_blocks;
+  const int32_t* ctx;          // [S] context lengths, new tokens included
+  int32_t S, Hq, G;
+  int32_t ctx_cap;             // min(max_context_len, max_blocks * bs)
+  float scale_log2;            // scale * log2(e)
+};
+
 // Workspace of pa_decode: a small header, the work-item list, and (only when
 // some context spans several partitions) the float32 partition states.
 struct WsLayout {
@@ -63,5 +80,12 @@ hipError_t launch_copy_blocks(const PoolGeom& g, const int32_t* pairs, int n, hi
 hipError_t launch_decode(const DecodeParams& p, int dtype, int D, hipStream_t stream);
 
 bool decode_supported(int dtype, int D, int G);
+
+// Causal prefill of the newest tokens of each sequence (same shape support as
+// decode).  Returns hipErrorInvalidValue when the grid would exceed its limit.
+hipError_t launch_prefill(const PrefillParams& p, int dtype, int D, hipStream_t stream);
+
+// Largest max_query_len a prefill launch accepts for group size G.
+int64_t prefill_max_query_len(int G);
 
 }  // namespace pa

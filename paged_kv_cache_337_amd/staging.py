@@ -138,3 +138,43 @@ def run_shared_script(pool: Pool, w, prefix_kv, private_kv, layers=(0,), device=
             pool.write_kv(layer, kd, vd, sd)
     torch.cuda.synchronize()
     return copies
+
+
+def prefill_inputs(batch, tables=None, device="cuda"):
+    """(q, query_start, block_tables, context_lens) of a prefill batch as
+    device tensors."""
+    tables = batch.block_tables if tables is None else tables
+    return (dev_tensor(batch.q, batch.dtype, device),
+            torch.from_numpy(np.ascontiguousarray(batch.query_start, dtype=np.int32)).to(device),
+            torch.from_numpy(np.ascontiguousarray(tables, dtype=np.int32)).to(device),
+            torch.from_numpy(np.ascontiguousarray(batch.context_lens, dtype=np.int32)).to(device))
+
+
+def run_prefill_script(pool: Pool, batch, layer: int = 0, device="cuda"):
+    """Build a prefill batch in ``pool`` through the library's block manager:
+    per sequence, append the cached tokens and write them, then append the new
+    tokens (one multi-token append each) and write them in one batched write
+    for all sequences.  Returns the host block tables and context lengths."""
+    seqs = []
+    new_k, new_v, new_slots = [], [], []
+    for i in range(batch.num_seqs):
+        K, V = batch.seq_kv(i)
+        c, n = int(batch.context_lens[i]), int(batch.query_lens[i])
+        s = pool.seq_create()
+        seqs.append(s)
+        if c > n:
+            slots, pairs = pool.seq_append(s, c - n)
+            assert not pairs
+            pool.write_kv(layer, dev_tensor(K[:c - n], batch.dtype, device),
+                          dev_tensor(V[:c - n], batch.dtype, device), torch.from_numpy(slots).to(device))
+        slots, pairs = pool.seq_append(s, n)
+        assert not pairs
+        new_k.append(K[c - n:])
+        new_v.append(V[c - n:])
+        new_slots.append(slots)
+    pool.write_kv(layer, dev_tensor(np.concatenate(new_k), batch.dtype, device),
+                  dev_tensor(np.concatenate(new_v), batch.dtype, device),
+                  torch.from_numpy(np.concatenate(new_slots)).to(device))
+    torch.cuda.synchronize()
+    width = max(-(-int(c) // batch.block_size) for c in batch.context_lens)
+    return pool.batch_tables(seqs, width)

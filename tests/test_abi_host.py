@@ -170,3 +170,53 @@ def test_shared_script_tables_match_model():
         assert np.array_equal(t2, tables) and np.array_equal(c2, ctx)
         assert got_copies == copies
         assert pool.state() == tuple(m.state()) or list(pool.state()) == list(m.state())
+
+
+def _call_prefill(pool, layer=0, q=1 << 24, S=2, Hq=8, qstart=1 << 25, T=10, maxq=5,
+                  tables=1 << 26, maxb=4, ctx=1 << 27, maxctx=64, scale=0.125, out=1 << 28):
+    vp = ctypes.c_void_p
+    rc = pa.lib.pa_prefill(pool.handle, layer, vp(q), S, Hq, vp(qstart), T, maxq, vp(tables),
+                           maxb, vp(ctx), maxctx, scale, vp(out), None)
+    return "OK" if rc == 0 else pa.STATUS.get(rc, "?")
+
+
+def test_prefill_argument_checks_need_no_device():
+    """Every rejection happens on the host, before any device work (the
+    placeholder pointers are never touched)."""
+    pool = pa.Pool(2, 16, 16, 2, 64, "bf16", device=None)
+    assert _call_prefill(pool, layer=2) == "INVALID_ARG"
+    assert _call_prefill(pool, layer=-1) == "INVALID_ARG"
+    assert _call_prefill(pool, S=-1) == "INVALID_ARG"
+    assert _call_prefill(pool, S=0) == "OK"       # nothing to do
+    assert _call_prefill(pool, T=0) == "OK"
+    assert _call_prefill(pool, Hq=7) == "INVALID_ARG"
+    assert _call_prefill(pool, Hq=2 * 17) == "UNSUPPORTED"
+    assert _call_prefill(pool, maxq=0) == "INVALID_ARG"
+    assert _call_prefill(pool, maxq=1 << 30) == "UNSUPPORTED"
+    assert _call_prefill(pool, q=0) == "INVALID_ARG"
+    assert _call_prefill(pool, qstart=0) == "INVALID_ARG"
+    assert _call_prefill(pool, out=(1 << 28) + 2) == "INVALID_ARG"
+    assert _call_prefill(pool, maxctx=0) == "INVALID_ARG"
+    assert _call_prefill(pool, scale=float("nan")) == "INVALID_ARG"
+    _call_prefill(pool, maxq=1 << 30)
+    assert "max_query_len" in pa.lib.pa_last_error().decode()
+
+
+def test_decode_argument_checks_need_no_device():
+    pool = pa.Pool(1, 16, 16, 2, 64, "f16", device=None)
+    vp = ctypes.c_void_p
+
+    def call(layer=0, S=2, Hq=4, P=0, ws=1 << 20, wsb=1 << 20, q=1 << 24, scale=0.125):
+        rc = pa.lib.pa_decode(pool.handle, layer, vp(q), S, Hq, vp(1 << 25), 4, vp(1 << 26), 64,
+                              scale, P, vp(ws), wsb, vp(1 << 27), None)
+        return "OK" if rc == 0 else pa.STATUS.get(rc, "?")
+
+    assert call(layer=1) == "INVALID_ARG"
+    assert call(S=0) == "OK"
+    assert call(Hq=3) == "INVALID_ARG"
+    assert call(Hq=2 * 17) == "UNSUPPORTED"
+    assert call(P=24) == "INVALID_ARG"
+    assert call(wsb=16) == "BUFFER_TOO_SMALL"
+    assert call(ws=(1 << 20) + 64) == "INVALID_ARG"
+    assert call(q=(1 << 24) + 8) == "INVALID_ARG"
+    assert call(scale=float("inf")) == "INVALID_ARG"
