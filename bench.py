@@ -1,4 +1,4 @@
-"""Paged decode benchmark on one MI355X.
+"""Paged decode (and prefill) benchmark on one MI355X.
 
 A step is one pass of the decode hot path over one batch: write the batch's
 new-token K/V rows into their cache slots (pa_write_kv), then decode attention
@@ -12,6 +12,10 @@ never finds the previous step's K/V in the 256 MB Infinity Cache.
 
 Prints one JSON line.  value = KV-read GB/s = algorithmic KV bytes of one step
 (valid tokens only: sum(ctx) * 2 * H_kv * D * 2 B) / wall time per step.
+
+`--workload prefill_llama3_8b | chunked_llama3_8b | prefill_tiny` times the
+prefill path instead: a step writes every sequence's new tokens (one batched
+pa_write_kv) and runs pa_prefill over them; value = causal-attention TFLOP/s.
 """
 from __future__ import annotations
 
@@ -36,7 +40,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="llama3_8b",
-                    choices=["tiny", "opt13b", "llama3_8b", "long_ctx", "shared", "shared_cow"])
+                    choices=["tiny", "opt13b", "llama3_8b", "long_ctx", "shared", "shared_cow",
+                             "prefill_tiny", "prefill_llama3_8b", "chunked_llama3_8b"])
     ap.add_argument("--contiguous", action="store_true",
                     help="place every sequence's blocks side by side in logical order (a "
                          "contiguous-cache control for the same kernel)")
@@ -110,11 +115,163 @@ def cpu_baseline(w, budget_s, tables, ctx):
     }
 
 
+def prefill_flops(w) -> int:
+    """Causal attention flops of a prefill batch: per new token and query
+    head, 2*D for q.k and 2*D for p.v per key it attends to."""
+    total = 0
+    for c, n in zip(w.context_lens.astype(np.int64), w.query_lens.astype(np.int64)):
+        keys = n * (c - n) + n * (n + 1) // 2  # sum over new tokens of (position + 1)
+        total += int(keys)
+    return 4 * w.head_dim * w.num_q_heads * total
+
+
+def cpu_baseline_prefill(w, budget_s):
+    """The oracle's causal prefill on the new tokens of the first sequences,
+    one token at a time, until the budget is spent."""
+    from oracle import attention as A
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    qs = w.query_start
+    flops, rows, t_total = 0, 0, 0.0
+    for i in range(w.num_seqs):
+        K, V = (A.to_f64(x, w.dtype) for x in w.seq_kv(i))
+        q = A.to_f64(w.q[qs[i]:qs[i + 1]], w.dtype)
+        c, n = K.shape[0], q.shape[0]
+        for k in range(n):
+            t0 = time.perf_counter()
+            A.prefill_one(q, K, V, w.scale, rows=[k])
+            t_total += time.perf_counter() - t0
+            flops += 4 * w.head_dim * w.num_q_heads * (c - n + k + 1)
+            rows += 1
+            if t_total >= budget_s:
+                break
+        if t_total >= budget_s:
+            break
+    return {
+        "value": round(flops / t_total / 1e12, 6),
+        "unit": "TFLOP/s",
+        "tokens_per_s": round(rows / t_total, 2),
+        "cores": int(threads),
+        "host_cpus": len(os.sched_getaffinity(0)),
+        "kind": "oracle",
+        "sample": f"first {rows} new tokens of the same batch (sequence order), {t_total:.1f} s of oracle time",
+    }
+
+
+PREFILL_METRIC = "paged causal prefill attention TFLOP/s (% of bf16 MFMA peak), Llama-3-8B-shaped GQA"
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3}
+
+
+def main_prefill(args):
+    """A step: one batched pa_write_kv of every sequence's new tokens, then
+    pa_prefill of those tokens over their cached contexts."""
+    import torch
+    import paged_kv_cache_337_amd as pa
+    import workloads as W
+    from paged_kv_cache_337_amd import staging as U
+
+    w = W.PREFILL_WORKLOADS[args.workload]()
+    eb = pa.ELEM_BYTES[w.dtype]
+    L = max(1, args.layers)
+    log(f"[bench] workload={w.name} S={w.num_seqs} context tokens={w.total_tokens} "
+        f"new tokens={int(w.query_lens.sum())} blocks={w.num_blocks} layers={L}")
+    t0 = time.time()
+    pool = U.make_pool(w, layers=L)
+    for layer in range(L):
+        U.fill_pool(pool, w, layer=layer)
+    log(f"[bench] pool filled ({pool.nbytes / 1e9:.2f} GB) in {time.time() - t0:.1f} s")
+    qs_h = w.query_start
+    first = (w.context_lens - w.query_lens).astype(np.int32)
+    slots_new = pa.slots_for_positions(w.block_tables, w.block_size, first, w.query_lens)
+    kn = np.concatenate([w.seq_kv(i)[0][first[i]:] for i in range(w.num_seqs)])
+    vn = np.concatenate([w.seq_kv(i)[1][first[i]:] for i in range(w.num_seqs)])
+    k_new, v_new = U.dev_tensor(kn, w.dtype), U.dev_tensor(vn, w.dtype)
+    slot_new = torch.from_numpy(slots_new).cuda()
+    q, qs, tables, ctx = U.prefill_inputs(w)
+    out = torch.empty_like(q)
+    stream = torch.cuda.current_stream()
+    max_q, max_ctx = w.max_query_len, w.max_context_len
+
+    def step(k, ev=None):
+        layer = k % L
+        pool.write_kv(layer, k_new, v_new, slot_new)
+        if ev is not None:
+            ev[0].record(stream)
+        pool.prefill(layer, q, qs, max_q, tables, ctx, max_ctx, w.scale, out=out)
+        if ev is not None:
+            ev[1].record(stream)
+
+    for k in range(args.warmup):
+        step(k)
+    torch.cuda.synchronize()
+    if not torch.isfinite(out.float()).all():
+        raise RuntimeError("non-finite prefill output")
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for k in range(args.steps):
+        step(args.warmup + k, evs[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    ms_per_step = wall * 1e3 / args.steps
+    pf_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    flops = prefill_flops(w)
+    ntok = int(qs_h[-1])
+    peak = MFMA_PEAK_TFLOPS[w.dtype]
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    achieved = flops / (pf_ms * 1e-3) / 1e12
+    res = {
+        "metric": PREFILL_METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": f"{w.name}: paged causal prefill, {w.num_seqs} seqs, {ntok} new tokens over "
+                        f"{w.total_tokens} context tokens, {w.num_q_heads}q/{w.num_kv_heads}kv heads, "
+                        f"head_dim {w.head_dim}, block_size {w.block_size}",
+            "batch": w.num_seqs, "new_tokens": ntok, "total_context_tokens": w.total_tokens,
+            "max_query_len": max_q, "max_context_len": max_ctx, "layer_slots_rotated": L,
+            "step": "pa_write_kv (all new tokens) + pa_prefill",
+        },
+        "tokens_per_s": round(ntok / (ms_per_step * 1e-3), 1),
+        "flops_per_step": flops,
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "pa_prefill (prefill_kernel)",
+            "achieved": round(achieved, 2),
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4),
+            "traffic": None,
+            "alg_flops_per_launch": flops,
+            "kv_bytes_per_launch": w.total_tokens * 2 * w.num_kv_heads * w.head_dim * eb,
+            "avg_launch_ms": round(pf_ms, 5),
+        },
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_prefill(w, args.cpu_budget_s)
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(json.dumps({"error": "this library runs on a single GPU; use --gpus 1"}))
         sys.exit(2)
+    if args.workload.startswith(("prefill", "chunked")):
+        return main_prefill(args)
 
     import torch
     import paged_kv_cache_337_amd as pa

@@ -72,6 +72,31 @@ __device__ __forceinline__ float from_storage<F32>(uint32_t b) { return __uint_a
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Two floats rounded to nearest even into one 32-bit pair (a in the low
+// half); gfx950 converts both in one instruction.
+template <typename T>
+__device__ __forceinline__ uint32_t pack2(float a, float b);
+template <>
+__device__ __forceinline__ uint32_t pack2<BF16>(float a, float b) {
+  typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+  const b2 v = {static_cast<__bf16>(a), static_cast<__bf16>(b)};
+  return __builtin_bit_cast(uint32_t, v);
+}
+template <>
+__device__ __forceinline__ uint32_t pack2<F16>(float a, float b) {
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  const h2 v = {static_cast<_Float16>(a), static_cast<_Float16>(b)};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// The 16-bit pair (1.0, 1.0).
+template <typename T>
+__device__ __forceinline__ constexpr uint32_t ones2();
+template <>
+__device__ __forceinline__ constexpr uint32_t ones2<BF16>() { return 0x3f803f80u; }
+template <>
+__device__ __forceinline__ constexpr uint32_t ones2<F16>() { return 0x3c003c00u; }
+
 // 16x16x32 (16-bit inputs) and 16x16x16 MFMA on raw bit vectors.
 template <typename T>
 __device__ __forceinline__ f32x4_t mfma_k32(uint4 a, uint4 b, f32x4_t c);

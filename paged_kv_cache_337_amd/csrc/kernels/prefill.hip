@@ -30,6 +30,8 @@
 // Memory safety: lengths and query offsets are clamped to the buffers the
 // caller declared, table reads stay inside the row and block ids outside
 // [0, N) read block 0 and are masked.
+#include <algorithm>
+
 #include "../launch.hpp"
 #include "common.hpp"
 #include "stream.hpp"
@@ -238,22 +240,315 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillParams 
   }
 }
 
+// ---------------------------------------------------------------------------
+// 16-bit pools: K/V staged once per workgroup in LDS.
+//
+// A stage is NP pairs of consecutive units (32 * NP tokens).  Each wave loads
+// its share of the stage's sub-tiles (K or V of one unit, 1 KiB per load
+// instruction, in flight while the previous stage is computed), zeroes tokens past the
+// context and units of invalid blocks, and writes it to one of two LDS
+// buffers; after a barrier every wave reads the stage's fragments.  K keeps
+// the pool's operand layout (A operand of S = K.Q^T, tokens x rows).  V is
+// stored interleaved per pair so that one 16-byte read is, for head_dim tile
+// t and lane (col, grp), the entries d = t*16 + col of tokens 4*grp .. 4*grp+3
+// of the pair's first unit, then of its second: the A operand of
+// O^T += V^T.P^T with v_mfma_f32_16x16x32 over the pair's 32 tokens, whose B
+// operand -- P of row col at those tokens -- is exactly what the lane holds
+// after S = K.Q^T.  The result has query rows along the lanes: a lane owns
+// one row (its softmax reference, its rescale factor, its sum) and four
+// consecutive head_dim entries per tile, stored with 8-byte writes.
+//
+// The softmax work per score is a max, one FMA (scale and reference folded),
+// one exp2 and half a packed convert: stages that lie wholly below every row's
+// position and inside the context take no mask, and the row sums come from
+// one more MFMA of P against ones.
+// ---------------------------------------------------------------------------
+template <int D, int NP>
+struct PrefillLds {
+  static constexpr int NCH = D / 32;
+  static constexpr int NT = D / 16;
+  uint4 k[2][2 * NP][NCH][64];  // [buffer][unit][chunk][lane]
+  uint2 v[2][NP][NT][64][2];    // [buffer][pair][head_dim tile][lane][unit of the pair]
+};
+
+// Zero the 16-bit entries of tokens >= valid in a V chunk: lane group grp
+// holds tokens 4*grp .. 4*grp+3 (two per 32-bit word), for two head_dim tiles.
+__device__ __forceinline__ uint4 zero_v_tail(uint4 x, int grp, int valid) {
+  const int t0 = 4 * grp;
+  const uint32_t m01 = (t0 + 0 < valid ? 0x0000ffffu : 0u) | (t0 + 1 < valid ? 0xffff0000u : 0u);
+  const uint32_t m23 = (t0 + 2 < valid ? 0x0000ffffu : 0u) | (t0 + 3 < valid ? 0xffff0000u : 0u);
+  return make_uint4(x.x & m01, x.y & m23, x.z & m01, x.w & m23);
+}
+
+template <typename T, int D, int NW, int NB, int NP>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4))) void prefill_lds_kernel(
+    PrefillParams p) {
+  static_assert(T::kBytes == 2, "16-bit pools only");
+  constexpr int NCH = D / 32;  // 1 KiB chunks per sub-tile
+  constexpr int NT = D / 16;
+  constexpr int kUnits = 2 * NP;         // units per stage
+  constexpr int kKeys = 16 * kUnits;     // keys per stage
+  constexpr int kRowsWave = 16 * NB;
+  constexpr int kRowsWG = kRowsWave * NW;
+  constexpr int kLoads = 2 * kUnits * NCH / NW;  // chunk loads per wave per stage
+  static_assert(kLoads >= 1 && kLoads <= NCH && NCH % kLoads == 0 && (2 * kUnits * NCH) % NW == 0,
+                "each wave loads a part of one sub-tile");
+  using B = typename T::bits;
+  __shared__ PrefillLds<D, NP> sm;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = rfl(threadIdx.x >> 6);
+  const int i = blockIdx.x / p.H;
+  const int h = blockIdx.x - i * p.H;
+  const int G = p.G;
+  const int qs = clampi(p.query_start[i], 0, p.num_q_tokens);
+  const int qe = clampi(p.query_start[i + 1], qs, p.num_q_tokens);
+  const int c = clampi(p.ctx[i], 0, p.ctx_cap);
+  int n = qe - qs;
+  n = n < p.max_query_len ? n : p.max_query_len;
+  n = n < c ? n : c;
+  const int rows = rfl(n * G);
+  const int ntiles = (rows + kRowsWG - 1) / kRowsWG;
+  const int tile = ntiles - 1 - static_cast<int>(blockIdx.y);
+  if (tile < 0) return;  // whole workgroup
+  const int first_pos = c - n;
+  const int wg_last_row = (tile * kRowsWG + kRowsWG < rows ? tile * kRowsWG + kRowsWG : rows) - 1;
+  const int nst = (first_pos + wg_last_row / G + kKeys) / kKeys;  // stages covering the workgroup's keys
+  const int r0 = tile * kRowsWG + wave * kRowsWave;
+  const bool active = r0 < rows;
+  const int last_row = (r0 + kRowsWave < rows ? r0 + kRowsWave : rows) - 1;
+  const int kmax = active ? first_pos + last_row / G : -1;  // last key this wave attends to
+
+  const int col = lane & 15, grp = lane >> 4;
+  uint4 qb[NB][NCH];
+  f32x4_t acc[NB][NT];  // O^T: head_dim t*16 + 4*grp + r of row col
+  f32x4_t lsum[NB];     // the row's sum (every entry)
+  float m_ref[NB];      // reference max of the row, log2 units
+  int qpos[NB];         // position of the lane's row (-1: padding row)
+  int qmin[NB];         // position of the tile's first row (wave-uniform)
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    const int row = r0 + 16 * b + col;
+    const bool valid = row < rows;
+    const int k = row / G, g = row - (row / G) * G;
+    qpos[b] = valid ? first_pos + k : -1;
+    qmin[b] = first_pos + (r0 + 16 * b) / G;
+    const char* qbase = static_cast<const char*>(p.q) +
+                        ((static_cast<size_t>(qs) + (valid ? k : 0)) * p.Hq + static_cast<size_t>(h) * G + g) * D * 2;
+#pragma unroll
+    for (int cc = 0; cc < NCH; ++cc)
+      qb[b][cc] = valid ? *reinterpret_cast<const uint4*>(qbase + (cc * 4 + grp) * 16) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[b][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    lsum[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    m_ref[b] = kNegInfP;
+  }
+
+  // Load assignment: sub-tile `sub` (unit sub >> 1, K or V by sub & 1),
+  // chunks [c0, c0 + kLoads).
+  const int sub = (wave * kLoads) / NCH;
+  const int unit = sub >> 1;
+  const bool is_v = sub & 1;
+  const int c0 = (wave * kLoads) % NCH;
+  const int32_t* trow = p.tables + static_cast<size_t>(i) * p.max_blocks;
+  UnitStream<D, 2> us;
+  us.begin(p, trow, 0, 0, h);
+  us.ids = us.fetch_ids(lane);
+  uint4 stg[kLoads];  // this wave's loads of the next stage
+  int valid_st;       // tokens of this wave's unit to keep (0 for an invalid block)
+
+  // Locate stage s's units and issue this wave's loads.
+  auto issue = [&](int s, uint4 (&r)[kLoads], int& valid) {
+    if (us.lb - us.lb_base + kUnits > 64) {
+      us.lb_base = us.lb;
+      us.ids = us.fetch_ids(lane);
+    }
+    const char* src = nullptr;
+    bool ok = false;
+#pragma unroll
+    for (int u = 0; u < kUnits; ++u) {
+      const char *kp, *vp;
+      const bool okk = us.locate(kp, vp);
+      if (u == unit) {
+        src = is_v ? vp : kp;
+        ok = okk;
+      }
+    }
+    const uint4* sp = reinterpret_cast<const uint4*>(src) + lane;
+#pragma unroll
+    for (int j = 0; j < kLoads; ++j) r[j] = sp[64 * (c0 + j)];
+    const int left = c - s * kKeys - unit * 16;
+    valid = !ok ? 0 : (left < 0 ? 0 : (left < 16 ? left : 16));
+  };
+  auto to_lds = [&](uint4 (&r)[kLoads], int valid, int buf) {
+    if (valid < 16) {  // wave-uniform: the context's last unit, or an invalid block
+      if (is_v) {
+#pragma unroll
+        for (int j = 0; j < kLoads; ++j) r[j] = zero_v_tail(r[j], grp, valid);
+      } else {
+#pragma unroll
+        for (int j = 0; j < kLoads; ++j)
+          if (col >= valid) r[j] = make_uint4(0, 0, 0, 0);
+      }
+    }
+    if (is_v) {
+#pragma unroll
+      for (int j = 0; j < kLoads; ++j) {
+        sm.v[buf][unit >> 1][2 * (c0 + j)][lane][unit & 1] = make_uint2(r[j].x, r[j].y);
+        sm.v[buf][unit >> 1][2 * (c0 + j) + 1][lane][unit & 1] = make_uint2(r[j].z, r[j].w);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < kLoads; ++j) sm.k[buf][unit][c0 + j][lane] = r[j];
+    }
+  };
+
+  const float sl2 = p.scale_log2;
+  const uint4 ones = make_uint4(ones2<T>(), ones2<T>(), ones2<T>(), ones2<T>());
+  // One stage from LDS buffer `buf`: keys key0 .. key0 + kKeys - 1.  The
+  // masked form is needed only where the stage reaches past some row's
+  // position (the causal diagonal and the context's end).
+  auto compute = [&](int buf, int key0, bool masked) {
+    f32x4_t sc[NB][kUnits];  // scores: token key0 + 16*u + 4*grp + r of row col
+#pragma unroll
+    for (int u = 0; u < kUnits; ++u) {
+      uint4 kf[NCH];
+#pragma unroll
+      for (int cc = 0; cc < NCH; ++cc) kf[cc] = sm.k[buf][u][cc][lane];
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        sc[b][u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int cc = 0; cc < NCH; ++cc) sc[b][u] = mfma_k32<T>(kf[cc], qb[b][cc], sc[b][u]);
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      // Keys past the context were zeroed by the loader; they and the keys
+      // beyond a row's position are masked where some row of the tile can
+      // see them.
+      if (masked && key0 + kKeys - 1 > qmin[b]) {
+        asm volatile("");  // keep the branch: most stages skip it
+        const int lim = qpos[b] - key0 - 4 * grp;
+#pragma unroll
+        for (int u = 0; u < kUnits; ++u)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) sc[b][u][r] = 16 * u + r <= lim ? sc[b][u][r] : kNegInfP;
+      }
+      float mraw = kNegInfP;
+#pragma unroll
+      for (int u = 0; u < kUnits; ++u)
+        mraw = fmaxf(mraw, fmaxf(fmaxf(sc[b][u][0], sc[b][u][1]), fmaxf(sc[b][u][2], sc[b][u][3])));
+      const float mloc = mraw * sl2;  // this lane's share of the row
+      if (wave_any(mloc > m_ref[b] + kRescaleLog2P)) {
+        // The row's maximum over its four lane groups, so that the row keeps
+        // one reference.
+        float mx = fmaxf(mloc, __shfl_xor(mloc, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float m_new = fmaxf(m_ref[b], mx);
+        const float alpha = m_new == kNegInfP ? 1.f : fast_exp2(m_ref[b] - m_new);
+        m_ref[b] = m_new;
+        lsum[b] *= alpha;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) acc[b][t] *= alpha;
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < NP; ++q) {
+      uint4 vv[NT];
+#pragma unroll
+      for (int t = 0; t < NT; ++t) vv[t] = *reinterpret_cast<const uint4*>(&sm.v[buf][q][t][lane][0]);
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const float nm = m_ref[b] == kNegInfP ? 0.f : -m_ref[b];
+        float e[8];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          e[r] = fast_exp2(fmaf(sc[b][2 * q][r], sl2, nm));
+          e[4 + r] = fast_exp2(fmaf(sc[b][2 * q + 1][r], sl2, nm));
+        }
+        const uint4 pb = make_uint4(pack2<T>(e[0], e[1]), pack2<T>(e[2], e[3]), pack2<T>(e[4], e[5]),
+                                    pack2<T>(e[6], e[7]));
+#pragma unroll
+        for (int t = 0; t < NT; ++t) acc[b][t] = mfma_k32<T>(vv[t], pb, acc[b][t]);
+        lsum[b] = mfma_k32<T>(ones, pb, lsum[b]);
+      }
+    }
+  };
+
+  // Pipeline: the loads of stage s + 1 are in flight in registers while
+  // stage s is computed from LDS; they are written to the other buffer after
+  // it, and one barrier per stage publishes them.
+  issue(0, stg, valid_st);
+  to_lds(stg, valid_st, 0);
+  __syncthreads();
+  // Stages below this wave's first row need no mask.
+  const int kfull = active ? qmin[0] - kKeys + 1 : -1;
+  for (int s = 0; s < nst; ++s) {
+    if (s + 1 < nst) issue(s + 1, stg, valid_st);
+    const int key0 = s * kKeys;
+    if (key0 <= kmax) compute(s & 1, key0, key0 > kfull);
+    if (s + 1 < nst) to_lds(stg, valid_st, (s + 1) & 1);
+    __syncthreads();
+  }
+
+  if (!active) return;
+  // Row col of tile b: head_dim entries t*16 + 4*grp .. +3, 8 bytes per store.
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    const int row = r0 + 16 * b + col;
+    if (row < rows) {
+      const float L = lsum[b][0];
+      const float inv = L > 0.f ? 1.f / L : 0.f;
+      const int k = row / G, g = row - (row / G) * G;
+      B* orow = static_cast<B*>(p.out) + ((static_cast<size_t>(qs) + k) * p.Hq + static_cast<size_t>(h) * G + g) * D;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const uint2 w = make_uint2(pack2<T>(acc[b][t][0] * inv, acc[b][t][1] * inv),
+                                   pack2<T>(acc[b][t][2] * inv, acc[b][t][3] * inv));
+        *reinterpret_cast<uint2*>(orow + t * 16 + 4 * grp) = w;
+      }
+    }
+  }
+}
+
+#ifndef PA_PREFILL_LDS_WAVES
+#define PA_PREFILL_LDS_WAVES 8
+#endif
+#ifndef PA_PREFILL_LDS_TILES
+#define PA_PREFILL_LDS_TILES 2
+#endif
+#ifndef PA_PREFILL_LDS_PAIRS
+#define PA_PREFILL_LDS_PAIRS 2
+#endif
+constexpr int kLdsWaves = PA_PREFILL_LDS_WAVES;
+constexpr int kLdsTiles = PA_PREFILL_LDS_TILES;
+constexpr int kLdsPairs = PA_PREFILL_LDS_PAIRS;
+
 template <typename T, int D>
 hipError_t launch_prefill_typed(const PrefillParams& p, hipStream_t stream) {
-  constexpr int kRowsWG = 16 * kTilesPerWave * kPrefillWaves;
+  constexpr bool kLds = T::kBytes == 2;
+  constexpr int kRowsWG = kLds ? 16 * kLdsTiles * kLdsWaves : 16 * kTilesPerWave * kPrefillWaves;
   const int64_t tiles = (static_cast<int64_t>(p.max_query_len) * p.G + kRowsWG - 1) / kRowsWG;
   if (tiles <= 0) return hipSuccess;
   if (tiles > 65535) return hipErrorInvalidValue;
   const dim3 grid(static_cast<unsigned>(p.S) * p.H, static_cast<unsigned>(tiles));
-  hipLaunchKernelGGL((prefill_kernel<T, D, kTilesPerWave, kPrefillPrefetch>), grid, dim3(kPrefillThreads), 0,
-                     stream, p);
+  if constexpr (kLds) {
+    hipLaunchKernelGGL((prefill_lds_kernel<T, D, kLdsWaves, kLdsTiles, kLdsPairs>), grid,
+                       dim3(64 * kLdsWaves), 0, stream, p);
+  } else {
+    hipLaunchKernelGGL((prefill_kernel<T, D, kTilesPerWave, kPrefillPrefetch>), grid, dim3(kPrefillThreads), 0,
+                       stream, p);
+  }
   return hipGetLastError();
 }
 
 }  // namespace
 
 int64_t prefill_max_query_len(int G) {
-  return static_cast<int64_t>(65535) * (16 * kTilesPerWave * kPrefillWaves) / (G > 0 ? G : 1);
+  // The smaller row tile of the two kernels bounds the grid's y extent.
+  const int64_t rows_wg = std::min(16 * kLdsTiles * kLdsWaves, 16 * kTilesPerWave * kPrefillWaves);
+  return static_cast<int64_t>(65535) * rows_wg / (G > 0 ? G : 1);
 }
 
 hipError_t launch_prefill(const PrefillParams& p, int dtype, int D, hipStream_t stream) {
