@@ -298,8 +298,18 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
 
   const int lane = threadIdx.x & 63;
   const int wave = rfl(threadIdx.x >> 6);
-  const int i = blockIdx.x / p.H;
-  const int h = blockIdx.x - i * p.H;
+  // Workgroup -> (sequence, kv head, row tile).  Consecutive workgroups go to
+  // the eight XCDs in turn; XCD x runs the (sequence, kv head) pairs
+  // x, x + 8, x + 16, ... one after the other, each pair's row tiles
+  // back to back and the last (heaviest) first, so the workgroups that run at
+  // the same time on an XCD read the same K/V through its L2.
+  const int xcd = blockIdx.x & 7;
+  const int slot = blockIdx.x >> 3;
+  const int pair = (slot / p.tiles) * 8 + xcd;
+  const int y = slot - (slot / p.tiles) * p.tiles;
+  if (pair >= p.S * p.H) return;  // whole workgroup
+  const int i = pair / p.H;
+  const int h = pair - i * p.H;
   const int G = p.G;
   const int qs = clampi(p.query_start[i], 0, p.num_q_tokens);
   const int qe = clampi(p.query_start[i + 1], qs, p.num_q_tokens);
@@ -309,7 +319,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
   n = n < c ? n : c;
   const int rows = rfl(n * G);
   const int ntiles = (rows + kRowsWG - 1) / kRowsWG;
-  const int tile = ntiles - 1 - static_cast<int>(blockIdx.y);
+  const int tile = ntiles - 1 - y;
   if (tile < 0) return;  // whole workgroup
   const int first_pos = c - n;
   const int wg_last_row = (tile * kRowsWG + kRowsWG < rows ? tile * kRowsWG + kRowsWG : rows) - 1;
@@ -357,22 +367,25 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
   uint4 stg[kLoads];  // this wave's loads of the next stage
   int valid_st;       // tokens of this wave's unit to keep (0 for an invalid block)
 
-  // Locate stage s's units and issue this wave's loads.
+  // This wave's unit of the next stage: logical block and 16-token sub-tile.
+  const int subs = p.bs >> 4;  // sub-tiles per block
+  int my_lb = unit / subs, my_sub = unit - (unit / subs) * subs;
+  // Locate this wave's unit of stage s (stages are issued in order) and
+  // issue its loads.
   auto issue = [&](int s, uint4 (&r)[kLoads], int& valid) {
-    if (us.lb - us.lb_base + kUnits > 64) {
-      us.lb_base = us.lb;
+    if (my_lb - us.lb_base >= 64) {
+      us.lb_base = my_lb;
       us.ids = us.fetch_ids(lane);
     }
-    const char* src = nullptr;
-    bool ok = false;
-#pragma unroll
-    for (int u = 0; u < kUnits; ++u) {
-      const char *kp, *vp;
-      const bool okk = us.locate(kp, vp);
-      if (u == unit) {
-        src = is_v ? vp : kp;
-        ok = okk;
-      }
+    us.lb = my_lb;
+    us.sub = my_sub;
+    const char *kp, *vp;
+    const bool ok = us.locate(kp, vp);
+    const char* src = is_v ? vp : kp;
+    my_sub += kUnits;
+    while (my_sub >= subs) {
+      my_sub -= subs;
+      ++my_lb;
     }
     const uint4* sp = reinterpret_cast<const uint4*>(src) + lane;
 #pragma unroll
@@ -534,8 +547,14 @@ hipError_t launch_prefill_typed(const PrefillParams& p, hipStream_t stream) {
   if (tiles > 65535) return hipErrorInvalidValue;
   const dim3 grid(static_cast<unsigned>(p.S) * p.H, static_cast<unsigned>(tiles));
   if constexpr (kLds) {
-    hipLaunchKernelGGL((prefill_lds_kernel<T, D, kLdsWaves, kLdsTiles, kLdsPairs>), grid,
-                       dim3(64 * kLdsWaves), 0, stream, p);
+    // One dimension: eight XCD lanes of ceil(S * H / 8) pairs x tiles slots.
+    PrefillParams q = p;
+    q.tiles = static_cast<int32_t>(tiles);
+    const int64_t pairs8 = (static_cast<int64_t>(p.S) * p.H + 7) / 8;
+    const int64_t wgs = 8 * pairs8 * tiles;
+    if (wgs > INT32_MAX) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((prefill_lds_kernel<T, D, kLdsWaves, kLdsTiles, kLdsPairs>), dim3(static_cast<unsigned>(wgs)),
+                       dim3(64 * kLdsWaves), 0, stream, q);
   } else {
     hipLaunchKernelGGL((prefill_kernel<T, D, kTilesPerWave, kPrefillPrefetch>), grid, dim3(kPrefillThreads), 0,
                        stream, p);
