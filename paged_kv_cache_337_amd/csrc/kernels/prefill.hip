@@ -10,22 +10,21 @@
 // length T_i whose last n_i tokens are new: new token k sits at position
 // T_i - n_i + k and attends to positions 0 .. T_i - n_i + k.
 //
-// Work split.  The query rows of one (sequence, kv head) are the pairs
-// (new token k, query head g of the group), row = k * G + g, so the 16
-// columns of an MFMA tile are always full whatever the group size.  A wave
-// owns NB tiles of 16 rows and streams the K/V units (16 tokens of one block)
-// from position 0 up to the last position its rows attend to; it keeps
-// NB independent online-softmax states and never exchanges data with the
-// other waves.  A workgroup is four such waves on consecutive rows; the grid
-// is (sequence x kv head, row tile) with the heaviest (last) row tiles of
-// every sequence dispatched first.
+// Query rows.  The rows of one (sequence, kv head) are the pairs (new token
+// k, query head g of the group), row = k * G + g, so the 16 columns of an
+// MFMA tile are full whatever the group size; a wave owns NB such tiles and
+// keeps one online softmax per row (reference raised lazily, only when a
+// score passes it by 2^8).  Scores are S = K.Q^T with
+// v_mfma_f32_16x16x32_{bf16,f16} (tokens x rows, head_dim reduced).
 //
-// Per unit and tile: S = K.Q^T with v_mfma_f32_16x16x32_{bf16,f16} (tokens x
-// rows, head_dim reduced; v_mfma_f32_16x16x4_f32 for float32 pools), the
-// causal mask per row by select, the online softmax with a lazily raised
-// reference (rescale only when a score passes the reference by 2^8), then
-// O += P.V with v_mfma_f32_16x16x16 (rows x head_dim, tokens reduced).  The K
-// and V fragments of a unit are loaded once and used for all NB tiles.
+// Two kernels:
+//   * 16-bit pools (prefill_lds_kernel): a workgroup of eight waves stages
+//     each 64-token stage of K/V in LDS once, with the next stage's loads in
+//     flight, and reduces P.V as O^T = V^T.P^T with v_mfma_f32_16x16x32 over
+//     32-token pairs; workgroups are ordered so that one XCD runs all row
+//     tiles of a (sequence, kv head) pair back to back (they share its L2).
+//   * float32 pools (prefill_kernel): each wave streams its own K/V units from
+//     the pool (v_mfma_f32_16x16x4_f32), with O += P.V per 16-token unit.
 //
 // Memory safety: lengths and query offsets are clamped to the buffers the
 // caller declared, table reads stay inside the row and block ids outside
