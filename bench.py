@@ -61,19 +61,27 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def counter_traffic(workload: str):
-    """HBM bytes per pa_decode call from the committed rocprofv3 counter record
-    of this workload (FETCH_SIZE + WRITE_SIZE, scaled by a copy of known size),
-    or None when the decode kernel source changed since it was taken."""
+def sources_sha256(paths) -> str:
+    """SHA-256 over the listed source files, in order."""
     import hashlib
-    rec = os.path.join(ROOT, "profiles", "decode_llama3_8b_b256.traffic.json")
+    h = hashlib.sha256()
+    for rel in paths:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def counter_traffic(record: str, workload: str):
+    """HBM bytes per call from a committed rocprofv3 counter record
+    (profiles/<record>.traffic.json: FETCH_SIZE + WRITE_SIZE, scaled by a copy
+    of known size), or None when the record is for another workload or any of
+    the kernel's sources changed since it was taken."""
+    rec = os.path.join(ROOT, "profiles", record + ".traffic.json")
     if not os.path.exists(rec):
         return None
     with open(rec) as f:
         r = json.load(f)
-    with open(os.path.join(ROOT, r["kernel_source"]), "rb") as f:
-        sha = hashlib.sha256(f.read()).hexdigest()
-    if r.get("workload") != workload or r.get("source_sha256") != sha:
+    if r.get("workload") != workload or r.get("sources_sha256") != sources_sha256(r["kernel_sources"]):
         return None
     return int(r["traffic_bytes_per_call"])
 
@@ -254,7 +262,8 @@ def main_prefill(args):
             "peak": peak,
             "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4),
-            "traffic": None,
+            "traffic": counter_traffic("prefill_llama3_8b", w.name) if L == 4 else None,
+            "traffic_unit": "bytes per launch (HBM)",
             "alg_flops_per_launch": flops,
             "kv_bytes_per_launch": w.total_tokens * 2 * w.num_kv_heads * w.head_dim * eb,
             "avg_launch_ms": round(pf_ms, 5),
@@ -396,7 +405,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": (counter_traffic(w.name)
+            "traffic": (counter_traffic("decode_llama3_8b_b256", w.name)
                         if P == w.partition_tokens and L == 4 and not args.contiguous else None),
             "alg_bytes_per_launch": alg_bytes,
             "avg_launch_ms": round(dec_ms, 5),

@@ -5,56 +5,90 @@
 // what a paged implementation must do; "PagedAttention: paging the KV cache like
 // an OS pages memory", "How it works", copies a shared block when it must be
 // modified.  The element placement follows the pool layout documented in pa.h.
+#include <type_traits>
+
 #include "../launch.hpp"
 #include "common.hpp"
 
 namespace pa {
 
-// One thread per (token, kv head, 16-byte chunk of the row).  The K chunk is a
-// single 16-byte store (E consecutive d stay consecutive in a K sub-tile);
-// the V elements of one token are 4 elements apart (token-inner order), so
-// they are stored one by one.
+// One wave per (group of four consecutive input tokens, kv head).
+//
+// K: a token's row is D / E chunks of 16 bytes, each one 16-byte store (E
+// consecutive d stay consecutive in a K sub-tile).
+// V: the sub-tile keeps four tokens side by side (token-inner order), so one
+// 16-byte chunk holds tokens 4m .. 4m+3 of R = E / 4 head_dim tiles at one
+// d % 16.  When the group's four slots are consecutive and start at a
+// multiple of four (the tokens of a prompt chunk), the wave assembles whole
+// chunks and stores 16 bytes at a time; otherwise (for example one new token
+// per sequence in decode) each token's V elements are stored one by one.
 template <int kBytes>
-__global__ __launch_bounds__(256) void write_kv_kernel(const uint4* __restrict__ k,
-                                                       const uint4* __restrict__ v,
-                                                       const int32_t* __restrict__ slots,
-                                                       int num_tokens, char* __restrict__ layer_base,
-                                                       int N, int H, int bs, int D) {
+__global__ __launch_bounds__(64) void write_kv_kernel(const uint4* __restrict__ k, const uint4* __restrict__ v,
+                                                      const int32_t* __restrict__ slots, int num_tokens,
+                                                      char* __restrict__ layer_base, int N, int H, int bs, int D) {
+  using Bits = typename std::conditional<kBytes == 4, uint32_t, uint16_t>::type;
   constexpr int E = 16 / kBytes;
   constexpr int R = E / 4;
   const int cpr = D / E;  // 16-byte chunks per (token, head) row
-  const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  const int64_t total = static_cast<int64_t>(num_tokens) * H * cpr;
-  if (gid >= total) return;
-  const int tok = static_cast<int>(gid / (H * cpr));
-  const int rem = static_cast<int>(gid % (H * cpr));
-  const int h = rem / cpr, c = rem % cpr;
-  const int32_t slot = slots[tok];
-  if (slot < 0) return;
-  const int32_t b = slot / bs;
-  if (b >= N) return;
-  const int t = slot % bs, sub = t / 16, r = t % 16;
-
-  const size_t region = (static_cast<size_t>(b) * H + h) * (2 * static_cast<size_t>(bs) * D);
-  const size_t kbase = region + static_cast<size_t>(sub) * 16 * D;
-  const size_t vbase = region + static_cast<size_t>(bs) * D + static_cast<size_t>(sub) * 16 * D;
-  const int d0 = c * E;
-  const int k_off = ((d0 / (4 * E)) * 64 + r + 16 * ((d0 % (4 * E)) / E)) * E;
-  const uint4 kv = k[gid];
-  const uint4 vv = v[gid];
-  *reinterpret_cast<uint4*>(layer_base + (kbase + k_off) * kBytes) = kv;
-
-  const uint32_t w[4] = {vv.x, vv.y, vv.z, vv.w};
+  const int lane = threadIdx.x;
+  const int t0 = blockIdx.x * 4;
+  const int h = blockIdx.y;
+  const int ntok = num_tokens - t0 < 4 ? num_tokens - t0 : 4;
+  int32_t sl[4];
 #pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const int d = d0 + e;
-    const int nd = d / 16;
-    const int v_off = (((nd / R) * 64 + d % 16 + 16 * (r / 4)) * R + nd % R) * 4 + r % 4;
-    char* dst = layer_base + (vbase + v_off) * kBytes;
-    if constexpr (kBytes == 4) {
-      *reinterpret_cast<uint32_t*>(dst) = w[e];
-    } else {
-      *reinterpret_cast<uint16_t*>(dst) = static_cast<uint16_t>(w[e / 2] >> (16 * (e % 2)));
+  for (int q = 0; q < 4; ++q) sl[q] = q < ntok ? slots[t0 + q] : -1;
+  const int32_t s0 = sl[0];
+  const bool group = ntok == 4 && s0 >= 0 && (s0 & 3) == 0 && sl[1] == s0 + 1 && sl[2] == s0 + 2 &&
+                     sl[3] == s0 + 3 && s0 / bs < N;
+
+  // K rows: one 16-byte store per chunk.
+  for (int x = lane; x < 4 * cpr; x += 64) {
+    const int q = x / cpr, c = x - (x / cpr) * cpr;
+    const int32_t slot = sl[q];
+    if (slot < 0 || slot / bs >= N) continue;
+    const int32_t b = slot / bs;
+    const int t = slot - b * bs, sub = t / 16, r = t % 16;
+    const size_t region = (static_cast<size_t>(b) * H + h) * (2 * static_cast<size_t>(bs) * D);
+    const int d0 = c * E;
+    const int k_off = ((d0 / (4 * E)) * 64 + r + 16 * ((d0 % (4 * E)) / E)) * E;
+    const size_t row = (static_cast<size_t>(t0 + q) * H + h) * cpr + c;
+    *reinterpret_cast<uint4*>(layer_base + (region + static_cast<size_t>(sub) * 16 * D + k_off) * kBytes) = k[row];
+  }
+
+  const Bits* vin = reinterpret_cast<const Bits*>(v);
+  if (group) {
+    // Chunk (P, j) of the group's token quad: head_dim tiles P*R .. P*R+R-1
+    // at d % 16 = j, four tokens each.
+    const int32_t b = s0 / bs;
+    const int t = s0 - b * bs, sub = t / 16, m = (t % 16) / 4;
+    const size_t vbase = (static_cast<size_t>(b) * H + h) * (2 * static_cast<size_t>(bs) * D) +
+                         static_cast<size_t>(bs) * D + static_cast<size_t>(sub) * 16 * D;
+    for (int x = lane; x < D / R; x += 64) {
+      const int P = x / 16, j = x % 16;
+      Bits e[E];
+#pragma unroll
+      for (int mm = 0; mm < R; ++mm)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          e[mm * 4 + q] = vin[(static_cast<size_t>(t0 + q) * H + h) * D + (P * R + mm) * 16 + j];
+      const size_t off = vbase + static_cast<size_t>((P * 64 + j + 16 * m) * E);
+      uint4 w;
+      __builtin_memcpy(&w, e, sizeof(w));
+      *reinterpret_cast<uint4*>(layer_base + off * kBytes) = w;
+    }
+  } else {
+    for (int x = lane; x < 4 * D; x += 64) {
+      const int q = x / D, d = x - (x / D) * D;
+      const int32_t slot = sl[q];
+      if (slot < 0 || slot / bs >= N) continue;
+      const int32_t b = slot / bs;
+      const int t = slot - b * bs, sub = t / 16, r = t % 16;
+      const size_t vbase = (static_cast<size_t>(b) * H + h) * (2 * static_cast<size_t>(bs) * D) +
+                           static_cast<size_t>(bs) * D + static_cast<size_t>(sub) * 16 * D;
+      const int nd = d / 16;
+      const int v_off = (((nd / R) * 64 + d % 16 + 16 * (r / 4)) * R + nd % R) * 4 + r % 4;
+      *reinterpret_cast<Bits*>(layer_base + (vbase + v_off) * kBytes) =
+          vin[(static_cast<size_t>(t0 + q) * H + h) * D + d];
     }
   }
 }
@@ -62,19 +96,15 @@ __global__ __launch_bounds__(256) void write_kv_kernel(const uint4* __restrict__
 hipError_t launch_write_kv(const PoolGeom& g, int layer, const void* k, const void* v,
                            const int32_t* slots, int num_tokens, hipStream_t stream) {
   if (num_tokens <= 0) return hipSuccess;
-  const int E = 16 / g.elem_bytes;
-  const int64_t total = static_cast<int64_t>(num_tokens) * g.H * (g.D / E);
-  const int threads = 256;
-  const int64_t blocks = (total + threads - 1) / threads;
+  if (g.H > 65535) return hipErrorInvalidValue;
+  const dim3 grid(static_cast<unsigned>((num_tokens + 3) / 4), static_cast<unsigned>(g.H));
   char* base = static_cast<char*>(g.base) + static_cast<size_t>(layer) * g.layer_elems() * g.elem_bytes;
   if (g.elem_bytes == 4) {
-    hipLaunchKernelGGL(write_kv_kernel<4>, dim3(static_cast<unsigned>(blocks)), dim3(threads), 0,
-                       stream, static_cast<const uint4*>(k), static_cast<const uint4*>(v), slots,
-                       num_tokens, base, g.N, g.H, g.bs, g.D);
+    hipLaunchKernelGGL(write_kv_kernel<4>, grid, dim3(64), 0, stream, static_cast<const uint4*>(k),
+                       static_cast<const uint4*>(v), slots, num_tokens, base, g.N, g.H, g.bs, g.D);
   } else {
-    hipLaunchKernelGGL(write_kv_kernel<2>, dim3(static_cast<unsigned>(blocks)), dim3(threads), 0,
-                       stream, static_cast<const uint4*>(k), static_cast<const uint4*>(v), slots,
-                       num_tokens, base, g.N, g.H, g.bs, g.D);
+    hipLaunchKernelGGL(write_kv_kernel<2>, grid, dim3(64), 0, stream, static_cast<const uint4*>(k),
+                       static_cast<const uint4*>(v), slots, num_tokens, base, g.N, g.H, g.bs, g.D);
   }
   return hipGetLastError();
 }

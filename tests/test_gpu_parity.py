@@ -47,6 +47,56 @@ SMALL = {
 }
 
 
+def _write_slots(N, bs, rng):
+    """Slots for a write exercising every path: an aligned run of consecutive
+    slots (whole four-token groups), a run starting one past a multiple of
+    four, a run holding a skipped token (-1), an out-of-range slot, scattered
+    single slots, and a count that leaves a partial last group."""
+    free = rng.permutation(N)
+    slots = []
+    b0, b1, b2 = (int(x) for x in free[:3])
+    slots += list(range(b0 * bs, b0 * bs + bs))                 # aligned, whole block
+    slots += list(range(b1 * bs + 1, b1 * bs + 1 + 11))        # starts at offset 1
+    run = list(range(b2 * bs, b2 * bs + 8))
+    run[5] = -1                                                # a skipped token
+    slots += run
+    slots.append(N * bs + 3)                                   # beyond the pool: skipped
+    rest = rng.permutation(np.arange(free[3] * bs, free[3] * bs + bs))[:7]
+    slots += [int(x) for x in rest]                            # scattered
+    return np.array(slots, dtype=np.int32)
+
+
+@pytest.mark.parametrize("dtype,D,bs", [("bf16", 128, 16), ("f16", 64, 32), ("f32", 128, 16), ("f32", 64, 48),
+                                        ("bf16", 64, 48)])
+def test_write_kv_every_path_bit_exact(dtype, D, bs):
+    import paged_kv_cache_337_amd as pa
+    from oracle import layout as LY
+    rng = np.random.default_rng(7)
+    N, H = 6, 3
+    slots = _write_slots(N, bs, rng)
+    T = len(slots)
+    assert T % 4 != 0
+    k = W.round_to_storage(rng.standard_normal((T, H, D), dtype=np.float32), dtype)
+    v = W.round_to_storage(rng.standard_normal((T, H, D), dtype=np.float32), dtype)
+    U.log(f"[write_kv paths] {dtype} D={D} bs={bs} T={T}")
+    pool = pa.Pool(2, N, bs, H, D, dtype)
+    U.poison(pool)
+    pool.write_kv(1, U.dev_tensor(k, dtype), U.dev_tensor(v, dtype), torch.from_numpy(slots).cuda())
+    torch.cuda.synchronize()
+    got = U.pool_bits(pool)
+    g = LY.Geometry(2, N, bs, H, D, dtype)
+    exp = np.full(g.num_elements, W.POISON_BITS[dtype], dtype=U.BITS[dtype])
+    kb, vb = U.to_bits(k, dtype), U.to_bits(v, dtype)
+    hh, dd = np.meshgrid(np.arange(H), np.arange(D), indexing="ij")
+    for x, s in enumerate(slots):
+        if s < 0 or s >= N * bs:
+            continue
+        b, t = divmod(int(s), bs)
+        exp[LY.element_index(g, 1, b, hh, 0, t, dd)] = kb[x]
+        exp[LY.element_index(g, 1, b, hh, 1, t, dd)] = vb[x]
+    assert np.array_equal(got, exp)
+
+
 @pytest.mark.parametrize("name", list(SMALL))
 def test_write_kv_bit_exact(name):
     w = SMALL[name]()
