@@ -23,6 +23,31 @@ Policy details the pages leave open (this library's reading):
     boundaries; every operation is all-or-nothing;
   * ``release`` walks the table in logical order, decrements, and pushes every
     block whose count reaches zero.
+
+Automatic prefix caching ("PagedAttention and KV Cache Compression", "What
+Most People Miss": the engine fingerprints every block of prompt text and
+points a request whose block matches to the existing block instead of
+processing it again; "Paged Attention Explained", "Support for Prefix
+Sharing").  This library's reading, off until enabled:
+  * a block's identity is its token ids together with the identity of the
+    block before it (its key: the parent's cache serial, 0 for a sequence's
+    first block, and the block_size token ids), because a block's K/V depend
+    on every earlier token; keys are compared exactly, the hash only finds
+    them;
+  * ``append_tokens(sid, ids)`` with the sequence at a block boundary looks
+    the appended whole blocks up in order and stops at the first miss; every
+    hit shares the cached block (count + 1, taken out of the free stack if it
+    was free) and its tokens need neither a write nor attention (slot -1);
+    hits are applied first, then copy-on-write, then fresh blocks;
+  * a block is registered when it becomes full and all its token ids are
+    known; if its key is already registered the existing entry stays and the
+    sequence continues from that entry's serial;
+  * a registered block popped from the free stack for new contents is
+    evicted (unregistered); registered blocks released to count 0 go to the
+    bottom of the free stack, so uncached free blocks are reused first and
+    cached ones least recently freed first;
+  * a plain ``append`` (token ids unknown) ends the sequence's chain: no
+    further lookups or registrations for it; ``fork`` copies the chain state.
 """
 from __future__ import annotations
 
@@ -43,6 +68,9 @@ OUT_OF_BLOCKS = "OUT_OF_BLOCKS"
 class _Seq:
     table: list
     length: int
+    chain: bool = True    # every token id so far is known
+    parent: int = 0       # cache serial of the last full block (0: none yet)
+    tail: tuple = ()      # token ids of the partially filled last block
 
 
 class AllocatorModel:
@@ -59,6 +87,13 @@ class AllocatorModel:
         self.seqs: dict[int, _Seq] = {}
         self.next_id = 0
         self.cow_copies = 0
+        # prefix cache
+        self.cache_on = False
+        self.cache: dict[tuple, int] = {}   # (parent serial, token ids) -> block
+        self.key_of: dict[int, tuple] = {}  # registered block -> key
+        self.serial_of: dict[int, int] = {}  # registered block -> serial
+        self.next_serial = 1
+        self.cache_counts = dict(registered=0, hit_blocks=0, evicted=0, lookups=0)
 
     # -- helpers ---------------------------------------------------------
     def _seq(self, sid) -> _Seq:
@@ -76,6 +111,15 @@ class AllocatorModel:
         self.seqs[sid] = _Seq([], 0)
         return sid
 
+    def _pop_fresh(self) -> int:
+        """Top of the free stack for new contents; a registered block is evicted."""
+        b = self.stack.pop()
+        if b in self.key_of:
+            del self.cache[self.key_of.pop(b)]
+            del self.serial_of[b]
+            self.cache_counts["evicted"] += 1
+        return b
+
     def append(self, sid: int, n_tokens: int):
         """Returns (slots, cow_pairs) for positions length .. length+n-1."""
         s = self._seq(sid)
@@ -83,27 +127,90 @@ class AllocatorModel:
             raise AllocError(INVALID_ARG, "token count cannot be negative")
         if n_tokens == 0:
             return [], []
+        slots, pairs, _ = self._append(s, n_tokens, None)
+        return slots, pairs
+
+    def append_tokens(self, sid: int, token_ids):
+        """Append tokens given by id.  Returns (slots, cow_pairs, n_cached):
+        slots of tokens served by cached blocks are -1."""
+        s = self._seq(sid)
+        ids = [int(t) for t in token_ids]
+        if not ids:
+            return [], [], 0
+        return self._append(s, len(ids), ids)
+
+    def _append(self, s: _Seq, n_tokens: int, ids):
+        bs = self.bs
         len0, len1 = s.length, s.length + n_tokens
-        fresh = self._nblocks(len1) - self._nblocks(len0)
-        cow = len0 % self.bs != 0 and self.refcount[s.table[-1]] > 1
-        if fresh + int(cow) > len(self.stack):
+        known = ids is not None and self.cache_on and s.chain
+        # lookups: whole blocks from a block boundary, up to the first miss
+        hits = []
+        lookups = 0
+        parent = s.parent
+        if known and len0 % bs == 0:
+            for j in range(n_tokens // bs):
+                key = (parent, tuple(ids[j * bs:(j + 1) * bs]))
+                lookups += 1
+                b = self.cache.get(key)
+                if b is None:
+                    break
+                hits.append(b)
+                parent = self.serial_of[b]
+        free_hits = [b for b in hits if self.refcount[b] == 0]
+        fresh = self._nblocks(len1) - self._nblocks(len0) - len(hits)
+        cow = len0 % bs != 0 and self.refcount[s.table[-1]] > 1
+        if fresh + int(cow) > len(self.stack) - len(free_hits):
             raise AllocError(OUT_OF_BLOCKS, "pool exhausted")
+        self.cache_counts["lookups"] += lookups
+        for b in hits:
+            if self.refcount[b] == 0:
+                self.stack.remove(b)
+            self.refcount[b] += 1
+            s.table.append(b)
+        self.cache_counts["hit_blocks"] += len(hits)
         pairs = []
         if cow:
             old = s.table[-1]
-            new = self.stack.pop()
+            new = self._pop_fresh()
             self.refcount[old] -= 1
             self.refcount[new] = 1
             s.table[-1] = new
             pairs.append((old, new))
             self.cow_copies += 1
         for _ in range(fresh):
-            b = self.stack.pop()
+            b = self._pop_fresh()
             self.refcount[b] = 1
             s.table.append(b)
-        slots = [s.table[p // self.bs] * self.bs + p % self.bs for p in range(len0, len1)]
+        n_cached = len(hits) * bs
+        slots = [-1] * n_cached + [s.table[p // bs] * bs + p % bs for p in range(len0 + n_cached, len1)]
         s.length = len1
-        return slots, pairs
+        # chain state and registration of blocks that became full
+        if ids is None or not self.cache_on:
+            s.chain = False
+        if s.chain:
+            s.parent = parent
+            tail = list(s.tail)
+            pos = len0 + n_cached
+            for t in ids[n_cached:]:
+                tail.append(t)
+                pos += 1
+                if pos % bs == 0:
+                    b = s.table[pos // bs - 1]
+                    key = (s.parent, tuple(tail))
+                    if key in self.cache:
+                        s.parent = self.serial_of[self.cache[key]]
+                    else:
+                        self.cache[key] = b
+                        self.key_of[b] = key
+                        self.serial_of[b] = self.next_serial
+                        s.parent = self.next_serial
+                        self.next_serial += 1
+                        self.cache_counts["registered"] += 1
+                    tail = []
+            s.tail = tuple(tail)
+        else:
+            s.tail = ()
+        return slots, pairs, n_cached
 
     def fork(self, parent: int) -> int:
         p = self._seq(parent)
@@ -111,7 +218,7 @@ class AllocatorModel:
             self.refcount[b] += 1
         cid = self.next_id
         self.next_id += 1
-        self.seqs[cid] = _Seq(list(p.table), p.length)
+        self.seqs[cid] = _Seq(list(p.table), p.length, p.chain, p.parent, p.tail)
         return cid
 
     def release(self, sid: int):
@@ -119,8 +226,26 @@ class AllocatorModel:
         for b in s.table:
             self.refcount[b] -= 1
             if self.refcount[b] == 0:
-                self.stack.append(b)
+                if self.cache_on and b in self.key_of:
+                    self.stack.insert(0, b)  # cached: reused last
+                else:
+                    self.stack.append(b)
         del self.seqs[sid]
+
+    def enable_prefix_cache(self, on: bool):
+        """Turn prefix caching on or off; turning it off forgets every entry
+        and ends every sequence's chain."""
+        self.cache_on = bool(on)
+        if not on:
+            self.cache.clear()
+            self.key_of.clear()
+            self.serial_of.clear()
+            for s in self.seqs.values():
+                s.chain = False
+                s.tail = ()
+
+    def cache_stats(self):
+        return dict(self.cache_counts, cached_blocks=len(self.cache))
 
     # -- state -----------------------------------------------------------
     def block_table(self, sid: int):

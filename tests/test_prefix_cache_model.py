@@ -1,0 +1,253 @@
+"""Pins of the allocator model's automatic prefix caching.
+
+The property that makes sharing correct is checked by simulation, with no
+reference to the model's own bookkeeping: every token that is not served by a
+cached block is "written" -- its slot records the token together with every
+token before it, which is what its K/V are a function of -- and afterwards
+every live sequence must read exactly its own prefixes through its block
+table; a hit that pointed a sequence at a block holding other tokens, or the
+same tokens after other ones, fails it.  Besides that: the worked behaviours
+the reading fixes (whole blocks only, from a block boundary, position-
+dependent identity, reuse after release, eviction order), allocator
+invariants under random scripts, and planted policy slips that the
+simulation catches."""
+import random
+
+import pytest
+from hypothesis import given, settings, strategies as st
+
+from oracle.allocator import AllocatorModel, AllocError
+
+
+class Sim:
+    """Model plus a record of what each physical slot holds."""
+
+    def __init__(self, N, bs, **kw):
+        self.m = AllocatorModel(N, bs, **kw)
+        self.m.enable_prefix_cache(True)
+        self.bs = bs
+        self.slot_tok = {}
+        self.toks = {}
+
+    def new(self):
+        s = self.m.create()
+        self.toks[s] = []
+        return s
+
+    def add(self, s, ids):
+        slots, pairs, n_cached = self.m.append_tokens(s, ids)
+        for a, b in pairs:  # copy-on-write copies the whole block
+            for t in range(self.bs):
+                if (a * self.bs + t) in self.slot_tok:
+                    self.slot_tok[b * self.bs + t] = self.slot_tok[a * self.bs + t]
+        full = self.toks[s] + list(ids)
+        base = len(self.toks[s])
+        for x, sl in enumerate(slots):
+            if sl >= 0:
+                # what a slot's K/V are a function of: the token and all before it
+                self.slot_tok[sl] = tuple(full[:base + x + 1])
+        assert all(x == -1 for x in slots[:n_cached]) and all(x >= 0 for x in slots[n_cached:])
+        self.toks[s] = full
+        return slots, n_cached
+
+    def fork(self, s):
+        c = self.m.fork(s)
+        self.toks[c] = list(self.toks[s])
+        return c
+
+    def release(self, s):
+        self.m.release(s)
+        del self.toks[s]
+
+    def check(self):
+        bs = self.bs
+        for s, ids in self.toks.items():
+            tbl = self.m.block_table(s)
+            for p in range(len(ids)):
+                assert self.slot_tok.get(tbl[p // bs] * bs + p % bs) == tuple(ids[:p + 1]), (s, p)
+        rc, stack = self.m.state()
+        refs = [0] * self.m.N
+        for s in self.toks:
+            for b in self.m.block_table(s):
+                refs[b] += 1
+        assert rc == refs
+        assert sorted(stack + [b for b in range(self.m.N) if rc[b] > 0]) == list(range(self.m.N))
+
+
+def test_shared_prompt_blocks_are_reused():
+    sim = Sim(32, 4)
+    a = sim.new()
+    _, n = sim.add(a, list(range(10)))
+    assert n == 0
+    b = sim.new()
+    slots, n = sim.add(b, list(range(10)) + [99])
+    assert n == 8 and slots[:8] == [-1] * 8            # two whole blocks, not the partial third
+    assert sim.m.block_table(b)[:2] == sim.m.block_table(a)[:2]
+    assert sim.m.block_table(b)[2] != sim.m.block_table(a)[2]
+    c = sim.new()
+    _, n = sim.add(c, [0, 1, 2, 3, 7, 7, 7, 7])
+    assert n == 4                                       # first block only
+    sim.check()
+    assert sim.m.cache_stats()["hit_blocks"] == 3
+
+
+def test_identity_depends_on_position():
+    sim = Sim(32, 4)
+    a = sim.new()
+    sim.add(a, [5, 5, 5, 5, 1, 2, 3, 4])
+    b = sim.new()
+    _, n = sim.add(b, [1, 2, 3, 4])                     # same ids as a's second block, other position
+    assert n == 0
+    sim.check()
+
+
+def test_lookups_only_at_block_boundaries():
+    sim = Sim(32, 4)
+    a = sim.new()
+    sim.add(a, [1, 2, 3, 4, 5, 6, 7, 8])
+    b = sim.new()
+    sim.add(b, [1, 2])
+    _, n = sim.add(b, [3, 4, 5, 6, 7, 8])               # b is mid-block: no lookup
+    assert n == 0
+    assert sim.m.block_table(b) != sim.m.block_table(a)
+    _, n = sim.add(b, [9, 9, 9, 9])                     # at a boundary, but b's chain is its own
+    assert n == 0
+    c = sim.new()
+    _, n = sim.add(c, [1, 2, 3, 4, 5, 6, 7, 8, 9, 9, 9, 9])
+    assert n == 12                                      # b's blocks were registered under a's keys
+    sim.check()
+
+
+def test_released_blocks_stay_cached_until_reused():
+    sim = Sim(7, 4)
+    a = sim.new()
+    sim.add(a, list(range(8)))
+    blocks = sim.m.block_table(a)
+    sim.release(a)
+    b = sim.new()
+    _, n = sim.add(b, list(range(8)))
+    assert n == 8 and sim.m.block_table(b) == blocks    # taken back out of the free stack
+    sim.release(b)
+    # the five uncached blocks are handed out before any cached one
+    c = sim.new()
+    sim.add(c, [50 + i for i in range(20)])
+    assert not set(sim.m.block_table(c)) & set(blocks)
+    # the next allocation evicts the least recently freed cached block (the first)
+    d = sim.new()
+    sim.add(d, [90, 91, 92, 93])
+    assert sim.m.block_table(d) == [blocks[0]]
+    assert sim.m.cache_stats()["evicted"] == 1
+    sim.release(c)
+    e = sim.new()
+    _, n = sim.add(e, list(range(8)))
+    assert n == 0                                       # the chain starts at the evicted block
+    sim.check()
+
+
+def test_plain_append_ends_the_chain():
+    sim = Sim(32, 4)
+    a = sim.new()
+    sim.add(a, [1, 2, 3, 4])
+    sim.m.append(a, 4)                                  # ids unknown
+    b = sim.new()
+    sim.add(b, [1, 2, 3, 4, 5, 6, 7, 8])
+    assert sim.m.cache_stats()["registered"] == 2       # a's second block was never registered
+    del sim.toks[a]
+    sim.m.release(a)
+    sim.check()
+
+
+def test_out_of_blocks_changes_nothing():
+    sim = Sim(3, 4)
+    a = sim.new()
+    sim.add(a, list(range(8)))
+    before = (sim.m.state(), sim.m.cache_stats(), sim.m.block_table(a))
+    b = sim.new()
+    with pytest.raises(AllocError):
+        sim.m.append_tokens(b, list(range(8)) + list(range(100, 108)))
+    assert (sim.m.state(), sim.m.cache_stats(), sim.m.block_table(a)) == before
+
+
+def _random_script(rng, sim, steps, vocab, prompts):
+    live = []
+    for _ in range(steps):
+        op = rng.random()
+        try:
+            if op < 0.45 or not live:
+                s = sim.new()
+                live.append(s)
+                p = list(rng.choice(prompts))
+                cut = rng.randint(1, len(p))
+                sim.add(s, p[:cut])
+            elif op < 0.75:
+                s = rng.choice(live)
+                sim.add(s, [rng.randrange(vocab) for _ in range(rng.randint(1, 9))])
+            elif op < 0.85:
+                live.append(sim.fork(rng.choice(live)))
+            else:
+                s = live.pop(rng.randrange(len(live)))
+                sim.release(s)
+        except AllocError as e:
+            assert e.code == "OUT_OF_BLOCKS"
+        sim.check()
+    return live
+
+
+@settings(max_examples=60, deadline=None)
+@given(st.integers(0, 10 ** 6), st.sampled_from([2, 4, 16]), st.integers(12, 60))
+def test_random_scripts_keep_contents_and_invariants(seed, bs, N):
+    rng = random.Random(seed)
+    sim = Sim(N, bs, free_order=rng.sample(range(N), N))
+    vocab = 5
+    prompts = [[rng.randrange(vocab) for _ in range(rng.randint(bs, 5 * bs))] for _ in range(4)]
+    _random_script(rng, sim, 40, vocab, prompts)
+
+
+# ------------------------------------------------------- planted slips ---
+
+class _NoParentKeys(dict):
+    """A cache whose keys forget the parent: a block is found by its own
+    token ids wherever it sits."""
+
+    @staticmethod
+    def _k(key):
+        return (0, key[1])
+
+    def get(self, key, default=None):
+        return super().get(self._k(key), default)
+
+    def __contains__(self, key):
+        return super().__contains__(self._k(key))
+
+    def __getitem__(self, key):
+        return super().__getitem__(self._k(key))
+
+    def __setitem__(self, key, value):
+        super().__setitem__(self._k(key), value)
+
+    def __delitem__(self, key):
+        super().__delitem__(self._k(key))
+
+
+def _slip_ignores_parent(m):
+    m.cache = _NoParentKeys()
+
+
+def _slip_no_eviction(m):
+    m._pop_fresh = lambda: m.stack.pop()
+
+
+@pytest.mark.parametrize("slip", [_slip_ignores_parent, _slip_no_eviction], ids=lambda f: f.__name__)
+def test_planted_policy_slips_are_caught(slip):
+    caught = False
+    for seed in range(40):
+        rng = random.Random(seed)
+        sim = Sim(14, 2, free_order=rng.sample(range(14), 14))
+        slip(sim.m)
+        prompts = [[rng.randrange(2) for _ in range(rng.randint(2, 8))] for _ in range(3)]
+        try:
+            _random_script(rng, sim, 40, 2, prompts)
+        except (AssertionError, KeyError):
+            caught = True
+            break
+    assert caught
