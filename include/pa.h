@@ -212,6 +212,46 @@ int pa_seq_create(pa_pool* pool, int* seq);
 int pa_seq_append(pa_pool* pool, int seq, int n_tokens, int32_t* slots_out,
                   int32_t* cow_pairs_out, int* n_cow);
 
+/* ---- Automatic prefix caching ("PagedAttention and KV Cache Compression",
+ * "What Most People Miss": every block of prompt text gets a fingerprint, and
+ * a request whose block matches points to the already processed block
+ * instead of processing it again; "Paged Attention Explained", "Support for
+ * Prefix Sharing").  Off when a pool is created.  A full block is identified
+ * exactly by its block_size token ids and the identity of the block before it
+ * (a block's K/V depend on every earlier token); the hash only finds
+ * candidates, so a collision never shares wrong contents. ---- */
+
+typedef struct {
+  int64_t cached_blocks; /* blocks findable now                        */
+  int64_t registered;    /* blocks registered so far                   */
+  int64_t hit_blocks;    /* blocks served from the cache so far        */
+  int64_t evicted;       /* registered blocks reused for new contents  */
+  int64_t lookups;       /* block lookups so far                       */
+} pa_prefix_stats;
+
+/* Turn prefix caching on (enable != 0) or off.  Turning it off forgets every
+ * entry and ends every sequence's chain. */
+int pa_prefix_cache_enable(pa_pool* pool, int enable);
+
+/* Append tokens given by id (host int32 [n_tokens]).  As pa_seq_append, and
+ * with caching on: when the sequence is at a block boundary, the appended
+ * whole blocks are looked up in order up to the first miss; each hit shares
+ * the cached block (taken back from the free blocks if it was free), and its
+ * tokens get slot -1 in slots_out (no pa_write_kv and no attention needed:
+ * run pa_prefill on the remaining *n_cached..n_tokens-1 tokens only).  Blocks
+ * that become full with known ids are registered.  A registered block that
+ * the manager reuses for new contents is evicted; registered blocks whose
+ * count drops to zero are reused after every uncached free block, least
+ * recently freed first.  Register a block's K/V (pa_write_kv) before any
+ * attention that reads it, as for any appended token.
+ *   n_cached  host, receives the number of tokens served by the cache
+ *             (a multiple of block_size, at the start of the appended run)
+ * Errors as pa_seq_append; all-or-nothing. */
+int pa_seq_append_tokens(pa_pool* pool, int seq, const int32_t* token_ids, int n_tokens,
+                         int32_t* slots_out, int32_t* cow_pairs_out, int* n_cow, int* n_cached);
+
+int pa_prefix_cache_stats(const pa_pool* pool, pa_prefix_stats* stats);
+
 /* Fork: the child shares every block of the parent (counts incremented in
  * logical order) and has the parent's length. */
 int pa_seq_fork(pa_pool* pool, int parent, int* child);

@@ -32,7 +32,8 @@ ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2}
 EXPORTS = [
     "pa_version", "pa_last_error", "pa_pool_required_bytes", "pa_alloc_pool", "pa_free",
     "pa_write_kv", "pa_decode_workspace_bytes", "pa_decode", "pa_prefill", "pa_copy_blocks",
-    "pa_seq_create", "pa_seq_append", "pa_seq_fork", "pa_seq_release", "pa_seq_block_table",
+    "pa_seq_create", "pa_seq_append", "pa_prefix_cache_enable", "pa_seq_append_tokens",
+    "pa_prefix_cache_stats", "pa_seq_fork", "pa_seq_release", "pa_seq_block_table",
     "pa_batch_tables", "pa_pool_state", "pa_pool_stats", "pa_slots_for_positions",
 ]
 
@@ -54,6 +55,11 @@ class Stats(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int64) for n in (
         "num_blocks", "free_blocks", "used_blocks", "shared_blocks", "cow_copies",
         "live_seqs", "logical_tokens", "tail_slots")]
+
+
+class PrefixStats(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in (
+        "cached_blocks", "registered", "hit_blocks", "evicted", "lookups")]
 
 
 def _load():
@@ -78,6 +84,9 @@ def _load():
         "pa_copy_blocks": (c_int, [vp, vp, c_int, vp]),
         "pa_seq_create": (c_int, [vp, intp]),
         "pa_seq_append": (c_int, [vp, c_int, c_int, i32p, i32p, intp]),
+        "pa_prefix_cache_enable": (c_int, [vp, c_int]),
+        "pa_seq_append_tokens": (c_int, [vp, c_int, i32p, c_int, i32p, i32p, intp, intp]),
+        "pa_prefix_cache_stats": (c_int, [vp, ctypes.POINTER(PrefixStats)]),
         "pa_seq_fork": (c_int, [vp, c_int, intp]),
         "pa_seq_release": (c_int, [vp, c_int]),
         "pa_seq_block_table": (c_int, [vp, c_int, i32p, c_int, intp, intp]),
@@ -242,6 +251,26 @@ class Pool:
         _check(lib.pa_seq_append(self.handle, seq, n_tokens, _i32(slots) if n_tokens > 0 else None,
                                  _i32(pairs), ctypes.byref(nc)), "pa_seq_append")
         return slots, [(int(pairs[0]), int(pairs[1]))] if nc.value else []
+
+    def enable_prefix_cache(self, on: bool = True):
+        _check(lib.pa_prefix_cache_enable(self.handle, 1 if on else 0), "pa_prefix_cache_enable")
+
+    def seq_append_tokens(self, seq: int, token_ids):
+        """(slots, cow_pairs, n_cached); slots of cached tokens are -1."""
+        ids = np.ascontiguousarray(token_ids, dtype=np.int32)
+        n = int(ids.shape[0])
+        slots = np.empty(max(n, 0), dtype=np.int32)
+        pairs = np.empty(2, dtype=np.int32)
+        nc, ncached = ctypes.c_int(), ctypes.c_int()
+        _check(lib.pa_seq_append_tokens(self.handle, seq, _i32(ids) if n > 0 else None, n,
+                                        _i32(slots) if n > 0 else None, _i32(pairs), ctypes.byref(nc),
+                                        ctypes.byref(ncached)), "pa_seq_append_tokens")
+        return slots, ([(int(pairs[0]), int(pairs[1]))] if nc.value else []), int(ncached.value)
+
+    def prefix_cache_stats(self) -> dict:
+        s = PrefixStats()
+        _check(lib.pa_prefix_cache_stats(self.handle, ctypes.byref(s)), "pa_prefix_cache_stats")
+        return {n: int(getattr(s, n)) for n, _ in PrefixStats._fields_}
 
     def seq_fork(self, parent: int) -> int:
         c = ctypes.c_int()

@@ -11,10 +11,25 @@
 // order first; sequence ids are never reused; fork and release walk tables in
 // logical order; at most one copy per append (only the last block can be
 // partially filled); every operation validates before it mutates.
+//
+// Automatic prefix caching ("PagedAttention and KV Cache Compression", "What
+// Most People Miss": every block of prompt text gets a fingerprint, and a
+// request whose block matches points to the existing block instead of
+// processing it again).  A full block is identified exactly by the cache
+// serial of the block before it (0 for a sequence's first block) and its
+// block_size token ids; the hash only finds candidates.  Lookups run from a
+// block boundary over the appended whole blocks and stop at the first miss;
+// hits are applied before copy-on-write and fresh blocks.  A block is
+// registered when it becomes full with known ids (an existing entry with the
+// same key stays).  A registered block popped for new contents is evicted;
+// registered blocks freed to count 0 go to the bottom of the free stack, so
+// uncached blocks are reused first and cached ones least recently freed
+// first.  An append without ids ends the sequence's chain; fork copies it.
 #pragma once
 
 #include <cstdint>
 #include <string>
+#include <unordered_map>
 #include <vector>
 
 namespace pa {
@@ -31,6 +46,17 @@ class BlockAllocator {
   int32_t create();
   AllocResult append(int32_t seq, int32_t n_tokens, int32_t* slots_out, int32_t* cow_pair,
                      int* n_cow, std::string* err);
+  // Append tokens by id; slots of tokens served by cached blocks are -1 and
+  // their count is *n_cached (a multiple of the block size).
+  AllocResult append_tokens(int32_t seq, const int32_t* ids, int32_t n_tokens, int32_t* slots_out,
+                            int32_t* cow_pair, int* n_cow, int* n_cached, std::string* err);
+  void enable_prefix_cache(bool on);
+  bool prefix_cache_enabled() const { return cache_on_; }
+  struct CacheCounts {
+    int64_t registered = 0, hit_blocks = 0, evicted = 0, lookups = 0;
+  };
+  const CacheCounts& cache_counts() const { return counts_; }
+  int64_t cached_blocks() const { return static_cast<int64_t>(cache_.size()); }
   AllocResult fork(int32_t parent, int32_t* child, std::string* err);
   AllocResult release(int32_t seq, std::string* err);
 
@@ -53,13 +79,35 @@ class BlockAllocator {
     std::vector<int32_t> table;
     int32_t length = 0;
     bool alive = false;
+    bool chain = true;          // every token id so far is known
+    int64_t parent = 0;         // cache serial of the last full block
+    std::vector<int32_t> tail;  // ids of the partially filled last block
   };
+  struct Key {
+    int64_t parent;
+    std::vector<int32_t> ids;
+    bool operator==(const Key& o) const { return parent == o.parent && ids == o.ids; }
+  };
+  struct KeyHash {
+    size_t operator()(const Key& k) const;
+  };
+  AllocResult append_impl(int32_t seq, int32_t n_tokens, const int32_t* ids, int32_t* slots_out,
+                          int32_t* cow_pair, int* n_cow, int* n_cached, std::string* err);
+  int32_t pop_fresh();
+
   int32_t n_, bs_;
   std::vector<int32_t> ref_;
   std::vector<int32_t> stack_;  // top = back()
   std::vector<Seq> seqs_;
   int64_t cow_copies_ = 0;
   int64_t live_count_ = 0;
+  // prefix cache
+  bool cache_on_ = false;
+  std::unordered_map<Key, int32_t, KeyHash> cache_;
+  std::vector<int64_t> serial_;   // per block, 0 = not registered
+  std::vector<Key> key_of_;       // per block, valid when registered
+  int64_t next_serial_ = 1;
+  CacheCounts counts_;
 };
 
 }  // namespace pa

@@ -391,6 +391,38 @@ int pa_seq_append(pa_pool* pool, int seq, int n_tokens, int32_t* slots_out, int3
   });
 }
 
+int pa_seq_append_tokens(pa_pool* pool, int seq, const int32_t* token_ids, int n_tokens, int32_t* slots_out,
+                         int32_t* cow_pairs_out, int* n_cow, int* n_cached) {
+  return guarded([&]() -> int {
+    if (!pool) return fail(PA_ERR_INVALID_ARG, "pool is NULL");
+    if (n_tokens > 0 && (!slots_out || !token_ids)) return fail(PA_ERR_INVALID_ARG, "NULL argument");
+    std::string err;
+    return alloc_status(
+        pool->alloc.append_tokens(seq, token_ids, n_tokens, slots_out, cow_pairs_out, n_cow, n_cached, &err), err);
+  });
+}
+
+int pa_prefix_cache_enable(pa_pool* pool, int enable) {
+  return guarded([&]() -> int {
+    if (!pool) return fail(PA_ERR_INVALID_ARG, "pool is NULL");
+    pool->alloc.enable_prefix_cache(enable != 0);
+    return PA_OK;
+  });
+}
+
+int pa_prefix_cache_stats(const pa_pool* pool, pa_prefix_stats* out) {
+  return guarded([&]() -> int {
+    if (!pool || !out) return fail(PA_ERR_INVALID_ARG, "NULL argument");
+    const auto& c = pool->alloc.cache_counts();
+    out->cached_blocks = pool->alloc.cached_blocks();
+    out->registered = c.registered;
+    out->hit_blocks = c.hit_blocks;
+    out->evicted = c.evicted;
+    out->lookups = c.lookups;
+    return PA_OK;
+  });
+}
+
 int pa_seq_fork(pa_pool* pool, int parent, int* child) {
   return guarded([&]() -> int {
     if (!pool || !child) return fail(PA_ERR_INVALID_ARG, "NULL argument");
