@@ -41,7 +41,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="llama3_8b",
                     choices=["tiny", "opt13b", "llama3_8b", "long_ctx", "shared", "shared_cow",
-                             "prefill_tiny", "prefill_llama3_8b", "chunked_llama3_8b"])
+                             "prefill_tiny", "prefill_llama3_8b", "chunked_llama3_8b", "prefix_cache"])
     ap.add_argument("--contiguous", action="store_true",
                     help="place every sequence's blocks side by side in logical order (a "
                          "contiguous-cache control for the same kernel)")
@@ -274,6 +274,154 @@ def main_prefill(args):
     print(json.dumps(res), flush=True)
 
 
+PREFIX_METRIC = "shared-system-prompt admission: requests/s with automatic prefix caching (write + prefill)"
+
+
+def main_prefix(args):
+    """64 Llama-3-8B-shaped requests share a 1024-token system prompt (each
+    adds a 64..256-token question).  With prefix caching the prompt's whole
+    blocks are found in the cache, so a step writes and prefills only the
+    rest; without it a step writes and prefills every token.  The prompt is
+    kept cached by a pinned sequence, as a served system prompt would be."""
+    import torch
+    import paged_kv_cache_337_amd as pa
+    import workloads as W
+    from paged_kv_cache_337_amd import staging as U
+
+    w = W.prefix_cache()
+    R, bs = w.num_requests, w.block_size
+    reqs = list(range(R))
+    lens = [len(w.request_ids(r)) for r in reqs]
+    total = sum(lens)
+    N = sum(-(-n // bs) for n in lens) * 2 + 64
+    pool = pa.Pool(1, N, bs, w.num_kv_heads, w.head_dim, w.dtype)
+    U.poison(pool)
+    log(f"[bench] prefix_cache: {R} requests, prompt {len(w.prompt_ids)}, {total} tokens, pool {N} blocks")
+
+    # without the cache: every token is appended, written and prefilled
+    plain = U.run_prefix_requests(pool, w, reqs)
+    assert all(nc == 0 for _, nc in plain)
+    in_plain = U.prefix_prefill_inputs(pool, w, plain, reqs)
+    k_all = U.dev_tensor(np.concatenate([w.request_kv(r)[0] for r in reqs]), w.dtype)
+    v_all = U.dev_tensor(np.concatenate([w.request_kv(r)[1] for r in reqs]), w.dtype)
+    slots_plain = torch.from_numpy(pa.slots_for_positions(
+        pool.batch_tables([s for s, _ in plain], max(-(-n // bs) for n in lens))[0], bs,
+        np.zeros(R, dtype=np.int32), np.array(lens, dtype=np.int32))).cuda()
+
+    # with the cache: a pinned sequence holds the prompt; requests are admitted
+    pool.enable_prefix_cache(True)
+    pin = pool.seq_create()
+    pslots, _, _ = pool.seq_append_tokens(pin, w.prompt_ids)
+    pk, pv = w.prompt_kv()
+    pool.write_kv(0, U.dev_tensor(pk, w.dtype), U.dev_tensor(pv, w.dtype), torch.from_numpy(pslots).cuda())
+    cached = U.run_prefix_requests(pool, w, reqs)
+    n_cached = sum(nc for _, nc in cached)
+    in_cached = U.prefix_prefill_inputs(pool, w, cached, reqs)
+    kc = U.dev_tensor(np.concatenate([w.request_kv(r)[0][nc:] for r, (_, nc) in zip(reqs, cached)]), w.dtype)
+    vc = U.dev_tensor(np.concatenate([w.request_kv(r)[1][nc:] for r, (_, nc) in zip(reqs, cached)]), w.dtype)
+    slc = []
+    for r, (s, nc) in zip(reqs, cached):
+        tbl = np.array(pool.seq_block_table(s)[0], dtype=np.int32)
+        pos = np.arange(nc, lens[r])
+        slc.append(tbl[pos // bs] * bs + pos % bs)
+    slots_cached = torch.from_numpy(np.concatenate(slc).astype(np.int32)).cuda()
+    stream = torch.cuda.current_stream()
+
+    def timed(kk, vv, slots, inp, steps, warmup):
+        q, qs, t, c, mq, mc = inp
+        out = torch.empty_like(q)
+        for _ in range(warmup):
+            pool.write_kv(0, kk, vv, slots)
+            pool.prefill(0, q, qs, mq, t, c, mc, w.scale, out=out)
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        t0 = time.perf_counter()
+        for e in evs:
+            pool.write_kv(0, kk, vv, slots)
+            e[0].record(stream)
+            pool.prefill(0, q, qs, mq, t, c, mc, w.scale, out=out)
+            e[1].record(stream)
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) / steps
+        if not torch.isfinite(out.float()).all():
+            raise RuntimeError("non-finite prefill output")
+        return wall * 1e3, float(np.mean([a.elapsed_time(b) for a, b in evs]))
+
+    ms_c, pf_c = timed(kc, vc, slots_cached, in_cached, args.steps, args.warmup)
+    ms_p, pf_p = timed(k_all, v_all, slots_plain, in_plain, args.steps, args.warmup)
+
+    def flops(admitted):
+        tot = 0
+        for r, (_, nc) in zip(reqs, admitted):
+            n, c = lens[r] - nc, lens[r]
+            tot += n * (c - n) + n * (n + 1) // 2
+        return 4 * w.head_dim * w.num_q_heads * tot
+
+    # block-manager cost alone (host-only pool, no device work): one
+    # pa_seq_append_tokens per request, without and with the cache
+    hp = pa.Pool(1, N, bs, w.num_kv_heads, w.head_dim, w.dtype, device=None)
+    ids_all = [w.request_ids(r) for r in reqs]
+    t0 = time.perf_counter()
+    hs = [hp.seq_create() for _ in reqs]
+    for sq, ids in zip(hs, ids_all):
+        hp.seq_append_tokens(sq, ids)
+    host_plain = time.perf_counter() - t0
+    for sq in hs:
+        hp.seq_release(sq)
+    hp.enable_prefix_cache(True)
+    hp.seq_append_tokens(hp.seq_create(), w.prompt_ids)
+    t0 = time.perf_counter()
+    hs = [hp.seq_create() for _ in reqs]
+    for sq, ids in zip(hs, ids_all):
+        hp.seq_append_tokens(sq, ids)
+    host_cached = time.perf_counter() - t0
+
+    f_c = flops(cached)
+    peak = MFMA_PEAK_TFLOPS[w.dtype]
+    achieved = f_c / (pf_c * 1e-3) / 1e12
+    res = {
+        "metric": PREFIX_METRIC,
+        "value": round(R / (ms_c * 1e-3), 1),
+        "unit": "requests/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_c, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": f"prefix_cache: {R} requests sharing a {len(w.prompt_ids)}-token system prompt, "
+                        f"questions 64-256 tokens ({total} tokens), {w.num_q_heads}q/{w.num_kv_heads}kv heads, "
+                        f"head_dim {w.head_dim}, block_size {bs}, one layer",
+            "step": "pa_write_kv (tokens the cache did not serve) + pa_prefill (those tokens)",
+        },
+        "tokens_served_from_cache": n_cached,
+        "tokens_written_and_prefilled": total - n_cached,
+        "without_cache": {"requests_per_s": round(R / (ms_p * 1e-3), 1), "ms_per_step": round(ms_p, 5),
+                          "prefill_ms": round(pf_p, 5), "tflops": round(flops(plain) / (pf_p * 1e-3) / 1e12, 2)},
+        "speedup_vs_no_cache": round(ms_p / ms_c, 3),
+        "host_block_manager_us_per_request": {
+            "cached": round(host_cached * 1e6 / R, 2), "no_cache": round(host_plain * 1e6 / R, 2),
+            "note": "pa_seq_create + pa_seq_append_tokens through ctypes, host-only pool"},
+        "prefix_cache_stats": pool.prefix_cache_stats(),
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "pa_prefill (prefill_lds_kernel) over the uncached tokens",
+            "achieved": round(achieved, 2),
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4),
+            "traffic": None,
+            "alg_flops_per_launch": f_c,
+            "avg_launch_ms": round(pf_c, 5),
+        },
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -281,6 +429,8 @@ def main():
         sys.exit(2)
     if args.workload.startswith(("prefill", "chunked")):
         return main_prefill(args)
+    if args.workload == "prefix_cache":
+        return main_prefix(args)
 
     import torch
     import paged_kv_cache_337_amd as pa

@@ -175,7 +175,8 @@ class Pool:
 
     def __del__(self):
         h = getattr(self, "handle", None)
-        if h is not None and h.value:
+        # at interpreter shutdown the module globals may already be gone
+        if h is not None and h.value and lib is not None:
             lib.pa_free(h)
             self.handle = None
 

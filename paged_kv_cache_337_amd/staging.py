@@ -178,3 +178,43 @@ def run_prefill_script(pool: Pool, batch, layer: int = 0, device="cuda"):
     torch.cuda.synchronize()
     width = max(-(-int(c) // batch.block_size) for c in batch.context_lens)
     return pool.batch_tables(seqs, width)
+
+
+def run_prefix_requests(pool: Pool, w, requests, layer: int = 0, device="cuda"):
+    """Admit requests of a shared-prompt batch through the block manager's
+    prefix cache: per request, one pa_seq_append_tokens of all its token ids,
+    then one batched pa_write_kv of every token the cache did not serve.
+    Returns [(sequence id, tokens served by the cache)] in request order."""
+    out = []
+    ks, vs, sl = [], [], []
+    for r in requests:
+        ids = w.request_ids(r)
+        s = pool.seq_create()
+        slots, pairs, n_cached = pool.seq_append_tokens(s, ids)
+        assert not pairs
+        k, v = w.request_kv(r)
+        ks.append(k[n_cached:])
+        vs.append(v[n_cached:])
+        sl.append(slots[n_cached:])
+        out.append((s, n_cached))
+    if sum(len(x) for x in sl):
+        pool.write_kv(layer, dev_tensor(np.concatenate(ks), w.dtype, device),
+                      dev_tensor(np.concatenate(vs), w.dtype, device),
+                      torch.from_numpy(np.concatenate(sl)).to(device))
+    torch.cuda.synchronize()
+    return out
+
+
+def prefix_prefill_inputs(pool: Pool, w, admitted, requests, device="cuda"):
+    """(q, query_start, block_tables, context_lens, max_query_len, max_context_len)
+    for prefilling the tokens the cache did not serve, one sequence per request."""
+    seqs = [s for s, _ in admitted]
+    lens = [len(w.request_ids(r)) for r in requests]
+    width = max(-(-n // w.block_size) for n in lens)
+    tables, ctx = pool.batch_tables(seqs, width)
+    qrows = [w.request_q(r)[nc:] for r, (_, nc) in zip(requests, admitted)]
+    qs = np.zeros(len(seqs) + 1, dtype=np.int32)
+    qs[1:] = np.cumsum([len(x) for x in qrows])
+    return (dev_tensor(np.concatenate(qrows), w.dtype, device), torch.from_numpy(qs).to(device),
+            torch.from_numpy(tables).to(device), torch.from_numpy(ctx).to(device),
+            int(max(len(x) for x in qrows)), int(ctx.max()))

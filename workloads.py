@@ -321,6 +321,74 @@ def custom_prefill(name: str, seed: int, dtype: str, ctx, qlens, hq: int, hkv: i
                     extra_blocks=extra_blocks)
 
 
+@dataclass
+class PrefixWorkload:
+    """Requests that share a system prompt: request r's tokens are the prompt's
+    ids followed by its own question ids.  A token's K/V and query rows are a
+    function of the request's tokens up to it, so the prompt's rows are drawn
+    once and shared by every request, and each question's rows per request."""
+
+    name: str
+    dtype: str
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    block_size: int
+    prompt_ids: np.ndarray          # int32 [P]
+    question_ids: list              # int32 arrays, one per request
+    scale: float
+    seed: int
+    kv_std: float = 1.0
+
+    @property
+    def num_requests(self) -> int:
+        return len(self.question_ids)
+
+    def request_ids(self, r: int) -> np.ndarray:
+        return np.concatenate([self.prompt_ids, self.question_ids[r]]).astype(np.int32)
+
+    def _rows(self, key, n, heads):
+        rng = np.random.default_rng([int(self.seed)] + list(key))
+        x = rng.standard_normal((n, heads, self.head_dim), dtype=np.float32)
+        return x
+
+    def prompt_kv(self):
+        k = self._rows((2, 0), len(self.prompt_ids), self.num_kv_heads) * np.float32(self.kv_std)
+        v = self._rows((2, 1), len(self.prompt_ids), self.num_kv_heads) * np.float32(self.kv_std)
+        return round_to_storage(k, self.dtype), round_to_storage(v, self.dtype)
+
+    def question_kv(self, r: int):
+        n = len(self.question_ids[r])
+        k = self._rows((3, r, 0), n, self.num_kv_heads) * np.float32(self.kv_std)
+        v = self._rows((3, r, 1), n, self.num_kv_heads) * np.float32(self.kv_std)
+        return round_to_storage(k, self.dtype), round_to_storage(v, self.dtype)
+
+    def request_kv(self, r: int):
+        pk, pv = self.prompt_kv()
+        qk, qv = self.question_kv(r)
+        return np.concatenate([pk, qk]), np.concatenate([pv, qv])
+
+    def request_q(self, r: int):
+        """Query rows of every token of request r, [P + Q_r, Hq, D]."""
+        pq = self._rows((4,), len(self.prompt_ids), self.num_q_heads)
+        qq = self._rows((5, r), len(self.question_ids[r]), self.num_q_heads)
+        return round_to_storage(np.concatenate([pq, qq]), self.dtype)
+
+
+def prefix_cache(seed: int = 10, requests: int = 64, prompt: int = 1024, dtype: str = "bf16",
+                 hq: int = 32, hkv: int = 8, d: int = 128, bs: int = 16, q_lo: int = 64,
+                 q_hi: int = 256) -> PrefixWorkload:
+    """Llama-3-8B-shaped requests sharing a 1024-token system prompt, each with
+    a question of uniform [64, 256] tokens (ids from a 128k vocabulary)."""
+    rng = np.random.default_rng([seed, 0])
+    prompt_ids = rng.integers(0, 128000, prompt).astype(np.int32)
+    lens = rng.integers(q_lo, q_hi, requests, endpoint=True)
+    qids = [rng.integers(0, 128000, int(n)).astype(np.int32) for n in lens]
+    return PrefixWorkload(name="prefix_cache", dtype=dtype, num_q_heads=hq, num_kv_heads=hkv,
+                          head_dim=d, block_size=bs, prompt_ids=prompt_ids, question_ids=qids,
+                          scale=float(np.float32(1.0 / np.sqrt(d))), seed=seed)
+
+
 PREFILL_WORKLOADS = {
     "prefill_tiny": prefill_tiny,
     "prefill_llama3_8b": prefill_llama3_8b,
