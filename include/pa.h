@@ -157,6 +157,10 @@ size_t pa_decode_workspace_bytes(const pa_pool* pool, int num_seqs, int num_q_he
  *   partition_tokens   0 = automatic, else a multiple of block_size and of 16
  *   workspace          device, >= pa_decode_workspace_bytes(...) bytes,
  *                      256-byte aligned; contents need no initialisation
+ * K/V are read with streaming (non-temporal) loads, or with cached loads when
+ * at least a quarter of the pool's used blocks are shared (reference count > 1
+ * in its block manager), so that the other readers of a shared block find it
+ * in L2 or the Infinity Cache; the result is the same either way.
  * Asynchronous on `stream`; the result is ready when the stream reaches it. */
 int pa_decode(const pa_pool* pool, int layer, const void* q, int num_seqs, int num_q_heads,
               const int32_t* block_tables, int max_blocks_per_seq,

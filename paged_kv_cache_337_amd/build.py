@@ -51,12 +51,18 @@ def _run(cmd):
 
 
 def build(verbose: bool = False) -> str:
+    from concurrent.futures import ThreadPoolExecutor
     os.makedirs(BUILD_DIR, exist_ok=True)
-    objs = []
-    for src in SOURCES:
+
+    def compile_one(src):
         obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
         lang = ["-x", "hip"] if src.endswith(".hip") else []
-        out = _run([HIPCC, *COMMON, *lang, "-c", src, "-o", obj])
+        return obj, _run([HIPCC, *COMMON, *lang, "-c", src, "-o", obj])
+
+    with ThreadPoolExecutor(min(len(SOURCES), os.cpu_count() or 1)) as ex:
+        results = list(ex.map(compile_one, SOURCES))
+    objs = []
+    for obj, out in results:
         if verbose and out:
             print(out)
         objs.append(obj)

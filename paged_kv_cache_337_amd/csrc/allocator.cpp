@@ -144,14 +144,14 @@ AllocResult BlockAllocator::append_impl(int32_t seq, int32_t n_tokens, const int
         }
       }
     }
-    ++ref_[b];
+    inc_ref(b);
     s.table.push_back(b);
   }
   counts_.hit_blocks += static_cast<int64_t>(hits.size());
   if (cow) {
     const int32_t old_b = s.table.back();
     const int32_t new_b = pop_fresh();
-    --ref_[old_b];
+    dec_ref(old_b);
     ref_[new_b] = 1;
     s.table.back() = new_b;
     if (cow_pair) {
@@ -221,7 +221,7 @@ AllocResult BlockAllocator::fork(int32_t parent, int32_t* child, std::string* er
     *err = "unknown or released parent sequence";
     return AllocResult::InvalidArg;
   }
-  for (int32_t b : seqs_[parent].table) ++ref_[b];
+  for (int32_t b : seqs_[parent].table) inc_ref(b);
   Seq c;
   c.table = seqs_[parent].table;
   c.length = seqs_[parent].length;
@@ -242,7 +242,7 @@ AllocResult BlockAllocator::release(int32_t seq, std::string* err) {
   }
   Seq& s = seqs_[seq];
   for (int32_t b : s.table) {
-    if (--ref_[b] == 0) {
+    if (dec_ref(b) == 0) {
       if (cache_on_ && serial_[b] != 0) {
         stack_.insert(stack_.begin(), b);  // cached: reused last
       } else {
@@ -274,11 +274,13 @@ int64_t BlockAllocator::tail_slots() const {
   return t;
 }
 
-int64_t BlockAllocator::shared_blocks() const {
-  int64_t c = 0;
-  for (int32_t r : ref_)
-    if (r > 1) ++c;
-  return c;
+void BlockAllocator::inc_ref(int32_t b) {
+  if (++ref_[b] == 2) ++shared_count_;
+}
+
+int32_t BlockAllocator::dec_ref(int32_t b) {
+  if (ref_[b]-- == 2) --shared_count_;
+  return ref_[b];
 }
 
 }  // namespace pa

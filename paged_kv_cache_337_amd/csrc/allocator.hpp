@@ -72,7 +72,7 @@ class BlockAllocator {
   int64_t live_seqs() const { return live_count_; }
   int64_t logical_tokens() const;
   int64_t tail_slots() const;
-  int64_t shared_blocks() const;
+  int64_t shared_blocks() const { return shared_count_; }  // blocks with count > 1
 
  private:
   struct Seq {
@@ -94,6 +94,8 @@ class BlockAllocator {
   AllocResult append_impl(int32_t seq, int32_t n_tokens, const int32_t* ids, int32_t* slots_out,
                           int32_t* cow_pair, int* n_cow, int* n_cached, std::string* err);
   int32_t pop_fresh();
+  void inc_ref(int32_t b);
+  int32_t dec_ref(int32_t b);  // returns the new count
 
   int32_t n_, bs_;
   std::vector<int32_t> ref_;
@@ -101,6 +103,7 @@ class BlockAllocator {
   std::vector<Seq> seqs_;
   int64_t cow_copies_ = 0;
   int64_t live_count_ = 0;
+  int64_t shared_count_ = 0;  // blocks with count > 1
   // prefix cache
   bool cache_on_ = false;
   std::unordered_map<Key, int32_t, KeyHash> cache_;

@@ -277,6 +277,13 @@ int pa_decode(const pa_pool* pool, int layer, const void* q, int num_seqs, int n
     p.items = reinterpret_cast<int4*>(ws + wl.items_off);
     p.ws_o = max_parts > 1 ? reinterpret_cast<float*>(ws + wl.o_off) : nullptr;
     p.ws_ml = max_parts > 1 ? reinterpret_cast<float*>(ws + wl.ml_off) : nullptr;
+    // Streaming loads suit K/V that one sequence reads once; when the block
+    // manager holds many shared blocks (forked branches, cached prefixes),
+    // cached loads let the other readers find them in L2 or the Infinity
+    // Cache.  Measured on MI355X: streaming is 9% faster on unshared batches,
+    // cached 14% faster on four branches per shared prefix.
+    const int64_t used = pool->alloc.num_blocks() - static_cast<int64_t>(pool->alloc.free_stack().size());
+    p.keep_in_cache = (used > 0 && 4 * pool->alloc.shared_blocks() >= used) ? 1 : 0;
     hipError_t e = pa::launch_decode(p, d.dtype, d.head_dim, s);
     return e == hipSuccess ? PA_OK : hip_fail(e, "decode launch");
   });

@@ -16,9 +16,16 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 // 16-byte streaming load (data read once: non-temporal hint).
+#ifndef PA_STREAM_NONTEMPORAL
+#define PA_STREAM_NONTEMPORAL 1
+#endif
 __device__ __forceinline__ uint4 load_stream16(const uint4* p) {
+#if PA_STREAM_NONTEMPORAL
   const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
   return make_uint4(v.x, v.y, v.z, v.w);
+#else
+  return *p;
+#endif
 }
 
 // Storage element tags.  `bits` is the type moved through memory.

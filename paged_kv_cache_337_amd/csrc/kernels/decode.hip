@@ -128,8 +128,8 @@ __device__ __forceinline__ Item make_item(const DecodeParams& p, int4 rec, int h
 }
 
 // The whole run of one item, its first piece's prologue already issued.
-template <int PF, int NCH, int D, int kBytes, typename Compute>
-__device__ __forceinline__ void stream_item(const DecodeParams& p, UnitStream<D, kBytes>& st,
+template <int PF, int NCH, typename Stream, typename Compute>
+__device__ __forceinline__ void stream_item(const DecodeParams& p, Stream& st,
                                             Frag<NCH> (&f)[PF + 1], bool (&ok)[PF + 1], const Item& it,
                                             int lane, Compute&& compute) {
   stream_run<PF, NCH>(p, st, f, ok, it.trow, it.start, it.u0, it.u1, it.h, lane, compute);
@@ -587,7 +587,7 @@ struct ValuPath {
 // whichever workgroup finishes first (measured: holding two indices per
 // workgroup costs more in the tail than it saves between items there).
 // ---------------------------------------------------------------------------
-template <typename Path, typename T, int D, bool kDeep>
+template <typename Path, typename T, int D, bool kDeep, bool kKeep>
 __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p, const int4* __restrict__ items) {
   constexpr int kBytes = T::kBytes;
   constexpr int NCH = Path::NCH;
@@ -613,7 +613,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p, const 
   Item it = make_item(p, items[cur / H], cur % H, P, wave);
   typename Path::Q q;
   Path::load_q(q, p, it, lane);
-  UnitStream<D, kBytes> st;
+  UnitStream<D, kBytes, kKeep> st;
   Frag<NCH> f[PF + 1];
   bool ok[PF + 1];
   st.begin(p, it.trow, it.start, it.u0, it.h);
@@ -775,8 +775,8 @@ constexpr int kDeepItemsPerWorkgroup = 16;
 template <typename Path, typename T, int D>
 hipError_t launch_decode_kernel(DecodeParams p, hipStream_t stream) {
   const int64_t work_bound = static_cast<int64_t>(p.S) * p.max_parts * p.H;
-  const void* k_shallow = reinterpret_cast<const void*>(&decode_kernel<Path, T, D, false>);
-  const void* k_deep = reinterpret_cast<const void*>(&decode_kernel<Path, T, D, true>);
+  const void* k_shallow = reinterpret_cast<const void*>(&decode_kernel<Path, T, D, false, false>);
+  const void* k_deep = reinterpret_cast<const void*>(&decode_kernel<Path, T, D, true, false>);
   int grid = persistent_grid(k_shallow);
   if (grid <= 0) return hipErrorInvalidValue;
   const bool deep = !p.auto_partition && work_bound >= static_cast<int64_t>(kDeepItemsPerWorkgroup) * grid;
@@ -788,10 +788,14 @@ hipError_t launch_decode_kernel(DecodeParams p, hipStream_t stream) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int4* items = static_cast<const int4*>(p.items);
+  // Cached loads when the batch shares blocks (the shallow schedule only:
+  // shared prefixes come with automatic partitioning in practice).
   if (deep) {
-    hipLaunchKernelGGL((decode_kernel<Path, T, D, true>), dim3(grid), dim3(kThreads), 0, stream, p, items);
+    hipLaunchKernelGGL((decode_kernel<Path, T, D, true, false>), dim3(grid), dim3(kThreads), 0, stream, p, items);
+  } else if (p.keep_in_cache) {
+    hipLaunchKernelGGL((decode_kernel<Path, T, D, false, true>), dim3(grid), dim3(kThreads), 0, stream, p, items);
   } else {
-    hipLaunchKernelGGL((decode_kernel<Path, T, D, false>), dim3(grid), dim3(kThreads), 0, stream, p, items);
+    hipLaunchKernelGGL((decode_kernel<Path, T, D, false, false>), dim3(grid), dim3(kThreads), 0, stream, p, items);
   }
   return hipGetLastError();
 }

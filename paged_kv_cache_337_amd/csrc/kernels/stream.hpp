@@ -28,7 +28,10 @@ struct Frag {
 // The block ids of a piece of the run (at most 64 logical blocks) are held one
 // per lane and read out with v_readlane, so locating a unit is scalar
 // arithmetic with no memory access.
-template <int D, int kBytes>
+// kKeep selects ordinary (cached) loads instead of streaming ones, for
+// batches whose sequences share blocks: the other readers of a shared block
+// then find it in L2 or the Infinity Cache.
+template <int D, int kBytes, bool kKeep = false>
 struct UnitStream {
   const char* layer_base;  // pool base + layer offset (bytes)
   const int32_t* trow;     // block-table row of the sequence
@@ -85,9 +88,9 @@ struct UnitStream {
     const uint4* kp = reinterpret_cast<const uint4*>(kb + lane_off);
     const uint4* vp = reinterpret_cast<const uint4*>(vb + lane_off);
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) f.k[c] = load_stream16(kp + 64 * c);
+    for (int c = 0; c < NCH; ++c) f.k[c] = kKeep ? kp[64 * c] : load_stream16(kp + 64 * c);
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) f.v[c] = load_stream16(vp + 64 * c);
+    for (int c = 0; c < NCH; ++c) f.v[c] = kKeep ? vp[64 * c] : load_stream16(vp + 64 * c);
     return ok;
   }
 };
@@ -137,8 +140,8 @@ __device__ __forceinline__ int piece_end(int bs, int start, int u) {
 // Units [u0, u1) of the token range starting at `start` of one table row,
 // the first piece's prologue already issued.  Runs longer than 64 blocks load
 // the ids of each further piece where it starts.
-template <int PF, int NCH, int D, int kBytes, typename Params, typename Compute>
-__device__ __forceinline__ void stream_run(const Params& p, UnitStream<D, kBytes>& st, Frag<NCH> (&f)[PF + 1],
+template <int PF, int NCH, typename Stream, typename Params, typename Compute>
+__device__ __forceinline__ void stream_run(const Params& p, Stream& st, Frag<NCH> (&f)[PF + 1],
                                            bool (&ok)[PF + 1], const int32_t* trow, int start, int u0, int u1,
                                            int head, int lane, Compute&& compute) {
   int a = u0;

@@ -34,6 +34,7 @@ struct DecodeParams {
   int4* items;               // [S * max_parts] (sequence, partition, context, partitions), longest first
   float* ws_o;               // [S, Hq, max_parts, D]
   float* ws_ml;              // [S, Hq, max_parts, 2] (max in log2 units, sum)
+  int32_t keep_in_cache;     // 1: read K/V with cached loads (sequences share blocks)
 };
 
 struct PrefillParams {
