@@ -48,6 +48,24 @@ Sharing").  This library's reading, off until enabled:
     cached ones least recently freed first;
   * a plain ``append`` (token ids unknown) ends the sequence's chain: no
     further lookups or registrations for it; ``fork`` copies the chain state.
+
+Swap to a host tier ("Paged Attention Explained", "Hybrid Memory Strategies":
+cached data may move to another memory tier when GPU memory runs short, at a
+transfer cost; "PagedAttention: paging the KV cache like an OS pages memory",
+"Why an agent should care", names the swap/preemption policy).  This
+library's reading:
+  * the host tier is a set of host blocks, each holding one device block of
+    every layer; its free blocks form a LIFO stack, initially ascending ids;
+  * ``swap_out`` gives every block of the sequence's table, in logical order,
+    the top host block, reports (device, host) pairs to copy, then releases
+    the device blocks as ``release`` would; the sequence keeps its length and
+    prefix-cache chain and becomes swapped (no append or fork until swapped
+    in);
+  * ``swap_in`` takes fresh device blocks (as an append would) in logical
+    order, reports (host, device) pairs, and returns the host blocks to the
+    host stack in logical order;
+  * both are all-or-nothing; releasing a swapped sequence frees its host
+    blocks.
 """
 from __future__ import annotations
 
@@ -71,6 +89,7 @@ class _Seq:
     chain: bool = True    # every token id so far is known
     parent: int = 0       # cache serial of the last full block (0: none yet)
     tail: tuple = ()      # token ids of the partially filled last block
+    host: list = None     # host blocks while swapped out (None: on the device)
 
 
 class AllocatorModel:
@@ -94,12 +113,18 @@ class AllocatorModel:
         self.serial_of: dict[int, int] = {}  # registered block -> serial
         self.next_serial = 1
         self.cache_counts = dict(registered=0, hit_blocks=0, evicted=0, lookups=0)
+        # host tier
+        self.host_n = 0
+        self.host_stack: list = []
 
     # -- helpers ---------------------------------------------------------
-    def _seq(self, sid) -> _Seq:
+    def _seq(self, sid, swapped_ok=False) -> _Seq:
         if sid not in self.seqs:
             raise AllocError(INVALID_ARG, f"no live sequence {sid}")
-        return self.seqs[sid]
+        s = self.seqs[sid]
+        if s.host is not None and not swapped_ok:
+            raise AllocError(INVALID_ARG, f"sequence {sid} is swapped out")
+        return s
 
     def _nblocks(self, n_tokens):
         return -(-n_tokens // self.bs)
@@ -222,7 +247,16 @@ class AllocatorModel:
         return cid
 
     def release(self, sid: int):
-        s = self._seq(sid)
+        s = self._seq(sid, swapped_ok=True)
+        if s.host is not None:
+            for hb in s.host:
+                self.host_stack.append(hb)
+            del self.seqs[sid]
+            return
+        self._free_device(s)
+        del self.seqs[sid]
+
+    def _free_device(self, s: _Seq):
         for b in s.table:
             self.refcount[b] -= 1
             if self.refcount[b] == 0:
@@ -230,7 +264,49 @@ class AllocatorModel:
                     self.stack.insert(0, b)  # cached: reused last
                 else:
                     self.stack.append(b)
-        del self.seqs[sid]
+
+    # -- host tier -------------------------------------------------------
+    def host_tier(self, num_host_blocks: int):
+        """Set up (or resize, with nothing swapped) the host tier."""
+        if num_host_blocks < 0:
+            raise AllocError(INVALID_ARG, "negative host block count")
+        if any(s.host is not None for s in self.seqs.values()):
+            raise AllocError(INVALID_ARG, "sequences are swapped out")
+        self.host_n = num_host_blocks
+        self.host_stack = list(range(num_host_blocks))[::-1]
+
+    def swap_out(self, sid: int):
+        """(device, host) pairs to copy out, in logical order."""
+        s = self._seq(sid)
+        n = len(s.table)
+        if n > len(self.host_stack):
+            raise AllocError(OUT_OF_BLOCKS, "host tier exhausted")
+        host = [self.host_stack.pop() for _ in range(n)]
+        pairs = list(zip(s.table, host))
+        self._free_device(s)
+        s.table = []
+        s.host = host
+        return pairs
+
+    def swap_in(self, sid: int):
+        """(host, device) pairs to copy in, in logical order."""
+        s = self._seq(sid, swapped_ok=True)
+        if s.host is None:
+            raise AllocError(INVALID_ARG, f"sequence {sid} is not swapped out")
+        n = len(s.host)
+        if n > len(self.stack):
+            raise AllocError(OUT_OF_BLOCKS, "pool exhausted")
+        table = []
+        for _ in range(n):
+            b = self._pop_fresh()
+            self.refcount[b] = 1
+            table.append(b)
+        pairs = list(zip(s.host, table))
+        for hb in s.host:
+            self.host_stack.append(hb)
+        s.table = table
+        s.host = None
+        return pairs
 
     def enable_prefix_cache(self, on: bool):
         """Turn prefix caching on or off; turning it off forgets every entry
@@ -249,10 +325,15 @@ class AllocatorModel:
 
     # -- state -----------------------------------------------------------
     def block_table(self, sid: int):
-        return list(self._seq(sid).table)
+        s = self._seq(sid, swapped_ok=True)
+        return list(s.table) if s.host is None else []
+
+    def host_table(self, sid: int):
+        s = self._seq(sid, swapped_ok=True)
+        return list(s.host or [])
 
     def length(self, sid: int) -> int:
-        return self._seq(sid).length
+        return self._seq(sid, swapped_ok=True).length
 
     def state(self):
         """(refcounts, free stack bottom->top)."""
@@ -267,6 +348,11 @@ class AllocatorModel:
             shared_blocks=sum(1 for c in self.refcount if c > 1),
             cow_copies=self.cow_copies,
             live_seqs=len(self.seqs),
-            logical_tokens=sum(s.length for s in live),
-            tail_slots=sum(len(s.table) * self.bs - s.length for s in live),
+            logical_tokens=sum(s.length for s in live if s.host is None),
+            tail_slots=sum(len(s.table) * self.bs - s.length for s in live if s.host is None),
         )
+
+    def host_state(self):
+        """(host blocks in use, host free stack bottom->top, swapped sequences)."""
+        used = self.host_n - len(self.host_stack)
+        return used, list(self.host_stack), sorted(k for k, s in self.seqs.items() if s.host is not None)
