@@ -41,7 +41,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="llama3_8b",
                     choices=["tiny", "opt13b", "llama3_8b", "long_ctx", "shared", "shared_cow",
-                             "prefill_tiny", "prefill_llama3_8b", "chunked_llama3_8b", "prefix_cache"])
+                             "prefill_tiny", "prefill_llama3_8b", "chunked_llama3_8b", "prefix_cache",
+                             "swap"])
     ap.add_argument("--contiguous", action="store_true",
                     help="place every sequence's blocks side by side in logical order (a "
                          "contiguous-cache control for the same kernel)")
@@ -422,6 +423,111 @@ def main_prefix(args):
     print(json.dumps(res), flush=True)
 
 
+SWAP_METRIC = "swap of whole sequences between the paged pool and pinned host memory, GB/s per direction"
+
+
+def main_swap(args):
+    """Every sequence of the Llama-3-8B-shaped decode batch (256 sequences,
+    1.5 GB of K/V in one layer) is swapped out to pinned host memory and back
+    in: block-manager calls, then one pa_swap_blocks launch per direction.  The
+    link's reference rate is a PyTorch copy of the same number of bytes between
+    a device tensor and a pinned host tensor (DMA engines)."""
+    import torch
+    import paged_kv_cache_337_amd as pa
+    import workloads as W
+    from paged_kv_cache_337_amd import staging as U
+
+    w = W.llama3_8b()
+    S, bs = w.num_seqs, w.block_size
+    pool = pa.Pool(1, w.num_blocks, bs, w.num_kv_heads, w.head_dim, w.dtype)
+    U.poison(pool)
+    seqs = [pool.seq_create() for _ in range(S)]
+    for s, c in zip(seqs, w.context_lens):
+        pool.seq_append(s, int(c))
+    tables, ctx = pool.batch_tables(seqs, w.max_blocks_per_seq)
+    U.fill_pool(pool, w, tables=tables)
+    nblk = w.num_blocks
+    pool.host_tier_init(nblk)
+    hbb = pool.host_block_bytes
+    host = torch.empty(nblk * hbb, dtype=torch.uint8, pin_memory=True)
+    moved = nblk * hbb
+    log(f"[bench] swap: {S} sequences, {nblk} blocks, {moved / 1e9:.2f} GB each way")
+    stream = torch.cuda.current_stream()
+    out_ms, in_ms, host_us = [], [], []
+    for _ in range(args.warmup + args.steps):
+        t0 = time.perf_counter()
+        pairs = [p for s in seqs for p in pool.seq_swap_out(s)]
+        host_us.append((time.perf_counter() - t0) * 1e6 / S)
+        pt = torch.tensor(pairs, dtype=torch.int32).cuda()
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        e[0].record(stream)
+        pool.swap_blocks(pt, host, 0)
+        e[1].record(stream)
+        pairs = [p for s in seqs for p in pool.seq_swap_in(s)]
+        pt = torch.tensor(pairs, dtype=torch.int32).cuda()
+        e[2].record(stream)
+        pool.swap_blocks(pt, host, 1)
+        e[3].record(stream)
+        torch.cuda.synchronize()
+        out_ms.append(e[0].elapsed_time(e[1]))
+        in_ms.append(e[2].elapsed_time(e[3]))
+    out_ms, in_ms = out_ms[args.warmup:], in_ms[args.warmup:]
+    # parity spot check: decode after the round trips equals decode before
+    q, t, c = U.device_inputs(w, tables=np.asarray(pool.batch_tables(seqs, w.max_blocks_per_seq)[0]), ctx=ctx)
+    out = pool.decode(0, q, t, c, w.max_context_len, w.scale, 0)
+    torch.cuda.synchronize()
+    if not torch.isfinite(out.float()).all():
+        raise RuntimeError("non-finite decode after swap")
+    # reference: DMA copies of the same bytes
+    dev = torch.empty(moved, dtype=torch.uint8, device="cuda")
+    ref = []
+    for direction in (0, 1):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        for k in range(2):
+            ev[0].record(stream)
+            if direction == 0:
+                host.copy_(dev, non_blocking=True)
+            else:
+                dev.copy_(host, non_blocking=True)
+            ev[1].record(stream)
+            torch.cuda.synchronize()
+        ref.append(moved / (ev[0].elapsed_time(ev[1]) * 1e-3) / 1e9)
+    gb_out = moved / (float(np.mean(out_ms)) * 1e-3) / 1e9
+    gb_in = moved / (float(np.mean(in_ms)) * 1e-3) / 1e9
+    res = {
+        "metric": SWAP_METRIC,
+        "value": round(min(gb_out, gb_in), 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(float(np.mean(out_ms)) + float(np.mean(in_ms)), 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": f"swap: llama3_8b batch, {S} sequences, {nblk} blocks of {hbb} B "
+                               f"({moved / 1e9:.2f} GB) out to pinned host memory and back in",
+                   "step": "pa_seq_swap_out x S + pa_swap_blocks(out), pa_seq_swap_in x S + pa_swap_blocks(in)"},
+        "swap_out_gbs": round(gb_out, 2),
+        "swap_in_gbs": round(gb_in, 2),
+        "dma_copy_gbs": {"device_to_host": round(ref[0], 2), "host_to_device": round(ref[1], 2)},
+        "host_block_manager_us_per_sequence": round(float(np.mean(host_us[args.warmup:])), 2),
+        "roofline": {
+            "bound": "host-link",
+            "kernel": "swap_blocks_kernel (one launch per direction)",
+            "achieved": round(min(gb_out, gb_in), 2),
+            "peak": round(min(ref), 2),
+            "unit": "GB/s",
+            "frac": round(min(gb_out, gb_in) / min(ref), 4),
+            "traffic": None,
+            "note": "peak = the DMA-engine copy rate of the same bytes measured in this run",
+        },
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -431,6 +537,8 @@ def main():
         return main_prefill(args)
     if args.workload == "prefix_cache":
         return main_prefix(args)
+    if args.workload == "swap":
+        return main_swap(args)
 
     import torch
     import paged_kv_cache_337_amd as pa

@@ -256,6 +256,51 @@ int pa_seq_append_tokens(pa_pool* pool, int seq, const int32_t* token_ids, int n
 
 int pa_prefix_cache_stats(const pa_pool* pool, pa_prefix_stats* stats);
 
+/* ---- Host tier: swapping sequences out of device memory ("Paged Attention
+ * Explained", "Hybrid Memory Strategies": cached data may move to another
+ * memory tier when GPU memory runs short, at a transfer cost; "PagedAttention:
+ * paging the KV cache like an OS pages memory", "Why an agent should care":
+ * swap/preemption policy).  A host block holds one device block of every
+ * layer: pa_host_block_bytes() bytes, layer-major, each layer's run laid out
+ * as in the pool.  The caller owns the host buffer (pinned host memory, e.g.
+ * torch pin_memory=True) of num_host_blocks such blocks. ---- */
+
+/* Bytes of one host block: L * H_KV * 2 * bs * D * B (0 for NULL). */
+size_t pa_host_block_bytes(const pa_pool* pool);
+
+/* Set up (or resize) the host tier's bookkeeping: host blocks 0 ..
+ * num_host_blocks - 1, all free.  Errors: INVALID_ARG (negative count, or
+ * some sequence is swapped out). */
+int pa_host_tier_init(pa_pool* pool, int num_host_blocks);
+
+/* Swap a resident sequence out: every block of its table, in logical order,
+ * is given a host block, (device, host) pairs go to host pairs_out [2 * n],
+ * and the device blocks are then released as by pa_seq_release (a block that
+ * another sequence shares stays on the device).  Copy the pairs with
+ * pa_swap_blocks(direction 0) on the stream that will next write the pool,
+ * before anything reuses the freed blocks.  The sequence keeps its length;
+ * it cannot be appended to, forked or decoded until swapped in; releasing it
+ * frees its host blocks.  Errors: INVALID_ARG, BUFFER_TOO_SMALL (cap_pairs),
+ * OUT_OF_BLOCKS (host tier full); all-or-nothing. */
+int pa_seq_swap_out(pa_pool* pool, int seq, int32_t* pairs_out, int cap_pairs, int* n_pairs);
+
+/* Swap a sequence back in: fresh device blocks in logical order, (host,
+ * device) pairs to pairs_out, the host blocks freed.  Copy with
+ * pa_swap_blocks(direction 1) before any attention reads the sequence.
+ * Errors: INVALID_ARG (not swapped out), BUFFER_TOO_SMALL, OUT_OF_BLOCKS
+ * (pool full); all-or-nothing. */
+int pa_seq_swap_in(pa_pool* pool, int seq, int32_t* pairs_out, int cap_pairs, int* n_pairs);
+
+/* Copy whole blocks (every layer) between the pool and the host buffer.
+ *   pairs      device int32 [n, 2]: (device, host) for direction 0 (out),
+ *              (host, device) for direction 1 (in); out-of-range ids skipped
+ *   host_buf   pinned host memory, 16-byte aligned, host_bytes long; the
+ *              kernel reads or writes it directly over the host link
+ * Errors: INVALID_ARG (host_buf not pinned host memory, bad direction).
+ * Asynchronous on `stream`. */
+int pa_swap_blocks(pa_pool* pool, const int32_t* pairs, int n, void* host_buf, size_t host_bytes,
+                   int direction, void* stream);
+
 /* Fork: the child shares every block of the parent (counts incremented in
  * logical order) and has the parent's length. */
 int pa_seq_fork(pa_pool* pool, int parent, int* child);

@@ -33,7 +33,8 @@ EXPORTS = [
     "pa_version", "pa_last_error", "pa_pool_required_bytes", "pa_alloc_pool", "pa_free",
     "pa_write_kv", "pa_decode_workspace_bytes", "pa_decode", "pa_prefill", "pa_copy_blocks",
     "pa_seq_create", "pa_seq_append", "pa_prefix_cache_enable", "pa_seq_append_tokens",
-    "pa_prefix_cache_stats", "pa_seq_fork", "pa_seq_release", "pa_seq_block_table",
+    "pa_prefix_cache_stats", "pa_host_block_bytes", "pa_host_tier_init", "pa_seq_swap_out",
+    "pa_seq_swap_in", "pa_swap_blocks", "pa_seq_fork", "pa_seq_release", "pa_seq_block_table",
     "pa_batch_tables", "pa_pool_state", "pa_pool_stats", "pa_slots_for_positions",
 ]
 
@@ -87,6 +88,11 @@ def _load():
         "pa_prefix_cache_enable": (c_int, [vp, c_int]),
         "pa_seq_append_tokens": (c_int, [vp, c_int, i32p, c_int, i32p, i32p, intp, intp]),
         "pa_prefix_cache_stats": (c_int, [vp, ctypes.POINTER(PrefixStats)]),
+        "pa_host_block_bytes": (c_sz, [vp]),
+        "pa_host_tier_init": (c_int, [vp, c_int]),
+        "pa_seq_swap_out": (c_int, [vp, c_int, i32p, c_int, intp]),
+        "pa_seq_swap_in": (c_int, [vp, c_int, i32p, c_int, intp]),
+        "pa_swap_blocks": (c_int, [vp, vp, c_int, vp, c_sz, c_int, vp]),
         "pa_seq_fork": (c_int, [vp, c_int, intp]),
         "pa_seq_release": (c_int, [vp, c_int]),
         "pa_seq_block_table": (c_int, [vp, c_int, i32p, c_int, intp, intp]),
@@ -272,6 +278,34 @@ class Pool:
         s = PrefixStats()
         _check(lib.pa_prefix_cache_stats(self.handle, ctypes.byref(s)), "pa_prefix_cache_stats")
         return {n: int(getattr(s, n)) for n, _ in PrefixStats._fields_}
+
+    # -- host tier ------------------------------------------------------
+    @property
+    def host_block_bytes(self) -> int:
+        return int(lib.pa_host_block_bytes(self.handle))
+
+    def host_tier_init(self, num_host_blocks: int):
+        _check(lib.pa_host_tier_init(self.handle, num_host_blocks), "pa_host_tier_init")
+
+    def _swap(self, fn, name, seq):
+        buf = np.empty(2 * max(self.N, 1), dtype=np.int32)
+        n = ctypes.c_int()
+        _check(fn(self.handle, seq, _i32(buf), self.N, ctypes.byref(n)), name)
+        return [(int(buf[2 * i]), int(buf[2 * i + 1])) for i in range(n.value)]
+
+    def seq_swap_out(self, seq: int):
+        """(device, host) block pairs to copy out."""
+        return self._swap(lib.pa_seq_swap_out, "pa_seq_swap_out", seq)
+
+    def seq_swap_in(self, seq: int):
+        """(host, device) block pairs to copy in."""
+        return self._swap(lib.pa_seq_swap_in, "pa_seq_swap_in", seq)
+
+    def swap_blocks(self, pairs: torch.Tensor, host_buf: torch.Tensor, direction: int, stream=None):
+        self._need_device()
+        _check(lib.pa_swap_blocks(self.handle, _ptr(pairs), int(pairs.shape[0]), _ptr(host_buf),
+                                  host_buf.numel() * host_buf.element_size(), int(direction), _stream(stream)),
+               "pa_swap_blocks")
 
     def seq_fork(self, parent: int) -> int:
         c = ctypes.c_int()

@@ -94,10 +94,7 @@ AllocResult BlockAllocator::append_impl(int32_t seq, int32_t n_tokens, const int
                                         int* n_cached, std::string* err) {
   if (n_cow) *n_cow = 0;
   if (n_cached) *n_cached = 0;
-  if (!live(seq)) {
-    *err = "unknown or released sequence";
-    return AllocResult::InvalidArg;
-  }
+  if (!resident(seq, err)) return AllocResult::InvalidArg;
   if (n_tokens < 0) {
     *err = "token count cannot be negative";
     return AllocResult::InvalidArg;
@@ -216,11 +213,20 @@ void BlockAllocator::enable_prefix_cache(bool on) {
   }
 }
 
-AllocResult BlockAllocator::fork(int32_t parent, int32_t* child, std::string* err) {
-  if (!live(parent)) {
-    *err = "unknown or released parent sequence";
-    return AllocResult::InvalidArg;
+bool BlockAllocator::resident(int32_t seq, std::string* err) const {
+  if (!live(seq)) {
+    *err = "unknown or released sequence";
+    return false;
   }
+  if (seqs_[seq].swapped) {
+    *err = "sequence is swapped out";
+    return false;
+  }
+  return true;
+}
+
+AllocResult BlockAllocator::fork(int32_t parent, int32_t* child, std::string* err) {
+  if (!resident(parent, err)) return AllocResult::InvalidArg;
   for (int32_t b : seqs_[parent].table) inc_ref(b);
   Seq c;
   c.table = seqs_[parent].table;
@@ -241,14 +247,13 @@ AllocResult BlockAllocator::release(int32_t seq, std::string* err) {
     return AllocResult::InvalidArg;
   }
   Seq& s = seqs_[seq];
-  for (int32_t b : s.table) {
-    if (dec_ref(b) == 0) {
-      if (cache_on_ && serial_[b] != 0) {
-        stack_.insert(stack_.begin(), b);  // cached: reused last
-      } else {
-        stack_.push_back(b);
-      }
-    }
+  if (s.swapped) {
+    for (int32_t hb : s.host) host_stack_.push_back(hb);
+    s.host.clear();
+    s.host.shrink_to_fit();
+    s.swapped = false;
+  } else {
+    free_device(s);
   }
   s.table.clear();
   s.table.shrink_to_fit();
@@ -260,17 +265,97 @@ AllocResult BlockAllocator::release(int32_t seq, std::string* err) {
   return AllocResult::Ok;
 }
 
+void BlockAllocator::free_device(Seq& s) {
+  for (int32_t b : s.table) {
+    if (dec_ref(b) == 0) {
+      if (cache_on_ && serial_[b] != 0) {
+        stack_.insert(stack_.begin(), b);  // cached: reused last
+      } else {
+        stack_.push_back(b);
+      }
+    }
+  }
+}
+
+AllocResult BlockAllocator::host_tier(int32_t num_host_blocks, std::string* err) {
+  if (num_host_blocks < 0) {
+    *err = "negative host block count";
+    return AllocResult::InvalidArg;
+  }
+  for (const Seq& s : seqs_) {
+    if (s.alive && s.swapped) {
+      *err = "sequences are swapped out";
+      return AllocResult::InvalidArg;
+    }
+  }
+  host_n_ = num_host_blocks;
+  host_stack_.clear();
+  for (int32_t i = num_host_blocks - 1; i >= 0; --i) host_stack_.push_back(i);
+  return AllocResult::Ok;
+}
+
+AllocResult BlockAllocator::swap_out(int32_t seq, std::vector<int32_t>* pairs, std::string* err) {
+  if (!resident(seq, err)) return AllocResult::InvalidArg;
+  Seq& s = seqs_[seq];
+  if (s.table.size() > host_stack_.size()) {
+    *err = "host tier exhausted";
+    return AllocResult::OutOfBlocks;
+  }
+  pairs->clear();
+  s.host.clear();
+  for (int32_t b : s.table) {
+    const int32_t hb = host_stack_.back();
+    host_stack_.pop_back();
+    pairs->push_back(b);
+    pairs->push_back(hb);
+    s.host.push_back(hb);
+  }
+  free_device(s);
+  s.table.clear();
+  s.swapped = true;
+  return AllocResult::Ok;
+}
+
+AllocResult BlockAllocator::swap_in(int32_t seq, std::vector<int32_t>* pairs, std::string* err) {
+  if (!live(seq)) {
+    *err = "unknown or released sequence";
+    return AllocResult::InvalidArg;
+  }
+  Seq& s = seqs_[seq];
+  if (!s.swapped) {
+    *err = "sequence is not swapped out";
+    return AllocResult::InvalidArg;
+  }
+  if (s.host.size() > stack_.size()) {
+    *err = "pool exhausted";
+    return AllocResult::OutOfBlocks;
+  }
+  pairs->clear();
+  s.table.clear();
+  for (int32_t hb : s.host) {
+    const int32_t b = pop_fresh();
+    ref_[b] = 1;
+    s.table.push_back(b);
+    pairs->push_back(hb);
+    pairs->push_back(b);
+  }
+  for (int32_t hb : s.host) host_stack_.push_back(hb);
+  s.host.clear();
+  s.swapped = false;
+  return AllocResult::Ok;
+}
+
 int64_t BlockAllocator::logical_tokens() const {
   int64_t t = 0;
   for (const Seq& s : seqs_)
-    if (s.alive) t += s.length;
+    if (s.alive && !s.swapped) t += s.length;
   return t;
 }
 
 int64_t BlockAllocator::tail_slots() const {
   int64_t t = 0;
   for (const Seq& s : seqs_)
-    if (s.alive) t += static_cast<int64_t>(s.table.size()) * bs_ - s.length;
+    if (s.alive && !s.swapped) t += static_cast<int64_t>(s.table.size()) * bs_ - s.length;
   return t;
 }
 

@@ -25,6 +25,15 @@
 // registered blocks freed to count 0 go to the bottom of the free stack, so
 // uncached blocks are reused first and cached ones least recently freed
 // first.  An append without ids ends the sequence's chain; fork copies it.
+//
+// Host tier ("Paged Attention Explained", "Hybrid Memory Strategies"): host
+// blocks each hold one device block of every layer; their free blocks form a
+// LIFO stack (initially ascending ids).  swap_out gives each block of the
+// sequence's table, in logical order, the top host block and then releases
+// the device blocks as release would (a block shared with another sequence
+// stays on the device); swap_in takes fresh device blocks in logical order
+// and returns the host blocks in logical order.  A swapped sequence keeps its
+// length and prefix-cache chain; it cannot grow or be forked until swapped in.
 #pragma once
 
 #include <cstdint>
@@ -51,6 +60,14 @@ class BlockAllocator {
   AllocResult append_tokens(int32_t seq, const int32_t* ids, int32_t n_tokens, int32_t* slots_out,
                             int32_t* cow_pair, int* n_cow, int* n_cached, std::string* err);
   void enable_prefix_cache(bool on);
+  AllocResult host_tier(int32_t num_host_blocks, std::string* err);
+  // pairs: (device, host) for swap_out, (host, device) for swap_in, [2 * n].
+  AllocResult swap_out(int32_t seq, std::vector<int32_t>* pairs, std::string* err);
+  AllocResult swap_in(int32_t seq, std::vector<int32_t>* pairs, std::string* err);
+  bool swapped(int32_t seq) const { return live(seq) && seqs_[seq].swapped; }
+  const std::vector<int32_t>& host_table(int32_t seq) const { return seqs_[seq].host; }
+  int32_t host_blocks() const { return host_n_; }
+  const std::vector<int32_t>& host_free_stack() const { return host_stack_; }
   bool prefix_cache_enabled() const { return cache_on_; }
   struct CacheCounts {
     int64_t registered = 0, hit_blocks = 0, evicted = 0, lookups = 0;
@@ -82,6 +99,8 @@ class BlockAllocator {
     bool chain = true;          // every token id so far is known
     int64_t parent = 0;         // cache serial of the last full block
     std::vector<int32_t> tail;  // ids of the partially filled last block
+    bool swapped = false;
+    std::vector<int32_t> host;  // host blocks while swapped out
   };
   struct Key {
     int64_t parent;
@@ -94,6 +113,8 @@ class BlockAllocator {
   AllocResult append_impl(int32_t seq, int32_t n_tokens, const int32_t* ids, int32_t* slots_out,
                           int32_t* cow_pair, int* n_cow, int* n_cached, std::string* err);
   int32_t pop_fresh();
+  void free_device(Seq& s);
+  bool resident(int32_t seq, std::string* err) const;
   void inc_ref(int32_t b);
   int32_t dec_ref(int32_t b);  // returns the new count
 
@@ -111,6 +132,9 @@ class BlockAllocator {
   std::vector<Key> key_of_;       // per block, valid when registered
   int64_t next_serial_ = 1;
   CacheCounts counts_;
+  // host tier
+  int32_t host_n_ = 0;
+  std::vector<int32_t> host_stack_;  // top = back()
 };
 
 }  // namespace pa

@@ -380,6 +380,73 @@ int pa_copy_blocks(pa_pool* pool, const int32_t* pairs, int n, void* stream) {
   });
 }
 
+size_t pa_host_block_bytes(const pa_pool* pool) {
+  if (!pool) return 0;
+  const pa_pool_desc& d = pool->desc;
+  return static_cast<size_t>(d.num_layers) * d.num_kv_heads * 2 * static_cast<size_t>(d.block_size) * d.head_dim *
+         elem_bytes(d.dtype);
+}
+
+int pa_host_tier_init(pa_pool* pool, int num_host_blocks) {
+  return guarded([&]() -> int {
+    if (!pool) return fail(PA_ERR_INVALID_ARG, "pool is NULL");
+    std::string err;
+    return alloc_status(pool->alloc.host_tier(num_host_blocks, &err), err);
+  });
+}
+
+namespace {
+int swap_seq(pa_pool* pool, int seq, int32_t* pairs_out, int cap_pairs, int* n_pairs, bool out) {
+  if (!pool || !n_pairs) return fail(PA_ERR_INVALID_ARG, "NULL argument");
+  *n_pairs = 0;
+  auto& a = pool->alloc;
+  if (!a.live(seq)) return fail(PA_ERR_INVALID_ARG, "unknown or released sequence");
+  const size_t need = out ? (a.swapped(seq) ? 0 : a.table(seq).size()) : a.host_table(seq).size();
+  if (static_cast<int64_t>(need) > cap_pairs) return fail(PA_ERR_BUFFER_TOO_SMALL, "pair capacity too small");
+  if (need > 0 && !pairs_out) return fail(PA_ERR_INVALID_ARG, "pairs_out is NULL");
+  std::vector<int32_t> pairs;
+  std::string err;
+  const pa::AllocResult r = out ? a.swap_out(seq, &pairs, &err) : a.swap_in(seq, &pairs, &err);
+  if (r != pa::AllocResult::Ok) return alloc_status(r, err);
+  std::copy(pairs.begin(), pairs.end(), pairs_out);
+  *n_pairs = static_cast<int>(pairs.size() / 2);
+  return PA_OK;
+}
+}  // namespace
+
+int pa_seq_swap_out(pa_pool* pool, int seq, int32_t* pairs_out, int cap_pairs, int* n_pairs) {
+  return guarded([&]() -> int { return swap_seq(pool, seq, pairs_out, cap_pairs, n_pairs, true); });
+}
+
+int pa_seq_swap_in(pa_pool* pool, int seq, int32_t* pairs_out, int cap_pairs, int* n_pairs) {
+  return guarded([&]() -> int { return swap_seq(pool, seq, pairs_out, cap_pairs, n_pairs, false); });
+}
+
+int pa_swap_blocks(pa_pool* pool, const int32_t* pairs, int n, void* host_buf, size_t host_bytes, int direction,
+                   void* stream) {
+  return guarded([&]() -> int {
+    if (!pool) return fail(PA_ERR_INVALID_ARG, "pool is NULL");
+    if (n < 0) return fail(PA_ERR_INVALID_ARG, "pair count cannot be negative");
+    if (direction != 0 && direction != 1) return fail(PA_ERR_INVALID_ARG, "direction must be 0 (out) or 1 (in)");
+    if (n == 0) return PA_OK;
+    if (!pairs || !host_buf) return fail(PA_ERR_INVALID_ARG, "NULL pointer");
+    if (reinterpret_cast<uintptr_t>(host_buf) & 15u) return fail(PA_ERR_INVALID_ARG, "host buffer must be 16-byte aligned");
+    // The kernel reads and writes the host buffer directly: it must be pinned
+    // host memory the device can address.
+    void* dev_view = nullptr;
+    hipError_t e = hipHostGetDevicePointer(&dev_view, host_buf, 0);
+    if (e != hipSuccess || !dev_view) {
+      (void)hipGetLastError();
+      return fail(PA_ERR_INVALID_ARG, "host buffer is not pinned host memory");
+    }
+    const size_t hbb = pa_host_block_bytes(pool);
+    const int64_t host_blocks = static_cast<int64_t>(host_bytes / hbb);
+    e = pa::launch_swap_blocks(geom_of(pool), pairs, n, dev_view, host_blocks, direction,
+                               static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? PA_OK : hip_fail(e, "swap_blocks launch");
+  });
+}
+
 int pa_seq_create(pa_pool* pool, int* seq) {
   return guarded([&]() -> int {
     if (!pool || !seq) return fail(PA_ERR_INVALID_ARG, "NULL argument");
@@ -468,6 +535,7 @@ int pa_batch_tables(const pa_pool* pool, const int* seqs, int num_seqs, int max_
     if (num_seqs < 0 || max_blocks < 0) return fail(PA_ERR_INVALID_ARG, "negative size");
     for (int i = 0; i < num_seqs; ++i) {
       if (!pool->alloc.live(seqs[i])) return fail(PA_ERR_INVALID_ARG, "unknown or released sequence");
+      if (pool->alloc.swapped(seqs[i])) return fail(PA_ERR_INVALID_ARG, "sequence is swapped out");
       if (static_cast<int>(pool->alloc.table(seqs[i]).size()) > max_blocks)
         return fail(PA_ERR_BUFFER_TOO_SMALL, "max_blocks too small");
     }

@@ -132,4 +132,36 @@ hipError_t launch_copy_blocks(const PoolGeom& g, const int32_t* pairs, int n, hi
   return hipGetLastError();
 }
 
+// Swap copies between the pool and a host tier.  grid.x = pair index,
+// grid.y = layer.  A device block of one layer is one contiguous run of
+// H * 2 * bs * D elements; a host block holds the runs of every layer side
+// by side.  dir 0 copies (device, host) pairs out, dir 1 (host, device) pairs
+// in.  Pairs with an id out of range are skipped.
+__global__ __launch_bounds__(256) void swap_blocks_kernel(char* __restrict__ pool, char* __restrict__ host,
+                                                          const int32_t* __restrict__ pairs, int N, int64_t host_n,
+                                                          size_t block_bytes, size_t layer_bytes, int L, int dir) {
+  const int32_t a = pairs[2 * blockIdx.x], b = pairs[2 * blockIdx.x + 1];
+  const int32_t dev = dir == 0 ? a : b;
+  const int32_t hb = dir == 0 ? b : a;
+  if (dev < 0 || dev >= N || hb < 0 || hb >= host_n) return;
+  const size_t l = blockIdx.y;
+  uint4* d = reinterpret_cast<uint4*>(pool + l * layer_bytes + static_cast<size_t>(dev) * block_bytes);
+  uint4* h = reinterpret_cast<uint4*>(host + (static_cast<size_t>(hb) * L + l) * block_bytes);
+  const uint4* src = dir == 0 ? d : h;
+  uint4* dst = dir == 0 ? h : d;
+  const size_t n16 = block_bytes / 16;
+  for (size_t i = threadIdx.x; i < n16; i += blockDim.x) dst[i] = src[i];
+}
+
+hipError_t launch_swap_blocks(const PoolGeom& g, const int32_t* pairs, int n, void* host, int64_t host_blocks,
+                              int dir, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  if (g.L > 65535) return hipErrorInvalidValue;
+  const size_t block_bytes = static_cast<size_t>(g.H) * 2 * g.bs * g.D * g.elem_bytes;
+  hipLaunchKernelGGL(swap_blocks_kernel, dim3(n, g.L), dim3(256), 0, stream, static_cast<char*>(g.base),
+                     static_cast<char*>(host), pairs, g.N, host_blocks, block_bytes, g.layer_elems() * g.elem_bytes,
+                     g.L, dir);
+  return hipGetLastError();
+}
+
 }  // namespace pa

@@ -78,6 +78,11 @@ hipError_t launch_write_kv(const PoolGeom& g, int layer, const void* k, const vo
 
 hipError_t launch_copy_blocks(const PoolGeom& g, const int32_t* pairs, int n, hipStream_t stream);
 
+// Whole-block copies between the pool and a host tier (host: device-usable
+// address of pinned host memory holding host_blocks blocks of every layer).
+hipError_t launch_swap_blocks(const PoolGeom& g, const int32_t* pairs, int n, void* host, int64_t host_blocks,
+                              int dir, hipStream_t stream);
+
 // Returns hipErrorInvalidValue when no kernel variant covers (dtype, D, G).
 hipError_t launch_decode(const DecodeParams& p, int dtype, int D, hipStream_t stream);
 
