@@ -52,6 +52,7 @@ constexpr float kRescaleLog2P = 8.0f;
 #define PA_PREFILL_PREFETCH 1
 #endif
 constexpr int kTilesPerWave = PA_PREFILL_TILES;
+
 constexpr int kPrefillPrefetch = PA_PREFILL_PREFETCH;
 
 __device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
@@ -281,7 +282,7 @@ __device__ __forceinline__ uint4 zero_v_tail(uint4 x, int grp, int valid) {
 
 template <typename T, int D, int NW, int NB, int NP>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4))) void prefill_lds_kernel(
-    PrefillParams p) {
+    PrefillParams p, const int32_t* __restrict__ tables) {
   static_assert(T::kBytes == 2, "16-bit pools only");
   constexpr int NCH = D / 32;  // 1 KiB chunks per sub-tile
   constexpr int NT = D / 16;
@@ -359,10 +360,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
   const int unit = sub >> 1;
   const bool is_v = sub & 1;
   const int c0 = (wave * kLoads) % NCH;
-  const int32_t* trow = p.tables + static_cast<size_t>(i) * p.max_blocks;
-  UnitStream<D, 2> us;
-  us.begin(p, trow, 0, 0, h);
-  us.ids = us.fetch_ids(lane);
+  // The table row is read with scalar loads (a __restrict__ argument), so
+  // that locating a unit never waits on the vector loads in flight.
+  const int32_t* trow = tables + static_cast<size_t>(i) * p.max_blocks;
+  const char* layer_base = static_cast<const char*>(p.pool) + p.layer_off * 2;
   uint4 stg[kLoads];  // this wave's loads of the next stage
   int valid_st;       // tokens of this wave's unit to keep (0 for an invalid block)
 
@@ -372,15 +373,11 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
   // Locate this wave's unit of stage s (stages are issued in order) and
   // issue its loads.
   auto issue = [&](int s, uint4 (&r)[kLoads], int& valid) {
-    if (my_lb - us.lb_base >= 64) {
-      us.lb_base = my_lb;
-      us.ids = us.fetch_ids(lane);
-    }
-    us.lb = my_lb;
-    us.sub = my_sub;
-    const char *kp, *vp;
-    const bool ok = us.locate(kp, vp);
-    const char* src = is_v ? vp : kp;
+    const int32_t bid = my_lb < p.max_blocks ? trow[my_lb] : -1;
+    const bool ok = bid >= 0 && bid < p.N;
+    const size_t region = (static_cast<size_t>(ok ? bid : 0) * p.H + h) * (2 * static_cast<size_t>(p.bs) * D);
+    const char* src = layer_base + (region + (is_v ? static_cast<size_t>(p.bs) * D : 0) +
+                                    static_cast<size_t>(my_sub) * 16 * D) * 2;
     my_sub += kUnits;
     while (my_sub >= subs) {
       my_sub -= subs;
@@ -491,11 +488,11 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
   // Pipeline: the loads of stage s + 1 are in flight in registers while
   // stage s is computed from LDS; they are written to the other buffer after
   // it, and one barrier per stage publishes them.
+  // Stages below this wave's first row need no mask.
+  const int kfull = active ? qmin[0] - kKeys + 1 : -1;
   issue(0, stg, valid_st);
   to_lds(stg, valid_st, 0);
   __syncthreads();
-  // Stages below this wave's first row need no mask.
-  const int kfull = active ? qmin[0] - kKeys + 1 : -1;
   for (int s = 0; s < nst; ++s) {
     if (s + 1 < nst) issue(s + 1, stg, valid_st);
     const int key0 = s * kKeys;
@@ -553,7 +550,7 @@ hipError_t launch_prefill_typed(const PrefillParams& p, hipStream_t stream) {
     const int64_t wgs = 8 * pairs8 * tiles;
     if (wgs > INT32_MAX) return hipErrorInvalidValue;
     hipLaunchKernelGGL((prefill_lds_kernel<T, D, kLdsWaves, kLdsTiles, kLdsPairs>), dim3(static_cast<unsigned>(wgs)),
-                       dim3(64 * kLdsWaves), 0, stream, q);
+                       dim3(64 * kLdsWaves), 0, stream, q, p.tables);
   } else {
     hipLaunchKernelGGL((prefill_kernel<T, D, kTilesPerWave, kPrefillPrefetch>), grid, dim3(kPrefillThreads), 0,
                        stream, p);
