@@ -69,6 +69,7 @@ constexpr int kWaves = 4;  // waves of a decode workgroup, sharing one work item
 constexpr int kThreads = 64 * kWaves;
 constexpr int kMergeWaves = 4;
 constexpr int kMergeThreads = 64 * kMergeWaves;
+constexpr int kWideMergeParts = 16;  // from this many partitions, a workgroup merges one row
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kRescaleLog2 = 8.0f;  // raise the reference only past 2^8
 constexpr int kPlanThreads = 1024;
@@ -214,6 +215,9 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeParams p) {
   __shared__ int wsum[kPlanThreads / 64];
   __shared__ long long wtok[kPlanThreads / 64];
   __shared__ int sP;
+  __shared__ int4 longs[kPlanThreads];  // (sequence, first item, full items, context)
+  __shared__ int long_np[kPlanThreads];
+  __shared__ int nlong;
   constexpr int kCached = 4;  // context lengths kept in registers per thread
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int cc[kCached];
@@ -283,15 +287,40 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeParams p) {
     p.header[2] = P;
   }
   __syncthreads();
-  for (int k = 0, i = threadIdx.x; i < p.S; ++k, i += kPlanThreads) {
-    const int c = ctx_of(k, i);
-    const int nfull = c / P, rem = c - nfull * P;
-    const int np = nfull + (rem > 0 || c == 0 ? 1 : 0);
-    if (nfull > 0) {
-      const int base = atomicAdd(&off[bin_of(P)], nfull);
-      for (int j = 0; j < nfull; ++j) p.items[base + j] = make_int4(i, j, c, np);
+  // Each thread writes its sequence's first kDirect full items and its
+  // partial one; the further full items of long sequences are written by the
+  // whole workgroup, so that a few long contexts do not serialise the plan.
+  constexpr int kDirect = 4;
+  const int rounds = (p.S + kPlanThreads - 1) / kPlanThreads;
+  for (int k = 0; k < rounds; ++k) {
+    const int i = threadIdx.x + k * kPlanThreads;
+    if (threadIdx.x == 0) nlong = 0;
+    __syncthreads();
+    if (i < p.S) {
+      const int c = ctx_of(k, i);
+      const int nfull = c / P, rem = c - nfull * P;
+      const int np = nfull + (rem > 0 || c == 0 ? 1 : 0);
+      if (nfull > 0) {
+        const int base = atomicAdd(&off[bin_of(P)], nfull);
+        const int direct = nfull < kDirect ? nfull : kDirect;
+        for (int j = 0; j < direct; ++j) p.items[base + j] = make_int4(i, j, c, np);
+        if (nfull > kDirect) {
+          const int e = atomicAdd(&nlong, 1);
+          longs[e] = make_int4(i, base, nfull, c);
+          long_np[e] = np;
+        }
+      }
+      if (rem > 0 || c == 0) p.items[atomicAdd(&off[bin_of(rem)], 1)] = make_int4(i, nfull, c, np);
     }
-    if (rem > 0 || c == 0) p.items[atomicAdd(&off[bin_of(rem)], 1)] = make_int4(i, nfull, c, np);
+    __syncthreads();
+    const int nl = nlong;
+    for (int e = 0; e < nl; ++e) {
+      const int4 L = longs[e];
+      const int np = long_np[e];
+      for (int j = kDirect + static_cast<int>(threadIdx.x); j < L.z; j += kPlanThreads)
+        p.items[L.y + j] = make_int4(L.x, j, L.w, np);
+    }
+    __syncthreads();
   }
 }
 
@@ -745,6 +774,101 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(DecodeParams p) {
     out[static_cast<size_t>(pair) * D + lane + 64 * k] = static_cast<B>(to_storage<T>(acc[k] * inv));
 }
 
+// Merge for contexts of many partitions: a workgroup of four waves per
+// (sequence, query head).  Wave w merges a contiguous quarter of the
+// partitions against its own maximum, loading eight partitions' rows at a
+// time (D / 64 consecutive floats per lane); the four results are then
+// combined through LDS with the same log-sum-exp weights.
+template <typename T, int D>
+__global__ __launch_bounds__(kMergeThreads) void merge_wide_kernel(DecodeParams p) {
+  constexpr int VEC = D / 64;  // consecutive head_dim entries per lane
+  __shared__ float s_m[kMergeWaves], s_l[kMergeWaves];
+  __shared__ float s_o[kMergeWaves][D];
+  const int lane = threadIdx.x & 63;
+  const int wave = rfl(threadIdx.x >> 6);
+  const int pair = blockIdx.x;
+  const int P = rfl(p.header[2]);
+  const int ctx = rfl(clamp_ctx(p, pair / p.Hq));
+  if (ctx <= P) return;  // written directly by the partition kernel
+  int np = (ctx + P - 1) / P;
+  np = np > p.max_parts ? p.max_parts : np;
+  const int per = (np + kMergeWaves - 1) / kMergeWaves;
+  const int j0 = wave * per;
+  const int j1 = j0 + per < np ? j0 + per : np;
+  const size_t e0 = static_cast<size_t>(pair) * p.max_parts;
+  const float* ml = p.ws_ml + 2 * e0;
+
+  float M = kNegInf;
+  for (int c0 = j0; c0 < j1; c0 += 64)
+    if (c0 + lane < j1) M = fmaxf(M, ml[2 * (c0 + lane)]);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+  float acc[VEC];
+#pragma unroll
+  for (int k = 0; k < VEC; ++k) acc[k] = 0.f;
+  float L = 0.f;
+  for (int c0 = j0; c0 < j1; c0 += 64) {
+    const int jj = c0 + lane;
+    const float mj = jj < j1 ? ml[2 * jj] : kNegInf;
+    const float wj = (mj == kNegInf) ? 0.f : ml[2 * jj + 1] * fast_exp2(mj - M);
+    L += wj;
+    const int n = j1 - c0 < 64 ? j1 - c0 : 64;
+    for (int t = 0; t < n; t += 8) {
+      float o[8][VEC];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int r = t + u < n ? t + u : n - 1;
+        const float* src = p.ws_o + (e0 + c0 + r) * D + VEC * lane;
+        if constexpr (VEC == 2) {
+          const float2 x = *reinterpret_cast<const float2*>(src);
+          o[u][0] = x.x;
+          o[u][1] = x.y;
+        } else {
+#pragma unroll
+          for (int k = 0; k < VEC; ++k) o[u][k] = src[k];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const float w = t + u < n ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(
+                                                         __builtin_bit_cast(int, wj), t + u))
+                                  : 0.f;
+#pragma unroll
+        for (int k = 0; k < VEC; ++k) acc[k] = fmaf(w, o[u][k], acc[k]);
+      }
+    }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) L += __shfl_xor(L, o);
+  if (lane == 0) {
+    s_m[wave] = M;
+    s_l[wave] = L;
+  }
+#pragma unroll
+  for (int k = 0; k < VEC; ++k) s_o[wave][VEC * lane + k] = acc[k];
+  __syncthreads();
+  if (wave != 0) return;
+  float Mt = s_m[0];
+#pragma unroll
+  for (int w = 1; w < kMergeWaves; ++w) Mt = fmaxf(Mt, s_m[w]);
+  float Lt = 0.f, o[VEC];
+#pragma unroll
+  for (int k = 0; k < VEC; ++k) o[k] = 0.f;
+#pragma unroll
+  for (int w = 0; w < kMergeWaves; ++w) {
+    const float f = s_m[w] == kNegInf ? 0.f : fast_exp2(s_m[w] - Mt);
+    Lt += f * s_l[w];
+#pragma unroll
+    for (int k = 0; k < VEC; ++k) o[k] += f * s_o[w][VEC * lane + k];
+  }
+  using B = typename T::bits;
+  B* out = static_cast<B*>(p.out);
+  const float inv = (Lt > 0.f) ? 1.f / Lt : 0.f;
+#pragma unroll
+  for (int k = 0; k < VEC; ++k)
+    out[static_cast<size_t>(pair) * D + VEC * lane + k] = static_cast<B>(to_storage<T>(o[k] * inv));
+}
+
 // Persistent grid: kWorkgroupsPerCU workgroups per CU (never more than the
 // kernel's occupancy allows), cached per device.
 int persistent_grid(const void* kernel) {
@@ -816,6 +940,10 @@ hipError_t launch_typed(const DecodeParams& p, hipStream_t stream) {
   }
   if (e != hipSuccess || p.max_parts <= 1) return e;
   const int pairs = p.S * p.Hq;
+  if (!p.auto_partition && p.max_parts >= kWideMergeParts) {
+    hipLaunchKernelGGL((merge_wide_kernel<T, D>), dim3(pairs), dim3(kMergeThreads), 0, stream, p);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL((merge_kernel<T, D>), dim3((pairs + kMergeWaves - 1) / kMergeWaves), dim3(kMergeThreads),
                      0, stream, p);
   return hipGetLastError();
