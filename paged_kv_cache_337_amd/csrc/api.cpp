@@ -72,12 +72,11 @@ pa::PoolGeom geom_of(const pa_pool* p) {
   return g;
 }
 
+// Read on every call (a getenv is far cheaper than any launch), so a process
+// can switch validation on and off.
 bool debug_enabled() {
-  static const bool on = [] {
-    const char* s = std::getenv("PA_DEBUG");
-    return s && *s && std::strcmp(s, "0") != 0;
-  }();
-  return on;
+  const char* s = std::getenv("PA_DEBUG");
+  return s && *s && std::strcmp(s, "0") != 0;
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
