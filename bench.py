@@ -613,7 +613,31 @@ def main():
 
     ms_per_step = wall * 1e3 / args.steps
     ev_ms = e_all[0].elapsed_time(e_all[1]) / args.steps
-    dec_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    call_ms = [a.elapsed_time(b) for a, b in evs]
+    dec_ms = float(np.mean(call_ms))
+
+    # Warm calls: the same layer again and again (no rotation), so whatever
+    # the Infinity Cache keeps between calls is found there.
+    warm = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(20)]
+    for a, b in warm:
+        a.record(stream)
+        pool.decode(0, q, tables, ctx, max_ctx, w.scale, P, out=out, workspace=ws)
+        b.record(stream)
+    torch.cuda.synchronize()
+    warm_ms = float(np.median([a.elapsed_time(b) for a, b in warm]))
+
+    # Read probe over the pool buffer: every 8 KiB chunk once, in a seeded
+    # random order (the decode kernel's access granularity, no arithmetic).
+    nchunks = pool.nbytes // 8192
+    order = torch.from_numpy(np.random.default_rng(0).permutation(nchunks).astype(np.int32)).cuda()
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    pev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(4)]
+    for a, b in pev:
+        a.record(stream)
+        pa.probe_read_chunks(pool.buf, order, sink)
+        b.record(stream)
+    torch.cuda.synchronize()
+    probe_gbs = nchunks * 8192 / (float(np.median([a.elapsed_time(b) for a, b in pev[1:]])) * 1e-3) / 1e9
     tok_bytes = 2 * w.num_kv_heads * w.head_dim * eb
     kv_bytes = int(host_ctx.astype(np.int64).sum()) * tok_bytes
     nblk = int(sum(-(-int(c) // w.block_size) for c in host_ctx))
@@ -667,6 +691,11 @@ def main():
                         if P == w.partition_tokens and L == 4 and not args.contiguous else None),
             "alg_bytes_per_launch": alg_bytes,
             "avg_launch_ms": round(dec_ms, 5),
+            "median_launch_ms": round(float(np.median(call_ms)), 5),
+            "warm_median_launch_ms": round(warm_ms, 5),
+            "warm_achieved": round(alg_bytes / (warm_ms * 1e-3) / 1e9, 2),
+            "probe_read_gbs": round(probe_gbs, 2),
+            "frac_of_probe": round(achieved / probe_gbs, 4),
         },
     }
     if args.copy_calib_blocks > 0:
@@ -679,6 +708,13 @@ def main():
         res["copy_calibration_bytes"] = nbytes
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_budget_s, host_tables, host_ctx)
+        try:
+            from threadpoolctl import threadpool_limits
+            with threadpool_limits(1):
+                one = cpu_baseline(w, max(args.cpu_budget_s / 4, 1.0), host_tables, host_ctx)
+            res["cpu_baseline"]["one_thread"] = {"value": one["value"], "sample": one["sample"]}
+        except ImportError:  # pragma: no cover
+            pass
     print(json.dumps(res), flush=True)
 
 

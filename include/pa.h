@@ -325,6 +325,16 @@ int pa_pool_state(const pa_pool* pool, int32_t* refcounts, int32_t* free_stack, 
 
 int pa_pool_stats(const pa_pool* pool, pa_stats* stats);
 
+/* Measurement helper (no part of the method): read num_chunks 8 KiB chunks of
+ * device buffer buf (buf_bytes long, 16-byte aligned) in the order of
+ * chunk_ids (device int32 [num_chunks]; ids outside the buffer read chunk 0)
+ * with the decode kernel's 16-byte streaming loads and launch shape of two
+ * workgroups per CU, writing at most one word to sink (device, 4 bytes) so
+ * the reads are kept.  Bracket it with events to get the HBM read rate paged
+ * 8 KiB runs can reach, the practical ceiling for pa_decode.  Asynchronous. */
+int pa_probe_read_chunks(const void* buf, size_t buf_bytes, const int32_t* chunk_ids, int num_chunks,
+                         void* sink, void* stream);
+
 /* Host helper: global slot numbers for positions [pos_begin, pos_begin +
  * n_tokens) of every sequence of a batch, written sequence-major into host
  * `slots_out`.  tables: host int32 [num_seqs, max_blocks]; pos_begin and

@@ -35,7 +35,7 @@ EXPORTS = [
     "pa_seq_create", "pa_seq_append", "pa_prefix_cache_enable", "pa_seq_append_tokens",
     "pa_prefix_cache_stats", "pa_host_block_bytes", "pa_host_tier_init", "pa_seq_swap_out",
     "pa_seq_swap_in", "pa_swap_blocks", "pa_seq_fork", "pa_seq_release", "pa_seq_block_table",
-    "pa_batch_tables", "pa_pool_state", "pa_pool_stats", "pa_slots_for_positions",
+    "pa_batch_tables", "pa_pool_state", "pa_pool_stats", "pa_probe_read_chunks", "pa_slots_for_positions",
 ]
 
 
@@ -99,6 +99,7 @@ def _load():
         "pa_batch_tables": (c_int, [vp, intp, c_int, c_int, i32p, i32p]),
         "pa_pool_state": (c_int, [vp, i32p, i32p, intp]),
         "pa_pool_stats": (c_int, [vp, ctypes.POINTER(Stats)]),
+        "pa_probe_read_chunks": (c_int, [vp, c_sz, vp, c_int, vp, vp]),
         "pa_slots_for_positions": (c_int, [i32p, c_int, c_int, c_int, i32p, i32p, i32p]),
     }
     for name, (res, args) in sig.items():
@@ -341,3 +342,9 @@ class Pool:
         s = Stats()
         _check(lib.pa_pool_stats(self.handle, ctypes.byref(s)), "pa_pool_stats")
         return {n: int(getattr(s, n)) for n, _ in Stats._fields_}
+
+
+def probe_read_chunks(buf: torch.Tensor, chunk_ids: torch.Tensor, sink: torch.Tensor, stream=None):
+    """Read-bandwidth probe over a device buffer (see pa_probe_read_chunks)."""
+    _check(lib.pa_probe_read_chunks(_ptr(buf), buf.numel() * buf.element_size(), _ptr(chunk_ids),
+                                    int(chunk_ids.numel()), _ptr(sink), _stream(stream)), "pa_probe_read_chunks")

@@ -24,6 +24,7 @@ SOURCES = [
     os.path.join(CSRC, "kernels", "cache_ops.hip"),
     os.path.join(CSRC, "kernels", "decode.hip"),
     os.path.join(CSRC, "kernels", "prefill.hip"),
+    os.path.join(CSRC, "kernels", "probe.hip"),
 ]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

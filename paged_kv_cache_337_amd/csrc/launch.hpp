@@ -88,6 +88,10 @@ hipError_t launch_decode(const DecodeParams& p, int dtype, int D, hipStream_t st
 
 bool decode_supported(int dtype, int D, int G);
 
+// Read probe: n chunks of 8 KiB of buf in the order of ids (device).
+hipError_t launch_probe_read(const void* buf, int64_t nchunks_buf, const int32_t* ids, int n, void* sink,
+                             hipStream_t stream);
+
 // Causal prefill of the newest tokens of each sequence (same shape support as
 // decode).  Returns hipErrorInvalidValue when the grid would exceed its limit.
 hipError_t launch_prefill(const PrefillParams& p, int dtype, int D, hipStream_t stream);
