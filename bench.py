@@ -72,6 +72,38 @@ def sources_sha256(paths) -> str:
     return h.hexdigest()
 
 
+def run_steps(step, first, steps, stream):
+    """Runs step(k) for k = first ... first+steps-1 back to back, as a serving
+    loop would: wall clock and one stream event on each side of the whole loop,
+    nothing recorded between steps.  Returns (wall ms per step, event ms per
+    step)."""
+    import torch
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for k in range(steps):
+        step(first + k)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return wall * 1e3 / steps, e0.elapsed_time(e1) / steps
+
+
+def call_times(step, first, steps, stream):
+    """Per-call durations (ms) of the hot-path call inside step: the same steps
+    again, step(k, ev) recording ev[0] just before that call and ev[1] just after
+    it on the stream the call launches on.  An event record leaves the stream
+    idle for a few microseconds, so this pass is kept apart from run_steps."""
+    import torch
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for k in range(steps):
+        step(first + k, evs[k])
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in evs]
+
+
 def counter_traffic(record: str, workload: str):
     """HBM bytes per call from a committed rocprofv3 counter record
     (profiles/<record>.traffic.json: FETCH_SIZE + WRITE_SIZE, scaled by a copy
@@ -218,16 +250,8 @@ def main_prefill(args):
     torch.cuda.synchronize()
     if not torch.isfinite(out.float()).all():
         raise RuntimeError("non-finite prefill output")
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t_start = time.perf_counter()
-    for k in range(args.steps):
-        step(args.warmup + k, evs[k])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t_start
-    ms_per_step = wall * 1e3 / args.steps
-    pf_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    ms_per_step, _ = run_steps(step, args.warmup, args.steps, stream)
+    pf_ms = float(np.mean(call_times(step, args.warmup + args.steps, args.steps, stream)))
     flops = prefill_flops(w)
     ntok = int(qs_h[-1])
     peak = MFMA_PEAK_TFLOPS[w.dtype]
@@ -335,18 +359,19 @@ def main_prefix(args):
             pool.write_kv(0, kk, vv, slots)
             pool.prefill(0, q, qs, mq, t, c, mc, w.scale, out=out)
         torch.cuda.synchronize()
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-        t0 = time.perf_counter()
-        for e in evs:
+        def step(_k, e=None):
             pool.write_kv(0, kk, vv, slots)
-            e[0].record(stream)
+            if e is not None:
+                e[0].record(stream)
             pool.prefill(0, q, qs, mq, t, c, mc, w.scale, out=out)
-            e[1].record(stream)
-        torch.cuda.synchronize()
-        wall = (time.perf_counter() - t0) / steps
+            if e is not None:
+                e[1].record(stream)
+
+        wall_ms, _ = run_steps(step, 0, steps, stream)
+        pf_ms = float(np.mean(call_times(step, 0, steps, stream)))
         if not torch.isfinite(out.float()).all():
             raise RuntimeError("non-finite prefill output")
-        return wall * 1e3, float(np.mean([a.elapsed_time(b) for a, b in evs]))
+        return wall_ms, pf_ms
 
     ms_c, pf_c = timed(kc, vc, slots_cached, in_cached, args.steps, args.warmup)
     ms_p, pf_p = timed(k_all, v_all, slots_plain, in_plain, args.steps, args.warmup)
@@ -599,21 +624,10 @@ def main():
     if not torch.isfinite(out.float()).all():
         raise RuntimeError("non-finite decode output")
 
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
-    e_all = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-    torch.cuda.synchronize()
-    t_start = time.perf_counter()
-    e_all[0].record(stream)
-    for k in range(args.steps):
-        step(args.warmup + k, evs[k])
-    e_all[1].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t_start
-
-    ms_per_step = wall * 1e3 / args.steps
-    ev_ms = e_all[0].elapsed_time(e_all[1]) / args.steps
-    call_ms = [a.elapsed_time(b) for a, b in evs]
+    ms_per_step, ev_ms = run_steps(step, args.warmup, args.steps, stream)
+    # The same steps again (continuing the layer rotation), timing each
+    # pa_decode call on its stream.
+    call_ms = call_times(step, args.warmup + args.steps, args.steps, stream)
     dec_ms = float(np.mean(call_ms))
 
     # Warm calls: the same layer again and again (no rotation), so whatever
