@@ -283,7 +283,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeParams p) {
   off[bin] = before + x - val;
   if (threadIdx.x == kPlanThreads - 1) {
     p.header[0] = before + x;
-    p.header[1] = 0;
+    p.header[1] = p.first_taken;
     p.header[2] = P;
   }
   __syncthreads();
@@ -630,13 +630,10 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p, const 
   const int total = rfl(p.header[0]) * H;
   const float sl2 = p.scale_log2;
 
-  if (threadIdx.x == 0) {
-    sm.slot[2] = atomicAdd(&p.header[1], 1);
-    if constexpr (kDeep) sm.slot[3] = atomicAdd(&p.header[1], 1);
-  }
-  __syncthreads();
-  int cur = rfl(sm.slot[2]);
-  int nxt = kDeep ? rfl(sm.slot[3]) : 0;
+  // The first index (two in the deep schedule) comes from the workgroup id;
+  // the plan kernel starts the counter past them.
+  int cur = blockIdx.x;
+  int nxt = kDeep ? static_cast<int>(blockIdx.x + gridDim.x) : 0;
   if (cur >= total) return;
 
   Item it = make_item(p, items[cur / H], cur % H, P, wave);
@@ -726,6 +723,21 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(DecodeParams p) {
   const size_t e0 = static_cast<size_t>(pair) * p.max_parts;
   const float* ml = p.ws_ml + 2 * e0;
 
+  constexpr int PER = D / 64;  // head_dim entries per lane
+  // Eight partitions' rows per step, their loads issued together; the first
+  // eight go out with the (m, l) pairs.
+  float orow[8][PER];
+  auto load_rows = [&](int c0, int t, int n) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int r = t + u < n ? t + u : n - 1;
+      const float* src = p.ws_o + (e0 + c0 + r) * D + lane;
+#pragma unroll
+      for (int k = 0; k < PER; ++k) orow[u][k] = src[64 * k];
+    }
+  };
+  load_rows(0, 0, np < 64 ? np : 64);
+
   // Partition states are held one per lane, 64 partitions at a time.
   float M = kNegInf;
   for (int c0 = 0; c0 < np; c0 += 64)
@@ -733,7 +745,6 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(DecodeParams p) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
 
-  constexpr int PER = D / 64;  // head_dim entries per lane
   float acc[PER];
 #pragma unroll
   for (int k = 0; k < PER; ++k) acc[k] = 0.f;
@@ -744,23 +755,15 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(DecodeParams p) {
     const float wj = (mj == kNegInf) ? 0.f : ml[2 * jj + 1] * fast_exp2(mj - M);
     L += wj;
     const int n = np - c0 < 64 ? np - c0 : 64;
-    // Eight partitions per step, their loads issued together.
     for (int t = 0; t < n; t += 8) {
-      float o[8][PER];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int r = t + u < n ? t + u : n - 1;
-        const float* src = p.ws_o + (e0 + c0 + r) * D + lane;
-#pragma unroll
-        for (int k = 0; k < PER; ++k) o[u][k] = src[64 * k];
-      }
+      if (c0 + t > 0) load_rows(c0, t, n);
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const float w = t + u < n ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(
                                                          __builtin_bit_cast(int, wj), t + u))
                                   : 0.f;
 #pragma unroll
-        for (int k = 0; k < PER; ++k) acc[k] = fmaf(w, o[u][k], acc[k]);
+        for (int k = 0; k < PER; ++k) acc[k] = fmaf(w, orow[u][k], acc[k]);
       }
     }
   }
@@ -798,6 +801,25 @@ __global__ __launch_bounds__(kMergeThreads) void merge_wide_kernel(DecodeParams 
   const size_t e0 = static_cast<size_t>(pair) * p.max_parts;
   const float* ml = p.ws_ml + 2 * e0;
 
+  // Rows eight at a time, the first eight requested with the (m, l) pairs.
+  // A wave with no partitions (j0 >= j1) loads nothing.
+  float orow[8][VEC];
+  auto load_rows = [&](int c0, int t, int n) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int r = t + u < n ? t + u : n - 1;
+      const float* src = p.ws_o + (e0 + c0 + r) * D + VEC * lane;
+      if constexpr (VEC == 2) {
+        const float2 x = *reinterpret_cast<const float2*>(src);
+        orow[u][0] = x.x;
+        orow[u][1] = x.y;
+      } else {
+#pragma unroll
+        for (int k = 0; k < VEC; ++k) orow[u][k] = src[k];
+      }
+    }
+  };
+  if (j0 < j1) load_rows(j0, 0, j1 - j0 < 64 ? j1 - j0 : 64);
   float M = kNegInf;
   for (int c0 = j0; c0 < j1; c0 += 64)
     if (c0 + lane < j1) M = fmaxf(M, ml[2 * (c0 + lane)]);
@@ -814,27 +836,14 @@ __global__ __launch_bounds__(kMergeThreads) void merge_wide_kernel(DecodeParams 
     L += wj;
     const int n = j1 - c0 < 64 ? j1 - c0 : 64;
     for (int t = 0; t < n; t += 8) {
-      float o[8][VEC];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int r = t + u < n ? t + u : n - 1;
-        const float* src = p.ws_o + (e0 + c0 + r) * D + VEC * lane;
-        if constexpr (VEC == 2) {
-          const float2 x = *reinterpret_cast<const float2*>(src);
-          o[u][0] = x.x;
-          o[u][1] = x.y;
-        } else {
-#pragma unroll
-          for (int k = 0; k < VEC; ++k) o[u][k] = src[k];
-        }
-      }
+      if (c0 + t > j0) load_rows(c0, t, n);
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const float w = t + u < n ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(
                                                          __builtin_bit_cast(int, wj), t + u))
                                   : 0.f;
 #pragma unroll
-        for (int k = 0; k < VEC; ++k) acc[k] = fmaf(w, o[u][k], acc[k]);
+        for (int k = 0; k < VEC; ++k) acc[k] = fmaf(w, orow[u][k], acc[k]);
       }
     }
   }
@@ -908,6 +917,7 @@ hipError_t launch_decode_kernel(DecodeParams p, hipStream_t stream) {
   if (grid <= 0) return hipErrorInvalidValue;
   if (grid > work_bound) grid = static_cast<int>(work_bound);
   p.grid = grid;
+  p.first_taken = deep ? 2 * grid : grid;
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
