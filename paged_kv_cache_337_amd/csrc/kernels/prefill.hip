@@ -418,24 +418,25 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
   // masked form is needed only where the stage reaches past some row's
   // position (the causal diagonal and the context's end).
   auto compute = [&](int buf, int key0, bool masked) {
+    // The stage's K fragments, read once and used by every row tile.
+    uint4 kf[kUnits][NCH];
+#pragma unroll
+    for (int u = 0; u < kUnits; ++u)
+#pragma unroll
+      for (int cc = 0; cc < NCH; ++cc) kf[u][cc] = sm.k[buf][u][cc][lane];
     f32x4_t sc[NB][kUnits];  // scores: token key0 + 16*u + 4*grp + r of row col
+    auto scores = [&](int b) {
 #pragma unroll
-    for (int u = 0; u < kUnits; ++u) {
-      uint4 kf[NCH];
-#pragma unroll
-      for (int cc = 0; cc < NCH; ++cc) kf[cc] = sm.k[buf][u][cc][lane];
-#pragma unroll
-      for (int b = 0; b < NB; ++b) {
+      for (int u = 0; u < kUnits; ++u) {
         sc[b][u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int cc = 0; cc < NCH; ++cc) sc[b][u] = mfma_k32<T>(kf[cc], qb[b][cc], sc[b][u]);
+        for (int cc = 0; cc < NCH; ++cc) sc[b][u] = mfma_k32<T>(kf[u][cc], qb[b][cc], sc[b][u]);
       }
-    }
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      // Keys past the context were zeroed by the loader; they and the keys
-      // beyond a row's position are masked where some row of the tile can
-      // see them.
+    };
+    // Mask and reference of tile b.  Keys past the context were zeroed by the
+    // loader; they and the keys beyond a row's position are masked where
+    // some row of the tile can see them.
+    auto prep = [&](int b) {
       if (masked && key0 + kKeys - 1 > qmin[b]) {
         asm volatile("");  // keep the branch: most stages skip it
         const int lim = qpos[b] - key0 - 4 * grp;
@@ -461,6 +462,41 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
 #pragma unroll
         for (int t = 0; t < NT; ++t) acc[b][t] *= alpha;
       }
+    };
+    // Weights of tile b at pair q (the B operand of O^T += V^T.P^T).
+    auto weights = [&](int b, int q) {
+      const float nm = m_ref[b] == kNegInfP ? 0.f : -m_ref[b];
+      float e[8];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        e[r] = fast_exp2(fmaf(sc[b][2 * q][r], sl2, nm));
+        e[4 + r] = fast_exp2(fmaf(sc[b][2 * q + 1][r], sl2, nm));
+      }
+      return make_uint4(pack2<T>(e[0], e[1]), pack2<T>(e[2], e[3]), pack2<T>(e[4], e[5]), pack2<T>(e[6], e[7]));
+    };
+    auto pv = [&](int b, const uint4 (&vv)[NT], uint4 pb) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) acc[b][t] = mfma_k32<T>(vv[t], pb, acc[b][t]);
+      lsum[b] = mfma_k32<T>(ones, pb, lsum[b]);
+    };
+    // Software pipeline over the row tiles: the score products of tile b go
+    // out while the weights of tile b - 1 are exponentiated, and the P.V
+    // products of the earlier tiles while the last tile's weights are.
+    uint4 pb[NB][NP];
+    scores(0);
+    prep(0);
+#pragma unroll
+    for (int b = 1; b < NB; ++b) {
+      scores(b);
+#pragma unroll
+      for (int q = 0; q < NP; ++q) pb[b - 1][q] = weights(b - 1, q);
+      // Scheduling: one score MFMA, then three VALU instructions of the weights.
+#pragma unroll
+      for (int k = 0; k < kUnits * NCH; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+      }
+      prep(b);
     }
 #pragma unroll
     for (int q = 0; q < NP; ++q) {
@@ -468,19 +504,15 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
 #pragma unroll
       for (int t = 0; t < NT; ++t) vv[t] = *reinterpret_cast<const uint4*>(&sm.v[buf][q][t][lane][0]);
 #pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        const float nm = m_ref[b] == kNegInfP ? 0.f : -m_ref[b];
-        float e[8];
+      for (int b = 0; b < NB - 1; ++b) pv(b, vv, pb[b][q]);
+      pv(NB - 1, vv, weights(NB - 1, q));
+      // Scheduling: the V reads first, then one P.V MFMA of the earlier tiles
+      // and two VALU instructions of the last tile's weights, in turn.
+      __builtin_amdgcn_sched_group_barrier(0x100, NT, 1);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          e[r] = fast_exp2(fmaf(sc[b][2 * q][r], sl2, nm));
-          e[4 + r] = fast_exp2(fmaf(sc[b][2 * q + 1][r], sl2, nm));
-        }
-        const uint4 pb = make_uint4(pack2<T>(e[0], e[1]), pack2<T>(e[2], e[3]), pack2<T>(e[4], e[5]),
-                                    pack2<T>(e[6], e[7]));
-#pragma unroll
-        for (int t = 0; t < NT; ++t) acc[b][t] = mfma_k32<T>(vv[t], pb, acc[b][t]);
-        lsum[b] = mfma_k32<T>(ones, pb, lsum[b]);
+      for (int k = 0; k < (NB - 1) * (NT + 1); ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+        __builtin_amdgcn_sched_group_barrier(0x002, 2, 1);
       }
     }
   };
