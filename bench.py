@@ -104,6 +104,21 @@ def call_times(step, first, steps, stream):
     return [a.elapsed_time(b) for a, b in evs]
 
 
+def copy_calibration(pool, w, layers, blocks):
+    """Copies `blocks` whole blocks (every layer) with pa_copy_blocks after the
+    timed work: a copy of known size (returned, read and written once each)
+    for scaling the FETCH_SIZE / WRITE_SIZE counters of the same run."""
+    import torch
+    import paged_kv_cache_337_amd as pa
+    n = min(blocks, w.num_blocks // 2)
+    pairs = torch.stack([torch.arange(n), torch.arange(n) + n], dim=1).to(torch.int32).cuda()
+    pool.copy_blocks(pairs)
+    torch.cuda.synchronize()
+    nbytes = n * layers * 2 * w.num_kv_heads * w.block_size * w.head_dim * pa.ELEM_BYTES[w.dtype]
+    log(f"[bench] copy calibration: {n} blocks, {nbytes} bytes read and {nbytes} written")
+    return nbytes
+
+
 def counter_traffic(record: str, workload: str):
     """HBM bytes per call from a committed rocprofv3 counter record
     (profiles/<record>.traffic.json: FETCH_SIZE + WRITE_SIZE, scaled by a copy
@@ -282,7 +297,7 @@ def main_prefill(args):
         "flops_per_step": flops,
         "roofline": {
             "bound": "mfma",
-            "kernel": "pa_prefill (prefill_kernel)",
+            "kernel": ("pa_prefill (prefill_lds_kernel)" if eb == 2 else "pa_prefill (prefill_kernel)"),
             "achieved": round(achieved, 2),
             "peak": peak,
             "unit": "TFLOP/s",
@@ -294,6 +309,8 @@ def main_prefill(args):
             "avg_launch_ms": round(pf_ms, 5),
         },
     }
+    if args.copy_calib_blocks > 0:
+        res["copy_calibration_bytes"] = copy_calibration(pool, w, L, args.copy_calib_blocks)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline_prefill(w, args.cpu_budget_s)
     print(json.dumps(res), flush=True)
@@ -713,13 +730,7 @@ def main():
         },
     }
     if args.copy_calib_blocks > 0:
-        n = min(args.copy_calib_blocks, w.num_blocks // 2)
-        pairs = torch.stack([torch.arange(n), torch.arange(n) + n], dim=1).to(torch.int32).cuda()
-        pool.copy_blocks(pairs)
-        torch.cuda.synchronize()
-        nbytes = n * L * 2 * w.num_kv_heads * w.block_size * w.head_dim * eb
-        log(f"[bench] copy calibration: {n} blocks, {nbytes} bytes read and {nbytes} written")
-        res["copy_calibration_bytes"] = nbytes
+        res["copy_calibration_bytes"] = copy_calibration(pool, w, L, args.copy_calib_blocks)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_budget_s, host_tables, host_ctx)
         try:
