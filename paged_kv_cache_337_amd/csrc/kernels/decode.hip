@@ -626,17 +626,26 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p, const 
   const int lane = threadIdx.x & 63;
   const int wave = rfl(threadIdx.x >> 6);
   const int H = p.H;
-  const int P = rfl(p.header[2]);
-  const int total = rfl(p.header[0]) * H;
+  const bool direct = p.direct != 0;
+  const int P = direct ? p.P : rfl(p.header[2]);
+  const int total = direct ? p.S * H : rfl(p.header[0]) * H;
   const float sl2 = p.scale_log2;
+  // Item record of work index w: from the plan's list, or (direct launch:
+  // every context within one partition) the sequence itself.
+  auto record = [&](int w) {
+    if (!direct) return items[w / H];
+    const int i = w / H;
+    return make_int4(i, 0, rfl(clamp_ctx(p, i)), 1);
+  };
 
   // The first index (two in the deep schedule) comes from the workgroup id;
-  // the plan kernel starts the counter past them.
+  // the plan kernel starts the counter past them.  A direct launch has one
+  // index per workgroup and never touches the counter.
   int cur = blockIdx.x;
   int nxt = kDeep ? static_cast<int>(blockIdx.x + gridDim.x) : 0;
   if (cur >= total) return;
 
-  Item it = make_item(p, items[cur / H], cur % H, P, wave);
+  Item it = make_item(p, record(cur), cur % H, P, wave);
   typename Path::Q q;
   Path::load_q(q, p, it, lane);
   UnitStream<D, kBytes, kKeep> st;
@@ -657,14 +666,14 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p, const 
   };
 
   for (int k = 0;; ++k) {
-    int nn = 0;
-    if (threadIdx.x == 0) nn = atomicAdd(&p.header[1], 1);
+    int nn = total;
+    if (threadIdx.x == 0 && !direct) nn = atomicAdd(&p.header[1], 1);
     if constexpr (kDeep) {
       // The next item (the current one again after the last: the loads below
       // are then harmless repeats, and always issuing them keeps the waits in
       // the stream exact).
       const bool has_next = nxt < total;
-      const Item nit = make_item(p, items[(has_next ? nxt : cur) / H], (has_next ? nxt : cur) % H, P, wave);
+      const Item nit = make_item(p, record(has_next ? nxt : cur), (has_next ? nxt : cur) % H, P, wave);
       typename Path::Q qn;
       Path::load_q(qn, p, nit, lane);
       int32_t ids_n;
@@ -698,7 +707,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p, const 
       __syncthreads();
       cur = rfl(sm.slot[k & 1]);
       if (cur >= total) break;
-      it = make_item(p, items[cur / H], cur % H, P, wave);
+      it = make_item(p, record(cur), cur % H, P, wave);
       Path::load_q(q, p, it, lane);
       st.begin(p, it.trow, it.start, it.u0, it.h);
       st.ids = st.fetch_ids(lane);
@@ -912,15 +921,22 @@ hipError_t launch_decode_kernel(DecodeParams p, hipStream_t stream) {
   const void* k_deep = reinterpret_cast<const void*>(&decode_kernel<Path, T, D, true, false>);
   int grid = persistent_grid(k_shallow);
   if (grid <= 0) return hipErrorInvalidValue;
-  const bool deep = !p.auto_partition && work_bound >= static_cast<int64_t>(kDeepItemsPerWorkgroup) * grid;
+  // Direct launch: every context fits one partition and every (sequence,
+  // kv head) pair gets a workgroup of its own, so the work list is the
+  // sequences in order and needs neither the plan kernel nor the counter.
+  p.direct = (p.max_parts == 1 && work_bound <= grid) ? 1 : 0;
+  const bool deep = !p.direct && !p.auto_partition &&
+                    work_bound >= static_cast<int64_t>(kDeepItemsPerWorkgroup) * grid;
   if (deep) grid = persistent_grid(k_deep);
   if (grid <= 0) return hipErrorInvalidValue;
   if (grid > work_bound) grid = static_cast<int>(work_bound);
   p.grid = grid;
   p.first_taken = deep ? 2 * grid : grid;
-  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, p);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (!p.direct) {
+    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   const int4* items = static_cast<const int4*>(p.items);
   // Cached loads when the batch shares blocks (the shallow schedule only:
   // shared prefixes come with automatic partitioning in practice).

@@ -30,6 +30,8 @@ struct DecodeParams {
   int32_t auto_partition;    // 1: the plan kernel may raise P (header[2])
   int32_t grid;              // workgroups of the decode kernel
   int32_t first_taken;       // work indices handed out by workgroup id before the counter
+  int32_t direct;            // 1: one (sequence, kv head) per workgroup, no plan, no counter
+                             //    (every context within one partition, S * H <= grid)
   int32_t max_parts;         // ceil(ctx_cap / P)
   int32_t* header;           // [0] work items, [1] next work index, [2] P used (device)
   int4* items;               // [S * max_parts] (sequence, partition, context, partitions), longest first
