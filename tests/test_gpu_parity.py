@@ -209,6 +209,28 @@ def test_contiguous_layout_equals_scattered():
     assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
 
 
+@pytest.mark.parametrize("dtype,hq,hkv,d", [("bf16", 32, 8, 128), ("f16", 8, 8, 128), ("f32", 4, 4, 64)])
+def test_direct_launch_equals_planned(dtype, hq, hkv, d):
+    """Contexts within one partition and few enough (sequence, kv head) pairs
+    take the direct launch (no plan kernel); a larger declared capacity sends
+    the same batch through the plan.  Both give the same bits and match the
+    oracle."""
+    w = W.custom("direct", 76, dtype, [1, 15, 16, 17, 200, 511, 512], hq, hkv, d, 16, extra_blocks=5)
+    pad = np.full((w.num_seqs, 48), -1, dtype=np.int32)
+    pad[:, :w.block_tables.shape[1]] = w.block_tables
+    pool = U.make_pool(w)
+    U.fill_pool(pool, w)
+    q, t, c = U.device_inputs(w, tables=pad)
+    outs = []
+    for max_ctx in (512, 768):  # one partition of 512 tokens, then two
+        out = pool.decode(0, q, t, c, max_ctx, w.scale, 0)
+        torch.cuda.synchronize()
+        outs.append(out.cpu())
+    bits = U.TORCH_BITS[dtype]
+    assert torch.equal(outs[0].view(bits), outs[1].view(bits))
+    U.check_close(U.out_f64(outs[0]), U.oracle_rows(w, range(w.num_seqs)), dtype, "direct launch")
+
+
 def test_planted_oracle_slips_fail_the_gates():
     """The gates are strong enough: oracle variants with a dropped last block,
     consecutive-vs-strided head grouping swapped, or the tail token dropped
