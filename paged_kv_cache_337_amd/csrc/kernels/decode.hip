@@ -9,12 +9,14 @@
 // FlashAttention) so K/V are read exactly once.
 //
 // Launch sequence of one pa_decode call:
-//   1. plan_kernel (one workgroup) cuts every context into partitions of P
+//   1. plan_kernel (one workgroup) cuts every context into work items of P
 //      tokens (P chosen from the total work when the caller asks for
-//      automatic partitioning) and writes the list of (sequence, partition,
-//      context) work items, full partitions first and the partial ones by
-//      decreasing size, so the tail of the decode consists of the smallest
-//      items.
+//      automatic partitioning; with many small explicit partitions an item is
+//      four consecutive partitions, one per wave) and writes the list of
+//      (sequence, item, context) records, full items first and the partial
+//      ones by decreasing size, so the tail of the decode consists of the
+//      smallest items.  Small batches whose contexts all fit one partition
+//      skip this kernel (direct launch).
 //   2. the decode kernel is persistent: one workgroup of four wave64s per CU
 //      takes work indices (item, kv head) from an atomic counter.  For many
 //      small items it runs two indices ahead and streams item after item:
@@ -99,29 +101,32 @@ constexpr int kWorkgroupsPerCU = PA_WG_PER_CU;
 
 // One work item as one wave of the workgroup sees it (all values uniform).
 struct Item {
-  int i, j, h;     // sequence, partition, kv head
+  int i, j, h;     // sequence, work item within the sequence, kv head
   int ctx;         // context length (clamped)
-  int start;       // first token of the partition
-  int ntok;        // tokens in the partition
+  int start;       // first token of the item
+  int ntok;        // tokens in the item
   int u0, u1;      // this wave's run of 16-token units
-  int np;          // partitions of the sequence
+  int np;          // work items of the sequence
   const int32_t* trow;
 };
 
-// rec = (sequence, partition, clamped context, partitions of the sequence) as
-// written by plan_kernel.
-__device__ __forceinline__ Item make_item(const DecodeParams& p, int4 rec, int h, int P, int wave) {
+// rec = (sequence, item, clamped context, items of the sequence) as written
+// by plan_kernel; an item holds PI tokens.  With group == 1 the four waves
+// split the item evenly.  Otherwise the item is `group` consecutive
+// partitions of PI / group tokens and wave w computes partition w of it.
+// Either way the waves' states are then combined through LDS.
+__device__ __forceinline__ Item make_item(const DecodeParams& p, int4 rec, int h, int PI, int group, int wave) {
   Item it;
   it.i = rfl(rec.x);
   it.j = rfl(rec.y);
   it.ctx = rfl(rec.z);
   it.np = rfl(rec.w);
   it.h = h;
-  it.start = it.j * P;
+  it.start = it.j * PI;
   const int left = it.ctx - it.start;
-  it.ntok = left < P ? (left > 0 ? left : 0) : P;
+  it.ntok = left < PI ? (left > 0 ? left : 0) : PI;
   const int nunits = (it.ntok + 15) >> 4;
-  const int per = (nunits + kWaves - 1) / kWaves;
+  const int per = group > 1 ? (PI / group) >> 4 : (nunits + kWaves - 1) / kWaves;
   it.u0 = wave * per;
   it.u1 = it.u0 + per < nunits ? it.u0 + per : nunits;
   it.trow = p.tables + static_cast<size_t>(it.i) * p.max_blocks;
@@ -251,7 +256,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeParams p) {
     sP = p.P;
   }
   __syncthreads();
-  const int P = sP;
+  const int P = sP * p.group;  // tokens per work item (header[2]; the merge's unit)
   const int top = (P >> 4) - 1 < kPlanBins - 1 ? (P >> 4) - 1 : kPlanBins - 1;
   auto bin_of = [&](int ntok) {
     const int units = (ntok + 15) >> 4;
@@ -645,7 +650,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p, const 
   int nxt = kDeep ? static_cast<int>(blockIdx.x + gridDim.x) : 0;
   if (cur >= total) return;
 
-  Item it = make_item(p, record(cur), cur % H, P, wave);
+  const int group = p.group;
+  Item it = make_item(p, record(cur), cur % H, P, group, wave);
   typename Path::Q q;
   Path::load_q(q, p, it, lane);
   UnitStream<D, kBytes, kKeep> st;
@@ -673,7 +679,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p, const 
       // are then harmless repeats, and always issuing them keeps the waits in
       // the stream exact).
       const bool has_next = nxt < total;
-      const Item nit = make_item(p, record(has_next ? nxt : cur), (has_next ? nxt : cur) % H, P, wave);
+      const Item nit = make_item(p, record(has_next ? nxt : cur), (has_next ? nxt : cur) % H, P, group, wave);
       typename Path::Q qn;
       Path::load_q(qn, p, nit, lane);
       int32_t ids_n;
@@ -707,7 +713,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p, const 
       __syncthreads();
       cur = rfl(sm.slot[k & 1]);
       if (cur >= total) break;
-      it = make_item(p, record(cur), cur % H, P, wave);
+      it = make_item(p, record(cur), cur % H, P, group, wave);
       Path::load_q(q, p, it, lane);
       st.begin(p, it.trow, it.start, it.u0, it.h);
       st.ids = st.fetch_ids(lane);
@@ -913,6 +919,8 @@ int persistent_grid(const void* kernel) {
 // Items per workgroup from which the deep schedule pays (an upper bound
 // from the host's view: every sequence at the maximum context length).
 constexpr int kDeepItemsPerWorkgroup = 16;
+// Largest partition that a single wave streams alone in grouped items.
+constexpr int kMaxGroupedPartition = 1024;
 
 template <typename Path, typename T, int D>
 hipError_t launch_decode_kernel(DecodeParams p, hipStream_t stream) {
@@ -932,6 +940,15 @@ hipError_t launch_decode_kernel(DecodeParams p, hipStream_t stream) {
   if (grid > work_bound) grid = static_cast<int>(work_bound);
   p.grid = grid;
   p.first_taken = deep ? 2 * grid : grid;
+  // Many small explicit partitions: a work item is four consecutive
+  // partitions, one per wave (the workspace keeps its per-partition stride,
+  // which bounds the number of items).  Each wave computes its partition's softmax
+  // state; the four states are combined through LDS (the first level of the
+  // log-sum-exp merge) and the item's state goes to the workspace for the
+  // merge kernel (the second level).  Measured at cfg4 (512-token
+  // partitions): one partition per item, split over the four waves, wrote
+  // and merged four times as many states and took 10% longer.
+  p.group = (deep && p.P <= kMaxGroupedPartition) ? kWaves : 1;
   if (!p.direct) {
     hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, p);
     hipError_t e = hipGetLastError();

@@ -30,6 +30,8 @@ struct DecodeParams {
   int32_t auto_partition;    // 1: the plan kernel may raise P (header[2])
   int32_t grid;              // workgroups of the decode kernel
   int32_t first_taken;       // work indices handed out by workgroup id before the counter
+  int32_t group;             // partitions per work item: 1, or one per wave (each wave then
+                             //    computes one partition and writes its state itself)
   int32_t direct;            // 1: one (sequence, kv head) per workgroup, no plan, no counter
                              //    (every context within one partition, S * H <= grid)
   int32_t max_parts;         // ceil(ctx_cap / P)
