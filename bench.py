@@ -37,7 +37,7 @@ METRIC = "paged decode KV-read GB/s (% of HBM peak) + seqs/s, Llama-3-8B-shaped 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="llama3_8b",
                     choices=["tiny", "opt13b", "llama3_8b", "long_ctx", "shared", "shared_cow",
@@ -701,7 +701,8 @@ def main():
                         f"heads, head_dim {w.head_dim}, block_size {w.block_size}"
                         + (", contiguous block placement" if args.contiguous and not shared else ""),
             "batch": w.num_seqs, "total_context_tokens": w.total_tokens,
-            "max_context_len": max_ctx, "partition_tokens": P or 512,
+            "max_context_len": max_ctx,
+            "partition_tokens": P if P else "automatic (at least 512, chosen on the device)",
             "layer_slots_rotated": L,
             "step": "pa_write_kv (1 new token/seq) + pa_decode",
         },
