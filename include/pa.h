@@ -145,8 +145,12 @@ size_t pa_decode_workspace_bytes(const pa_pool* pool, int num_seqs, int num_q_he
  *     out[i, g] = softmax_p(scale * q[i, g] . K_i[p, h]) . V_i[p, h],
  *     p = 0 .. context_lens[i] - 1,
  * where K_i/V_i are read through block_tables row i.  Contexts longer than
- * `partition_tokens` are split into partitions whose softmax states are merged
- * by log-sum-exp weighting.
+ * `partition_tokens` are split into partitions of that many tokens; each
+ * partition's softmax state (max, sum, weighted V) is computed on its own and
+ * the states are combined by log-sum-exp weighting, possibly in stages (with
+ * many small partitions, four neighbours are combined on chip before the
+ * final merge).  The combination is associative, so the staging changes only
+ * float32 rounding.
  *   q, out             device [num_seqs, num_q_heads, D], pool dtype,
  *                      out written with round-to-nearest-even from float32
  *   block_tables       device int32 [num_seqs, max_blocks_per_seq]; entries
