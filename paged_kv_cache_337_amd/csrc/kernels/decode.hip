@@ -946,12 +946,13 @@ hipError_t launch_decode_kernel(DecodeParams p, hipStream_t stream) {
   p.first_taken = deep ? 2 * grid : grid;
   // Many small explicit partitions: a work item is four consecutive
   // partitions, one per wave (the workspace keeps its per-partition stride,
-  // which bounds the number of items).  Each wave computes its partition's softmax
-  // state; the four states are combined through LDS (the first level of the
-  // log-sum-exp merge) and the item's state goes to the workspace for the
-  // merge kernel (the second level).  Measured at cfg4 (512-token
-  // partitions): one partition per item, split over the four waves, wrote
-  // and merged four times as many states and took 10% longer.
+  // which bounds the number of items).  Each wave computes its partition's
+  // softmax state; the four states are combined through LDS (the first
+  // level of the log-sum-exp merge) and the item's state goes to the
+  // workspace for the merge kernel (the second level).  Measured on the
+  // long-context batch (8 x 32K-128K tokens, 512-token partitions): one
+  // partition per item, split over the four waves, wrote and merged four
+  // times as many states and took 7% longer.
   p.group = (deep && p.P <= kMaxGroupedPartition) ? kWaves : 1;
   if (!p.direct) {
     hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, p);
