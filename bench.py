@@ -42,7 +42,7 @@ def parse():
     ap.add_argument("--workload", default="llama3_8b",
                     choices=["tiny", "opt13b", "llama3_8b", "long_ctx", "shared", "shared_cow",
                              "prefill_tiny", "prefill_llama3_8b", "chunked_llama3_8b", "prefix_cache",
-                             "swap"])
+                             "swap", "probe"])
     ap.add_argument("--contiguous", action="store_true",
                     help="place every sequence's blocks side by side in logical order (a "
                          "contiguous-cache control for the same kernel)")
@@ -570,6 +570,39 @@ def main_swap(args):
     print(json.dumps(res), flush=True)
 
 
+def main_probe(args):
+    """HBM read rate of the decode kernel's access pattern (pa_probe_read_chunks:
+    whole 8 KiB chunks, 16-byte streaming loads, no arithmetic) over a 6 GiB
+    buffer, for chunk orders of growing contiguity: random 8 KiB chunks (one
+    (block, kv head) region of the pool), random runs of 4, 8 and 32 chunks,
+    and the identity order.  It bounds what any block placement could gain."""
+    import torch
+    import paged_kv_cache_337_amd as pa
+    nbytes = 6 << 30
+    buf = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+    nchunks = nbytes // 8192
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    rng = np.random.default_rng(0)
+
+    def runs(g):
+        starts = rng.permutation(nchunks // g)
+        return (starts[:, None] * g + np.arange(g)[None, :]).reshape(-1).astype(np.int32)
+
+    orders = {"random_8KiB": rng.permutation(nchunks).astype(np.int32), "random_32KiB_runs": runs(4),
+              "random_64KiB_runs": runs(8), "random_256KiB_runs": runs(32),
+              "identity": np.arange(nchunks, dtype=np.int32)}
+    stream = torch.cuda.current_stream()
+    rates = {}
+    for name, order in orders.items():
+        od = torch.from_numpy(order).cuda()
+        ms = call_times(lambda _k, ev: (ev[0].record(stream), pa.probe_read_chunks(buf, od, sink),
+                                        ev[1].record(stream)), 0, 1 + max(args.steps // 20, 3), stream)
+        rates[name] = round(nbytes / (float(np.median(ms[1:])) * 1e-3) / 1e9, 1)
+    print(json.dumps({"metric": "HBM read probe GB/s by chunk contiguity (pa_probe_read_chunks, 6 GiB)",
+                      "value": rates["random_8KiB"], "unit": "GB/s", "n_gpus": 1, "higher_is_better": True,
+                      "data": "synthetic", "rates": rates, "peak": HBM_PEAK_GBS}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -581,6 +614,8 @@ def main():
         return main_prefix(args)
     if args.workload == "swap":
         return main_swap(args)
+    if args.workload == "probe":
+        return main_probe(args)
 
     import torch
     import paged_kv_cache_337_amd as pa
