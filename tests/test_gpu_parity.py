@@ -231,15 +231,16 @@ def test_direct_launch_equals_planned(dtype, hq, hkv, d):
     U.check_close(U.out_f64(outs[0]), U.oracle_rows(w, range(w.num_seqs)), dtype, "direct launch")
 
 
-@pytest.mark.parametrize("dtype,hq,hkv,d,P", [("bf16", 32, 8, 128, 16), ("bf16", 64, 8, 128, 48),
-                                               ("f16", 8, 8, 128, 16), ("f32", 16, 8, 64, 32)])
-def test_grouped_partitions_match_oracle(dtype, hq, hkv, d, P):
+@pytest.mark.parametrize("dtype,hq,hkv,d,P,bs", [("bf16", 32, 8, 128, 16, 16), ("bf16", 64, 8, 128, 48, 16),
+                                                  ("f16", 8, 8, 128, 16, 16), ("f32", 16, 8, 64, 32, 16),
+                                                  ("bf16", 64, 8, 128, 32, 32), ("f16", 16, 8, 64, 32, 32)])
+def test_grouped_partitions_match_oracle(dtype, hq, hkv, d, P, bs):
     """Explicit partitions small enough for many work items per workgroup:
     a work item is four consecutive partitions, one per wave, whose states
     are merged through LDS before the merge kernel.  Every output element
     against the oracle, ragged last items included."""
     ctx = [1, 15, 16, 17, 63, 64, 65, 500, 999, 1000, 1337, 2048]
-    w = W.custom("grouped", 77, dtype, ctx, hq, hkv, d, 16)
+    w = W.custom("grouped", 77, dtype, ctx, hq, hkv, d, bs)
     max_parts = -(-w.max_context_len // P)
     assert w.num_seqs * max_parts * hkv >= 16 * 256  # the many-items (grouped) schedule
     pool = U.make_pool(w)
