@@ -306,3 +306,33 @@ def test_planted_mistakes_are_caught(mutant):
         if np.max(np.abs(mutant(q, Kf, Vf, w.scale) - _sdpa(q, Kf, Vf, w.scale))) > 1e-6:
             caught = True
     assert caught
+
+
+def test_staged_lse_merge_equals_unsplit():
+    """Split-K over fixed partitions, combined in two stages: four neighbouring
+    partition states into a group state (max M, sum L relative to M, output),
+    then the group states.  The log-sum-exp combination is associative, so the
+    staged result is the unsplit attention to rounding; carrying a group's sum
+    wrongly (L = 1) is caught."""
+    rng = np.random.default_rng(11)
+    for T, P in [(1, 16), (100, 16), (1000, 64), (2049, 512), (5000, 512)]:
+        q = rng.standard_normal((8, 32))
+        K = rng.standard_normal((T, 2, 32)) * 2.0
+        V = rng.standard_normal((T, 2, 32))
+        states = [A.partition_state(q, K[a:a + P], V[a:a + P], 0.17) for a in range(0, T, P)]
+
+        def staged(carry_sum=True):
+            groups = []
+            for g0 in range(0, len(states), 4):
+                grp = states[g0:g0 + 4]
+                ms = np.array([st[0] for st in grp])
+                ls = np.array([st[1] for st in grp])
+                M = ms.max(axis=0)
+                L = (ls * np.exp(ms - M)).sum(axis=0) if carry_sum else np.ones_like(M)
+                groups.append((M, L, A.lse_merge(ms, ls, [st[2] for st in grp])))
+            return A.lse_merge([g[0] for g in groups], [g[1] for g in groups], [g[2] for g in groups])
+
+        ref = A.decode_one(q, K, V, 0.17)
+        assert np.max(np.abs(staged() - ref)) <= 1e-12, (T, P)
+        if len(states) > 4:  # two or more groups: the group sums matter
+            assert np.max(np.abs(staged(carry_sum=False) - ref)) > 1e-6, (T, P)
