@@ -130,6 +130,36 @@ def _stream(stream=None) -> ctypes.c_void_p:
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _bad(fn: str, msg: str):
+    raise PAError(-1, fn, msg)
+
+
+def _need(t, fn: str, name: str, dtype=None, ndim=None, last=None, dim1=None, min_rows=None):
+    """Checks a tensor argument before its address is handed to a kernel: the
+    kernels trust shapes, dtypes and strides, so a mismatch here would become
+    an out-of-bounds device access there.  Device placement is checked last."""
+    if not isinstance(t, torch.Tensor):
+        _bad(fn, f"{name} must be a torch.Tensor")
+    if dtype is not None and t.dtype != dtype:
+        _bad(fn, f"{name} has dtype {t.dtype}, expected {dtype}")
+    if ndim is not None and t.dim() != ndim:
+        _bad(fn, f"{name} must have {ndim} dimensions, has {t.dim()}")
+    if last is not None and t.shape[-1] != last:
+        _bad(fn, f"{name} last dimension is {t.shape[-1]}, expected {last}")
+    if dim1 is not None and t.shape[1] != dim1:
+        _bad(fn, f"{name} dimension 1 is {t.shape[1]}, expected {dim1}")
+    if min_rows is not None and t.shape[0] < min_rows:
+        _bad(fn, f"{name} has {t.shape[0]} rows, needs at least {min_rows}")
+    if not t.is_contiguous():
+        _bad(fn, f"{name} must be contiguous")
+
+
+def _on_device(fn: str, *named):
+    for name, t in named:
+        if t is not None and t.device.type != "cuda":
+            _bad(fn, f"{name} must be a device tensor (is on {t.device})")
+
+
 def version() -> str:
     return lib.pa_version().decode()
 
@@ -199,8 +229,13 @@ class Pool:
     # -- device operations ---------------------------------------------
     def write_kv(self, layer: int, k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor,
                  stream=None):
-        self._need_device()
+        fn, dt = "pa_write_kv", TORCH_DTYPE[self.dtype]
+        _need(slot_mapping, fn, "slot_mapping", torch.int32, 1)
         n = int(slot_mapping.shape[0])
+        for name, t in (("k", k), ("v", v)):
+            _need(t, fn, name, dt, 3, self.D, self.H, n)
+        _on_device(fn, ("k", k), ("v", v), ("slot_mapping", slot_mapping))
+        self._need_device()
         _check(lib.pa_write_kv(self.handle, layer, _ptr(k), _ptr(v), _ptr(slot_mapping), n,
                                _stream(stream)), "pa_write_kv")
 
@@ -212,14 +247,28 @@ class Pool:
                context_lens: torch.Tensor, max_context_len: int, scale: float,
                partition_tokens: int = 0, out: torch.Tensor | None = None,
                workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
-        self._need_device()
+        fn, dt = "pa_decode", TORCH_DTYPE[self.dtype]
+        _need(q, fn, "q", dt, 3, self.D)
         S, Hq, _ = q.shape
+        _need(block_tables, fn, "block_tables", torch.int32, 2, min_rows=S)
+        _need(context_lens, fn, "context_lens", torch.int32, 1, min_rows=S)
+        if out is not None:
+            _need(out, fn, "out", dt, 3, self.D, Hq, S)
+        if workspace is not None:
+            _need(workspace, fn, "workspace")
+        _on_device(fn, ("q", q), ("block_tables", block_tables), ("context_lens", context_lens),
+                   ("out", out), ("workspace", workspace))
+        self._need_device()
         if out is None:
             out = torch.empty_like(q)
         if workspace is None:
             need = self.workspace_bytes(S, Hq, max_context_len, partition_tokens)
             workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-        wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+            if stream is not None:
+                # allocated on the current stream, used on `stream`: keep the
+                # caching allocator from reusing it before that work is done
+                workspace.record_stream(stream)
+        wsb = workspace.numel() * workspace.element_size()
         _check(lib.pa_decode(self.handle, layer, _ptr(q), S, Hq, _ptr(block_tables),
                              int(block_tables.shape[1]), _ptr(context_lens), int(max_context_len),
                              float(scale), int(partition_tokens), _ptr(workspace), wsb, _ptr(out),
@@ -231,8 +280,18 @@ class Pool:
                 scale: float, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
         """Causal attention of each sequence's newest tokens (rows
         query_start[i] .. query_start[i+1] - 1 of q) over its cached context."""
-        self._need_device()
+        fn, dt = "pa_prefill", TORCH_DTYPE[self.dtype]
+        _need(q, fn, "q", dt, 3, self.D)
         T, Hq, _ = q.shape
+        _need(query_start, fn, "query_start", torch.int32, 1, min_rows=1)
+        S = int(query_start.shape[0]) - 1
+        _need(block_tables, fn, "block_tables", torch.int32, 2, min_rows=S)
+        _need(context_lens, fn, "context_lens", torch.int32, 1, min_rows=S)
+        if out is not None:
+            _need(out, fn, "out", dt, 3, self.D, Hq, T)
+        _on_device(fn, ("q", q), ("query_start", query_start), ("block_tables", block_tables),
+                   ("context_lens", context_lens), ("out", out))
+        self._need_device()
         if out is None:
             out = torch.empty_like(q)
         _check(lib.pa_prefill(self.handle, layer, _ptr(q), int(query_start.shape[0]) - 1, Hq,
@@ -242,6 +301,8 @@ class Pool:
         return out
 
     def copy_blocks(self, pairs: torch.Tensor, stream=None):
+        _need(pairs, "pa_copy_blocks", "pairs", torch.int32, 2, last=2)
+        _on_device("pa_copy_blocks", ("pairs", pairs))
         self._need_device()
         _check(lib.pa_copy_blocks(self.handle, _ptr(pairs), int(pairs.shape[0]), _stream(stream)),
                "pa_copy_blocks")
@@ -303,6 +364,9 @@ class Pool:
         return self._swap(lib.pa_seq_swap_in, "pa_seq_swap_in", seq)
 
     def swap_blocks(self, pairs: torch.Tensor, host_buf: torch.Tensor, direction: int, stream=None):
+        _need(pairs, "pa_swap_blocks", "pairs", torch.int32, 2, last=2)
+        _need(host_buf, "pa_swap_blocks", "host_buf")
+        _on_device("pa_swap_blocks", ("pairs", pairs))
         self._need_device()
         _check(lib.pa_swap_blocks(self.handle, _ptr(pairs), int(pairs.shape[0]), _ptr(host_buf),
                                   host_buf.numel() * host_buf.element_size(), int(direction), _stream(stream)),

@@ -220,3 +220,46 @@ def test_decode_argument_checks_need_no_device():
     assert call(ws=(1 << 20) + 64) == "INVALID_ARG"
     assert call(q=(1 << 24) + 8) == "INVALID_ARG"
     assert call(scale=float("inf")) == "INVALID_ARG"
+
+
+def test_binding_rejects_mismatched_tensors_before_any_launch():
+    """The kernels trust shapes, dtypes and strides.  The binding checks every
+    tensor it hands over (dtype against the pool, head_dim, kv heads, rows,
+    contiguity, int32 index arrays, device) and raises before the library is
+    called.  Host-only: an allocator-only pool and CPU tensors, so every call
+    below ends in a PAError and nothing reaches a device."""
+    import torch
+    pool = pa.Pool(1, 8, 16, 2, 64, "bf16", device=None)
+    bf = torch.bfloat16
+    q = torch.zeros(3, 4, 64, dtype=bf)
+    t = torch.zeros(3, 4, dtype=torch.int32)
+    c = torch.ones(3, dtype=torch.int32)
+
+    def msg(f):
+        with pytest.raises(pa.PAError) as e:
+            f()
+        assert e.value.status == "INVALID_ARG"
+        return str(e.value)
+
+    assert "dtype" in msg(lambda: pool.decode(0, q.float(), t, c, 16, 0.1))
+    assert "last dimension" in msg(lambda: pool.decode(0, torch.zeros(3, 4, 128, dtype=bf), t, c, 16, 0.1))
+    assert "contiguous" in msg(lambda: pool.decode(0, q.transpose(0, 1), t, c, 16, 0.1))
+    assert "block_tables" in msg(lambda: pool.decode(0, q, t.long(), c, 16, 0.1))
+    assert "rows" in msg(lambda: pool.decode(0, q, t[:2], c, 16, 0.1))
+    assert "context_lens" in msg(lambda: pool.decode(0, q, t, c[:1], 16, 0.1))
+    assert "out" in msg(lambda: pool.decode(0, q, t, c, 16, 0.1, out=torch.zeros(3, 4, 64, dtype=torch.float16)))
+    assert "device tensor" in msg(lambda: pool.decode(0, q, t, c, 16, 0.1))
+
+    k = torch.zeros(5, 2, 64, dtype=bf)
+    s = torch.arange(5, dtype=torch.int32)
+    assert "dimension 1" in msg(lambda: pool.write_kv(0, torch.zeros(5, 3, 64, dtype=bf), k, s))
+    assert "rows" in msg(lambda: pool.write_kv(0, k, k, torch.arange(6, dtype=torch.int32)))
+    assert "slot_mapping" in msg(lambda: pool.write_kv(0, k, k, s.long()))
+    assert "dtype" in msg(lambda: pool.write_kv(0, k.half(), k, s))
+    assert "device tensor" in msg(lambda: pool.write_kv(0, k, k, s))
+
+    qs = torch.tensor([0, 2, 5], dtype=torch.int32)
+    assert "last dimension" in msg(lambda: pool.prefill(0, torch.zeros(5, 4, 32, dtype=bf), qs, 3, t[:2], c[:2], 16, 0.1))
+    assert "query_start" in msg(lambda: pool.prefill(0, q, qs.long(), 3, t[:2], c[:2], 16, 0.1))
+    assert "device tensor" in msg(lambda: pool.prefill(0, torch.zeros(5, 4, 64, dtype=bf), qs, 3, t[:2], c[:2], 16, 0.1))
+    assert "pairs" in msg(lambda: pool.copy_blocks(torch.zeros(2, 3, dtype=torch.int32)))

@@ -192,7 +192,8 @@ def test_physical_relabeling_is_bit_identical():
 
 def test_contiguous_layout_equals_scattered():
     """Identity tables (blocks in logical order) give the same bits as a random
-    placement: paging changes only where K/V sit."""
+    placement, and both match the oracle element by element: paging changes
+    only where K/V sit."""
     w = W.scaled_down(W.llama3_8b(), 8, 900)
     ident = np.full_like(w.block_tables, -1)
     off = 0
@@ -201,11 +202,13 @@ def test_contiguous_layout_equals_scattered():
         ident[i, :nb] = np.arange(off, off + nb)
         off += nb
     outs = []
-    for tables in (w.block_tables, ident):
+    ref = U.oracle_rows(w, range(w.num_seqs))
+    for name, tables in (("scattered", w.block_tables), ("consecutive", ident)):
         pool = U.make_pool(w)
         U.fill_pool(pool, w, tables=tables)
         q, t, c = U.device_inputs(w, tables=tables)
         outs.append(U.run_decode(pool, w, q, t, c).cpu())
+        U.check_close(U.out_f64(outs[-1]), ref, w.dtype, f"{name} blocks")
     assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
 
 
@@ -314,7 +317,7 @@ def test_argument_errors():
 FULL = {
     "opt13b": (W.opt13b, 8),
     "llama3_8b": (W.llama3_8b, 10),
-    "long_ctx": (W.long_ctx, 2),
+    "long_ctx": (W.long_ctx, 8),   # every sequence of the batch
 }
 
 
@@ -331,8 +334,11 @@ def test_decode_full_size_sampled(name):
     assert np.isfinite(got).all()
     order = np.argsort(w.context_lens)
     rng = np.random.default_rng(0)
-    pick = sorted(set([int(order[0]), int(order[-1])] +
-                      rng.choice(w.num_seqs, nsample - 2, replace=False).tolist()))
+    if nsample >= w.num_seqs:
+        pick = list(range(w.num_seqs))
+    else:
+        pick = sorted(set([int(order[0]), int(order[-1])] +
+                          rng.choice(w.num_seqs, nsample - 2, replace=False).tolist()))
     U.check_close(got[pick], U.oracle_rows(w, pick), w.dtype, f"{name} seqs {pick}")
     # cache placement of the sampled sequences follows the documented layout
     from oracle import layout as LY

@@ -336,3 +336,97 @@ def test_staged_lse_merge_equals_unsplit():
         assert np.max(np.abs(staged() - ref)) <= 1e-12, (T, P)
         if len(states) > 4:  # two or more groups: the group sums matter
             assert np.max(np.abs(staged(carry_sum=False) - ref)) > 1e-6, (T, P)
+
+
+# --------------------------------------------------- storage widening -------
+#
+# Every other attention pin feeds its inputs through ``A.to_f64``, so a slip
+# there (a wrong shift, a lost sign bit, the wrong half of the word) would pass
+# them all.  These pins fix the widening from outside the oracle: bfloat16 is
+# the upper 16 bits of an IEEE-754 binary32 (1 sign, 8 exponent, 7 fraction
+# bits), binary16 has 1/5/10 bits; the values below follow from those formats
+# alone, and the exhaustive check compares with torch's own bfloat16 type.
+
+def _bf16_fixed_points():
+    return [
+        (0x3F80, 1.0), (0xBF80, -1.0), (0xC000, -2.0), (0x4049, 3.140625),
+        (0x3F81, 1.0 + 2.0 ** -7), (0x0080, 2.0 ** -126),           # smallest normal
+        (0x0001, 2.0 ** -133), (0x8001, -(2.0 ** -133)),            # smallest subnormal
+        (0x7F7F, (2.0 - 2.0 ** -7) * 2.0 ** 127),                   # largest finite
+        (0x7F80, math.inf), (0xFF80, -math.inf), (0x0000, 0.0),
+    ]
+
+
+def _f16_fixed_points():
+    return [
+        (0x3C00, 1.0), (0xC000, -2.0), (0x0001, 2.0 ** -24), (0x0400, 2.0 ** -14),
+        (0x7BFF, 65504.0), (0x3555, 0.333251953125), (0xFC00, -math.inf),
+    ]
+
+
+def _widening_failures(fn):
+    """Names of the widening pins that ``fn(bits_or_values, dtype)`` fails."""
+    import torch
+    bad = []
+    bits = np.array([b for b, _ in _bf16_fixed_points()], dtype=np.uint16)
+    want = np.array([v for _, v in _bf16_fixed_points()])
+    got = fn(bits, "bf16")
+    if got.dtype != np.float64 or not np.array_equal(got, want):
+        bad.append("bf16 fixed points")
+    # -0.0 keeps its sign
+    if not np.signbit(fn(np.array([0x8000], dtype=np.uint16), "bf16")[0]):
+        bad.append("bf16 negative zero")
+    # every bf16 pattern against torch's bfloat16 -> float64 conversion
+    allb = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    ref = torch.from_numpy(allb.view(np.int16).copy()).view(torch.bfloat16).double().numpy()
+    with np.errstate(invalid="ignore"):
+        got = fn(allb, "bf16")
+    nan = np.isnan(ref)
+    if not (np.array_equal(np.isnan(got), nan) and np.array_equal(got[~nan], ref[~nan])):
+        bad.append("bf16 exhaustive")
+    hb = np.array([b for b, _ in _f16_fixed_points()], dtype=np.uint16)
+    hv = np.array([v for _, v in _f16_fixed_points()])
+    if not np.array_equal(fn(hb.view(np.float16), "f16"), hv):
+        bad.append("f16 fixed points")
+    f32 = np.array([1.0, -2.5, 2.0 ** -149, 3.4028234663852886e38], dtype=np.float32)
+    if not np.array_equal(fn(f32, "f32"), f32.astype(np.float64)):
+        bad.append("f32 identity")
+    return bad
+
+
+def test_storage_widening_is_exact():
+    assert _widening_failures(A.to_f64) == []
+
+
+def _widening_mutants():
+    def shift_15(x, dt):
+        if dt == "bf16":
+            return (np.asarray(x, dtype=np.uint16).astype(np.uint32) << 15).view(np.float32).astype(np.float64)
+        return A.to_f64(x, dt)
+
+    def lost_sign(x, dt):
+        if dt == "bf16":
+            return A.to_f64(np.asarray(x, dtype=np.uint16) & np.uint16(0x7FFF), dt)
+        return A.to_f64(x, dt)
+
+    def low_half(x, dt):  # the bits placed in the low half of the word
+        if dt == "bf16":
+            return np.asarray(x, dtype=np.uint16).astype(np.uint32).view(np.float32).astype(np.float64)
+        return A.to_f64(x, dt)
+
+    def via_f16(x, dt):  # bf16 bits read as binary16
+        if dt == "bf16":
+            return np.asarray(x, dtype=np.uint16).view(np.float16).astype(np.float64)
+        return A.to_f64(x, dt)
+
+    def rounded_f16(x, dt):  # f16 widened through a lossy path
+        if dt == "f16":
+            return np.asarray(x).astype(np.float64).round(3)
+        return A.to_f64(x, dt)
+
+    return [shift_15, lost_sign, low_half, via_f16, rounded_f16]
+
+
+@pytest.mark.parametrize("mutant", _widening_mutants(), ids=lambda f: f.__name__)
+def test_widening_slips_are_caught(mutant):
+    assert _widening_failures(mutant) != []
