@@ -195,7 +195,11 @@ int pa_prefill(const pa_pool* pool, int layer, const void* q, int num_seqs, int 
                const int32_t* block_tables, int max_blocks_per_seq, const int32_t* context_lens,
                int max_context_len, float scale, void* out, void* stream);
 
-/* Copy whole blocks (every layer, head, K and V) for copy-on-write.
+/* Copy whole blocks (every layer, head, K and V) for copy-on-write: a block
+ * that several sequences share is copied before one of them modifies it
+ * ("PagedAttention: paging the KV cache like an OS pages memory", "How it
+ * works"; glossary entry "Copy-on-Write" of "PagedAttention and KV Cache
+ * Compression").  pa_seq_append reports the pairs to copy.
  *   pairs  device int32 [n, 2] of (source, destination) block ids.
  * Run it before the pa_write_kv that writes into the destinations.  Sources
  * and destinations must be distinct. */
