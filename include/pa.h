@@ -131,9 +131,11 @@ int pa_write_kv(pa_pool* pool, int layer, const void* k, const void* v,
                 const int32_t* slot_mapping, int num_tokens, void* stream);
 
 /* Device workspace bytes pa_decode needs: a work-item list (one entry per
- * (sequence, partition) of up to max_context_len tokens) and, when contexts
- * can span several partitions, float32 partial outputs plus running max and
- * sum per query head and partition.  Always > 0 for valid arguments.
+ * (sequence, partition) of up to max_context_len tokens, plus one for a split
+ * at a shared prefix's end), per-sequence partition counts and shared groups,
+ * and, when contexts can span several partitions, float32 partial outputs
+ * plus running max and sum per query head and partition.  Always > 0 for
+ * valid arguments.
  * pa_decode initialises what it needs itself; calls that share one workspace
  * must not overlap. */
 size_t pa_decode_workspace_bytes(const pa_pool* pool, int num_seqs, int num_q_heads,
@@ -161,10 +163,17 @@ size_t pa_decode_workspace_bytes(const pa_pool* pool, int num_seqs, int num_q_he
  *   partition_tokens   0 = automatic, else a multiple of block_size and of 16
  *   workspace          device, >= pa_decode_workspace_bytes(...) bytes,
  *                      256-byte aligned; contents need no initialisation
- * K/V are read with streaming (non-temporal) loads, or with cached loads when
- * at least a quarter of the pool's used blocks are shared (reference count > 1
- * in its block manager), so that the other readers of a shared block find it
- * in L2 or the Infinity Cache; the result is the same either way.
+ * Shared prefixes ("Support for Prefix Sharing"; blocks shared by reference
+ * count, "How it works"): when the pool's block manager holds a shared block
+ * (reference count > 1), the partition size is automatic, contexts can span
+ * several partitions, num_seqs <= 1024 and G <= 8, the call first groups the
+ * sequences whose tables begin with the same full block, verifies id by id
+ * how many leading full blocks each shares with the group's lowest sequence
+ * (at most 2048 64-entry comparisons per call), and reads every common
+ * prefix of at least 256 tokens once for up to min(4, 16 / G) sequences
+ * together.  Each sequence is then split at its shared prefix's end, which
+ * changes only float32 rounding.  Tables from any source stay correct: only
+ * verified equal ids are shared.
  * Asynchronous on `stream`; the result is ready when the stream reaches it. */
 int pa_decode(const pa_pool* pool, int layer, const void* q, int num_seqs, int num_q_heads,
               const int32_t* block_tables, int max_blocks_per_seq,

@@ -271,18 +271,21 @@ int pa_decode(const pa_pool* pool, int layer, const void* q, int num_seqs, int n
     p.P = P;
     p.auto_partition = automatic ? 1 : 0;
     p.max_parts = max_parts;
+    p.ws_stride = wl.stride;
     char* ws = static_cast<char*>(workspace);
     p.header = reinterpret_cast<int32_t*>(ws + wl.header_off);
     p.items = reinterpret_cast<int4*>(ws + wl.items_off);
+    p.seq_np = reinterpret_cast<int32_t*>(ws + wl.np_off);
+    p.groups = reinterpret_cast<int4*>(ws + wl.groups_off);
     p.ws_o = max_parts > 1 ? reinterpret_cast<float*>(ws + wl.o_off) : nullptr;
     p.ws_ml = max_parts > 1 ? reinterpret_cast<float*>(ws + wl.ml_off) : nullptr;
-    // Streaming loads suit K/V that one sequence reads once; when the block
-    // manager holds many shared blocks (forked branches, cached prefixes),
-    // cached loads let the other readers find them in L2 or the Infinity
-    // Cache.  Measured on MI355X: streaming is 9% faster on unshared batches,
-    // cached 14% faster on four branches per shared prefix.
-    const int64_t used = pool->alloc.num_blocks() - static_cast<int64_t>(pool->alloc.free_stack().size());
-    p.keep_in_cache = (used > 0 && 4 * pool->alloc.shared_blocks() >= used) ? 1 : 0;
+    // Sequences can share blocks only if the block manager holds a block
+    // with more than one reference (forked branches, cached prefixes).  Then
+    // the plan looks for sequences of this batch whose tables begin with the
+    // same blocks and reads each such common prefix once for all of them;
+    // otherwise it keeps the plain plan.  The plan itself verifies every
+    // shared block id, so tables from any source stay correct either way.
+    p.share = pool->alloc.shared_blocks() > 0 ? 1 : 0;
     hipError_t e = pa::launch_decode(p, d.dtype, d.head_dim, s);
     return e == hipSuccess ? PA_OK : hip_fail(e, "decode launch");
   });

@@ -99,16 +99,34 @@ constexpr int kWorkgroupsPerCU = PA_WG_PER_CU;
 // Work items.
 // ---------------------------------------------------------------------------
 
+// Sequences one shared work item covers at most (their G query heads each
+// take a column of the 16-wide score tile).
+constexpr int kShareMaxMembers = 4;
+
 // One work item as one wave of the workgroup sees it (all values uniform).
+// An item covers the tokens [start, start + ntok) of one sequence or, with
+// the sharing plan, possibly of a prefix that several sequences share (x < 0:
+// shared group ~x).  The members of a shared group are looked up where they
+// are needed -- query rows at the start, outputs at the end -- so that no
+// more registers stay live through the item than for a single sequence.
 struct Item {
-  int i, j, h;     // sequence, work item within the sequence, kv head
+  int i, j, h;     // sequence (a shared group's first member), partition slot, kv head
   int ctx;         // context length (clamped)
   int start;       // first token of the item
   int ntok;        // tokens in the item
   int u0, u1;      // this wave's run of 16-token units
   int np;          // work items of the sequence
-  const int32_t* trow;
+  int x;           // record's first field: the sequence, or ~group with the sharing plan
+  int cols;        // query-head columns of the score tile: G per member sequence
+  const int32_t* trow;  // block-table row the K/V ids are read from
 };
+
+__device__ __forceinline__ void split_units(Item& it, int per_fixed, int wave) {
+  const int nunits = (it.ntok + 15) >> 4;
+  const int per = per_fixed > 0 ? per_fixed : (nunits + kWaves - 1) / kWaves;
+  it.u0 = wave * per;
+  it.u1 = it.u0 + per < nunits ? it.u0 + per : nunits;
+}
 
 // rec = (sequence, item, clamped context, items of the sequence) as written
 // by plan_kernel; an item holds PI tokens.  With group == 1 the four waves
@@ -125,10 +143,38 @@ __device__ __forceinline__ Item make_item(const DecodeParams& p, int4 rec, int h
   it.start = it.j * PI;
   const int left = it.ctx - it.start;
   it.ntok = left < PI ? (left > 0 ? left : 0) : PI;
-  const int nunits = (it.ntok + 15) >> 4;
-  const int per = group > 1 ? (PI / group) >> 4 : (nunits + kWaves - 1) / kWaves;
-  it.u0 = wave * per;
-  it.u1 = it.u0 + per < nunits ? it.u0 + per : nunits;
+  split_units(it, group > 1 ? (PI / group) >> 4 : 0, wave);
+  it.trow = p.tables + static_cast<size_t>(it.i) * p.max_blocks;
+  it.x = it.i;
+  it.cols = p.G;
+  return it;
+}
+
+// Member sequences of an item of the sharing plan (-1 = none).
+__device__ __forceinline__ int4 item_members(const Item& it, const int4* __restrict__ groups) {
+  if (it.x >= 0) return make_int4(it.x, -1, -1, -1);
+  const int4 g = groups[~it.x];
+  return make_int4(rfl(g.x), rfl(g.y), rfl(g.z), rfl(g.w));
+}
+
+// Sharing plan: rec = (sequence, partition slot, first token, end token), or
+// (~group, ...) for an item over a prefix that the group's members share;
+// groups[g] lists those members.
+__device__ __forceinline__ Item make_item_share(const DecodeParams& p, int4 rec, int h, int wave,
+                                                const int4* __restrict__ groups) {
+  Item it;
+  it.x = rfl(rec.x);
+  it.j = rfl(rec.y);
+  it.start = rfl(rec.z);
+  const int end = rfl(rec.w);
+  it.ntok = end > it.start ? end - it.start : 0;
+  it.ctx = end;
+  it.h = h;
+  it.np = 0;  // per member, read where the item's states are written
+  split_units(it, 0, wave);
+  const int4 m = item_members(it, groups);
+  it.i = m.x;
+  it.cols = (1 + (m.y >= 0) + (m.z >= 0) + (m.w >= 0)) * p.G;
   it.trow = p.tables + static_cast<size_t>(it.i) * p.max_blocks;
   return it;
 }
@@ -163,29 +209,49 @@ __device__ __forceinline__ void store_out(const DecodeParams& p, size_t row, int
   static_cast<B*>(p.out)[row * D + d] = static_cast<B>(to_storage<T>(o));
 }
 
-template <typename T, int D, int GMAX>
-__device__ __forceinline__ void finish_partition(const DecodeParams& p, MergeSmem<D, GMAX>& sm, const Item& it) {
+template <typename T, int D, int GMAX, bool kShare = false>
+__device__ __forceinline__ void finish_partition(const DecodeParams& p, MergeSmem<D, GMAX>& sm, const Item& it,
+                                                 const int4* __restrict__ groups = nullptr,
+                                                 const int32_t* __restrict__ seq_np = nullptr) {
+  // Sharing plan: column c is query head c % G of member c / G, and each
+  // member has its own number of states.
+  int4 mem = make_int4(it.i, -1, -1, -1), mnp = make_int4(it.np, -1, -1, -1);
+  if constexpr (kShare) {
+    mem = item_members(it, groups);
+    mnp.x = rfl(seq_np[mem.x]);
+    mnp.y = mem.y >= 0 ? rfl(seq_np[mem.y]) : -1;
+    mnp.z = mem.z >= 0 ? rfl(seq_np[mem.z]) : -1;
+    mnp.w = mem.w >= 0 ? rfl(seq_np[mem.w]) : -1;
+  }
   __syncthreads();
   const int G = p.G;
-  for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
-    const int g = idx / D, d = idx - g * D;
-    float M = sm.m[0][g];
+  const int rows = kShare ? it.cols : G;
+  for (int idx = threadIdx.x; idx < rows * D; idx += kThreads) {
+    const int c = idx / D, d = idx - c * D;
+    float M = sm.m[0][c];
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, sm.m[w][g]);
+    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, sm.m[w][c]);
     float L = 0.f, O = 0.f;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
-      const float mw = sm.m[w][g];
+      const float mw = sm.m[w][c];
       const float f = (mw == kNegInf) ? 0.f : fast_exp2(mw - M);
-      L += f * sm.l[w][g];
-      O += f * sm.o[w][g][d];
+      L += f * sm.l[w][c];
+      O += f * sm.o[w][c][d];
     }
-    const size_t row = static_cast<size_t>(it.i) * p.Hq + it.h * G + g;
+    int seq = it.i, np = it.np, g = c;
+    if constexpr (kShare) {
+      const int m = c / G;
+      g = c - m * G;
+      seq = m == 0 ? mem.x : m == 1 ? mem.y : m == 2 ? mem.z : mem.w;
+      np = m == 0 ? mnp.x : m == 1 ? mnp.y : m == 2 ? mnp.z : mnp.w;
+    }
+    const size_t row = static_cast<size_t>(seq) * p.Hq + it.h * G + g;
     const float o = (L > 0.f) ? O / L : 0.f;
-    if (it.np == 1) {
+    if (np == 1) {
       store_out<T>(p, row, d, D, o);
     } else {
-      const size_t e = row * p.max_parts + it.j;
+      const size_t e = row * p.ws_stride + it.j;
       p.ws_o[e * D + d] = o;
       if (d == 0) {
         p.ws_ml[2 * e] = M;
@@ -334,6 +400,282 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeParams p) {
 }
 
 // ---------------------------------------------------------------------------
+// Sharing plan: one workgroup, one sequence per thread.
+//
+// Sequences that share blocks (forked branches, cached prompt prefixes) hold
+// the same block ids at the start of their tables ("Support for Prefix
+// Sharing"; blocks are shared by reference count and only the storage is
+// shared, "How it works").  The plan finds, for each group of sequences whose
+// tables begin with the same block, the full blocks every member has in
+// common with the group's lowest sequence (checked id by id), and cuts the
+// group into subgroups of up to share_nmax members.  A subgroup's common
+// prefix becomes work items of its own whose score tile holds the query heads
+// of all its members, so those K/V tiles are read from HBM once for the
+// subgroup; each member's remaining tokens are ordinary items.  The states of
+// both kinds are combined by the merge kernel like any partitions.
+//
+// Records: (sequence, partition slot, first token, end token) for a
+// sequence's own tokens, (~subgroup, slot, first, end) for a shared prefix.
+// seq_np[i] is the number of states of sequence i; groups[g] its members.
+// ---------------------------------------------------------------------------
+constexpr int kShareMaxSeqs = kPlanThreads;  // batches up to this size are examined
+constexpr int kShareHashBits = 11;
+constexpr int kShareHash = 1 << kShareHashBits;  // open addressing at load factor <= 1/2
+static_assert(kShareHash >= 2 * kShareMaxSeqs, "hash load factor");
+static_assert(kShareHash >= kPlanBins, "the hash arrays hold the size bins afterwards");
+constexpr int kMinSharedTokens = 256;  // shorter common prefixes are read per sequence
+#ifndef PA_SHARE_ITEMS_PER_WG
+#define PA_SHARE_ITEMS_PER_WG 2
+#endif
+constexpr int kShareItemsPerWorkgroup = PA_SHARE_ITEMS_PER_WG;
+constexpr int kCmpBatch = 8;           // comparison tasks whose loads a wave issues together
+constexpr int kMaxCmpTasks = kShareHash;  // 64-entry comparison tasks checked per call
+
+// Exclusive prefix sum of one value per thread in thread order; `total`
+// receives the sum.  Ends with a barrier, so `wsum` can be reused at once.
+__device__ __forceinline__ int block_scan(int v, int* wsum, int& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) wsum[wave] = x;
+  __syncthreads();
+  int before = 0, all = 0;
+  for (int w = 0; w < kPlanThreads / 64; ++w) {
+    const int s = wsum[w];
+    before += w < wave ? s : 0;
+    all += s;
+  }
+  __syncthreads();
+  total = all;
+  return before + x - v;
+}
+
+__global__ __launch_bounds__(kPlanThreads) void plan_share_kernel(DecodeParams p) {
+  __shared__ int hk[kShareHash];          // first block ids (-1 = empty), then size bins
+  __shared__ int hv[kShareHash];          // lowest sequence per first block, then bin offsets
+  __shared__ int lead[kShareMaxSeqs];     // lowest sequence of each sequence's group
+  __shared__ int gcount[kShareMaxSeqs];   // sequences beside the leader in its group
+  __shared__ int cpre[kShareMaxSeqs];     // full blocks in common with the leader
+  __shared__ int sbase[kShareMaxSeqs];    // first subgroup id of a leader's group
+  __shared__ int mlist[kShareMaxSeqs];    // the non-leaders, in index order
+  __shared__ int mcap[kShareMaxSeqs];     // blocks to compare for each of them
+  __shared__ int tbase[kShareMaxSeqs];    // first comparison task of each of them
+  __shared__ int sls[kShareMaxSeqs / 2];  // shared full blocks of each subgroup
+  __shared__ int smem[kShareMaxSeqs / 2][kShareMaxMembers];
+  __shared__ int wsum[kPlanThreads / 64];
+  __shared__ long long wtok[kPlanThreads / 64];
+  __shared__ int sP, sact;
+  const int t = threadIdx.x, lane = t & 63, wave = rfl(t >> 6);
+  const int bs = p.bs, nmax = p.share_nmax;
+  const bool live = t < p.S;
+  // the first table entry is read beside the length (every row has one)
+  const int b0 = live ? p.tables[static_cast<size_t>(t) * p.max_blocks] : -1;
+  const int c = live ? clamp_ctx(p, t) : 0;
+  const int nfb = c / bs;  // full blocks
+  const bool keyed = nfb > 0 && b0 >= 0 && b0 < p.N;
+  for (int k = t; k < kShareHash; k += kPlanThreads) {
+    hk[k] = -1;
+    hv[k] = 0x7fffffff;
+  }
+  gcount[t] = 0;
+  cpre[t] = nfb;
+  __syncthreads();
+
+  // 1. Groups: sequences whose first block is the same physical block.
+  int slot = 0;
+  if (keyed) {
+    uint32_t hh = (static_cast<uint32_t>(b0) * 2654435761u) >> (32 - kShareHashBits);
+    for (;;) {  // ends: at most kShareMaxSeqs keys in kShareHash slots
+      const int old = atomicCAS(&hk[hh], -1, b0);
+      if (old == -1 || old == b0) break;
+      hh = (hh + 1) & (kShareHash - 1);
+    }
+    slot = static_cast<int>(hh);
+    atomicMin(&hv[slot], t);
+  }
+  __syncthreads();
+  const int L = keyed ? hv[slot] : t;
+  lead[t] = L;
+  if (L != t) atomicAdd(&gcount[L], 1);
+  __syncthreads();
+
+  // 2. Rank in the group by sequence index; subgroups of nmax consecutive
+  //    ranks (a lone last member stays on its own).
+  int rank = 0;
+  if (L != t) {
+    rank = 1;
+    for (int j = L + 1; j < t; ++j) rank += lead[j] == L ? 1 : 0;
+  }
+  const int gn = live ? gcount[L] + 1 : 0;
+  const int gsub = gn >= 2 ? gn / nmax + (gn % nmax >= 2 ? 1 : 0) : 0;
+  // one scan for both: subgroups per leader (low 16 bits), members (high)
+  const bool member = live && L != t;
+  int both = 0;
+  const int sc = block_scan((L == t ? gsub : 0) | (member ? 1 << 16 : 0), wsum, both);
+  const int nsub_total = both & 0xffff, nmem = both >> 16;
+  sbase[t] = sc & 0xffff;
+  if (member) mlist[sc >> 16] = t;
+  for (int k = t; k < nsub_total; k += kPlanThreads) {
+    sls[k] = 0x7fffffff;
+#pragma unroll
+    for (int m = 0; m < kShareMaxMembers; ++m) smem[k][m] = -1;
+  }
+  __syncthreads();
+  const int sub = rank / nmax;
+  const int sid = (live && sub < gsub) ? sbase[L] + sub : -1;
+  if (sid >= 0) smem[sid][rank - sub * nmax] = t;
+
+  // 3. Each non-leader's table against its leader's, over the full blocks
+  //    both hold: tasks of 64 entries (one per lane), each task's member
+  //    found in an owner array (the hash arrays are free now), the loads of
+  //    kCmpBatch tasks per wave issued together.  At most kMaxCmpTasks tasks
+  //    are checked; a member whose tasks lie beyond shares only what was
+  //    checked.
+  int ntk = 0, cap = 0;
+  if (t < nmem) {
+    const int m = mlist[t];
+    cap = min(cpre[m], cpre[lead[m]]);
+    ntk = (cap + 63) / 64;
+  }
+  int ntask = 0;
+  const int tb = block_scan(ntk, wsum, ntask);
+  int* towner = hk;
+  if (t < nmem) {
+    const int e = min(tb + ntk, kMaxCmpTasks);
+    for (int k = tb; k < e; ++k) towner[k] = t;
+    cap = min(cap, max(e - tb, 0) * 64);
+    mcap[t] = cap;
+    tbase[t] = tb;
+    cpre[mlist[t]] = cap;
+  }
+  __syncthreads();
+  ntask = min(ntask, kMaxCmpTasks);
+  constexpr int kWavesPlan = kPlanThreads / 64;
+  for (int base = wave; base < ntask; base += kWavesPlan * kCmpBatch) {
+    // Lane r < kCmpBatch looks up task base + r * kWavesPlan (three LDS round
+    // trips for the whole batch); the values are then broadcast by readlane.
+    const int mtk = base + (lane % kCmpBatch) * kWavesPlan;
+    const int own = towner[mtk < ntask ? mtk : 0];
+    const int mm = mlist[own];
+    const int ml = lead[mm];
+    const int mcp = mtk < ntask ? mcap[own] : 0;
+    const int mk0 = (mtk - tbase[own]) * 64;
+    int tm[kCmpBatch], tk0[kCmpBatch], tcap[kCmpBatch], va[kCmpBatch], vb[kCmpBatch];
+#pragma unroll
+    for (int r = 0; r < kCmpBatch; ++r) {
+      tm[r] = __builtin_amdgcn_readlane(mm, r);
+      tk0[r] = __builtin_amdgcn_readlane(mk0, r);
+      tcap[r] = __builtin_amdgcn_readlane(mcp, r);
+      const int tl = __builtin_amdgcn_readlane(ml, r);
+      const int k = tk0[r] + lane;
+      const int kk = k < tcap[r] ? k : 0;  // tcap <= both rows' full blocks <= max_blocks
+      va[r] = p.tables[static_cast<size_t>(tm[r]) * p.max_blocks + kk];
+      vb[r] = p.tables[static_cast<size_t>(tl) * p.max_blocks + kk];
+    }
+#pragma unroll
+    for (int r = 0; r < kCmpBatch; ++r) {
+      const uint64_t bad = __builtin_amdgcn_ballot_w64(tk0[r] + lane < tcap[r] && va[r] != vb[r]);
+      if (lane == 0 && bad != 0) atomicMin(&cpre[tm[r]], tk0[r] + static_cast<int>(__builtin_ctzll(bad)));
+    }
+  }
+  __syncthreads();
+
+  // 4. A subgroup shares the full blocks all its members hold in common with
+  //    the leader (the leader's own full blocks when it is a member).
+  if (sid >= 0) atomicMin(&sls[sid], cpre[t]);
+  __syncthreads();
+  int Ls = 0;
+  bool head = false;
+  if (sid >= 0 && sls[sid] * bs >= kMinSharedTokens) {
+    Ls = sls[sid] * bs;
+    head = rank == sub * nmax;
+  }
+
+  // 5. Partition size from the work that remains: each sequence's own
+  //    tokens once and each shared prefix once.
+  long long tok = live ? c - Ls : 0;
+  if (head) tok += Ls;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) tok += __shfl_xor(tok, o);
+  if (lane == 0) wtok[wave] = tok;
+  __syncthreads();
+  if (wave == 0) {
+    long long total = lane < kPlanThreads / 64 ? wtok[lane] : 0;
+#pragma unroll
+    for (int o = 8; o >= 1; o >>= 1) total += __shfl_xor(total, o);
+    total *= p.H;
+    // 32-bit arithmetic once the cap is known not to apply
+    const int cap_p = kMaxAutoPartition / bs * bs;
+    const int slots = p.grid * kShareItemsPerWorkgroup;
+    int P = cap_p;
+    if (total <= static_cast<long long>(slots) * cap_p) {
+      const int per = (static_cast<int>(total) + slots - 1) / slots;
+      P = (per + bs - 1) / bs * bs;
+      P = P > cap_p ? cap_p : P;
+    }
+    if (lane == 0) sP = P < p.P ? p.P : P;
+  }
+  int* cnt = hk;  // the hash is no longer read
+  int* off = hv;
+  for (int b = t; b < kPlanBins; b += kPlanThreads) cnt[b] = 0;
+  if (t == 0) sact = 0;
+  __syncthreads();
+  const int P = sP;
+  const int top = (P >> 4) - 1 < kPlanBins - 1 ? (P >> 4) - 1 : kPlanBins - 1;
+  auto bin_of = [&](int ntok) {
+    const int units = (ntok + 15) >> 4;
+    const int b = units > 0 ? units - 1 : 0;
+    return b < top ? b : top;
+  };
+
+  // 6. Items: the sequence's own tokens [Ls, c) in P-token pieces (an empty
+  //    context still gets one item, which writes zeros), and for a
+  //    subgroup's first member the shared prefix [0, Ls).
+  const int tail = c - Ls;
+  const int nsh = Ls > 0 ? (Ls + P - 1) / P : 0;
+  const int tfull = tail / P, trem = tail - tfull * P;
+  const bool tlast = trem > 0 || (live && c == 0);
+  if (live) p.seq_np[t] = nsh + tfull + (tlast ? 1 : 0);
+  const int sfull = head ? Ls / P : 0, srem = head ? Ls - sfull * P : 0;
+  if (tfull + sfull > 0) atomicAdd(&cnt[bin_of(P)], tfull + sfull);
+  if (tlast) atomicAdd(&cnt[bin_of(trem)], 1);
+  if (srem > 0) atomicAdd(&cnt[bin_of(srem)], 1);
+  if (head) atomicAdd(&sact, 1);
+  __syncthreads();
+  // bin offsets in descending size order: thread t owns bin kPlanBins - 1 - t
+  static_assert(kPlanBins == kPlanThreads, "one bin per thread");
+  const int bin = kPlanBins - 1 - t;
+  int nitems = 0;
+  const int o = block_scan(cnt[bin], wsum, nitems);
+  const int nactive = sact;
+  off[bin] = o;
+  if (t == 0) {
+    p.header[0] = nitems;
+    p.header[1] = p.first_taken;
+    p.header[2] = P;
+    p.header[3] = nactive;
+  }
+  __syncthreads();
+  if (tfull > 0) {
+    const int base = atomicAdd(&off[bin_of(P)], tfull);
+    for (int j = 0; j < tfull; ++j) p.items[base + j] = make_int4(t, nsh + j, Ls + j * P, Ls + (j + 1) * P);
+  }
+  if (tlast) p.items[atomicAdd(&off[bin_of(trem)], 1)] = make_int4(t, nsh + tfull, Ls + tfull * P, c);
+  if (head) {
+    p.groups[sid] = make_int4(smem[sid][0], smem[sid][1], smem[sid][2], smem[sid][3]);
+    if (sfull > 0) {
+      const int base = atomicAdd(&off[bin_of(P)], sfull);
+      for (int j = 0; j < sfull; ++j) p.items[base + j] = make_int4(~sid, j, j * P, (j + 1) * P);
+    }
+    if (srem > 0) p.items[atomicAdd(&off[bin_of(srem)], 1)] = make_int4(~sid, sfull, sfull * P, Ls);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // MFMA path: 3 <= G <= 16 query heads per kv head (GM = G rounded up to 4, 8
 // or 16 sizes the LDS merge).
 // ---------------------------------------------------------------------------
@@ -364,6 +706,21 @@ struct MfmaPath {
     for (int c = 0; c < NCH; ++c)
       q.b[c] = (col < G) ? *reinterpret_cast<const uint4*>(qbase + ((c * 4 + grp) * E) * kBytes)
                          : make_uint4(0, 0, 0, 0);
+  }
+
+  // Sharing plan: column col is query head col % G of member col / G.
+  __device__ static void load_q_members(Q& q, const DecodeParams& p, const Item& it, int4 mem, int lane) {
+    const int col = lane & 15, grp = lane >> 4;
+    const int G = p.G;
+    const int m = col / G, g = col - m * G;
+    const int seq = m == 0 ? mem.x : m == 1 ? mem.y : m == 2 ? mem.z : mem.w;
+    const bool live = col < it.cols;
+    const char* qbase = static_cast<const char*>(p.q) +
+                        (static_cast<size_t>(live ? seq : 0) * p.Hq + static_cast<size_t>(it.h) * G + g) * D * kBytes;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c)
+      q.b[c] = live ? *reinterpret_cast<const uint4*>(qbase + ((c * 4 + grp) * E) * kBytes)
+                    : make_uint4(0, 0, 0, 0);
   }
 
   __device__ static void reset(State& s) {
@@ -625,8 +982,10 @@ struct ValuPath {
 // whichever workgroup finishes first (measured: holding two indices per
 // workgroup costs more in the tail than it saves between items there).
 // ---------------------------------------------------------------------------
-template <typename Path, typename T, int D, bool kDeep, bool kKeep>
-__global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p, const int4* __restrict__ items) {
+template <typename Path, typename T, int D, bool kDeep, bool kShare>
+__global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p, const int4* __restrict__ items,
+                                                          const int4* __restrict__ groups,
+                                                          const int32_t* __restrict__ seq_np) {
   constexpr int kBytes = T::kBytes;
   constexpr int NCH = Path::NCH;
   constexpr int PF = kPrefetch;
@@ -655,10 +1014,18 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p, const 
   if (cur >= total) return;
 
   const int group = p.group;
-  Item it = make_item(p, record(cur), cur % H, P, group, wave);
+  auto item_at = [&](int w) {
+    if constexpr (kShare) return make_item_share(p, record(w), w % H, wave, groups);
+    else return make_item(p, record(w), w % H, P, group, wave);
+  };
+  auto load_q = [&](typename Path::Q& qq, const Item& ii) {
+    if constexpr (kShare) Path::load_q_members(qq, p, ii, item_members(ii, groups), lane);
+    else Path::load_q(qq, p, ii, lane);
+  };
+  Item it = item_at(cur);
   typename Path::Q q;
-  Path::load_q(q, p, it, lane);
-  UnitStream<D, kBytes, kKeep> st;
+  load_q(q, it);
+  UnitStream<D, kBytes> st;
   Frag<NCH> f[PF + 1];
   bool ok[PF + 1];
   st.begin(p, it.trow, it.start, it.u0, it.h);
@@ -683,9 +1050,9 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p, const 
       // are then harmless repeats, and always issuing them keeps the waits in
       // the stream exact).
       const bool has_next = nxt < total;
-      const Item nit = make_item(p, record(has_next ? nxt : cur), (has_next ? nxt : cur) % H, P, group, wave);
+      const Item nit = item_at(has_next ? nxt : cur);
       typename Path::Q qn;
-      Path::load_q(qn, p, nit, lane);
+      load_q(qn, nit);
       int32_t ids_n;
       {
         const int kk = (nit.start + nit.u0 * 16) / p.bs + lane;
@@ -700,8 +1067,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p, const 
       st.begin(p, nit.trow, nit.start, nit.u0, nit.h);
       st.ids = has_next ? ids_n : -1;
       prologue<PF, NCH>(st, f, ok, lane);
-      Path::to_lds(s, sm, wave, lane, p.G);
-      finish_partition<T, D, Smem::kRows>(p, sm, it);
+      Path::to_lds(s, sm, wave, lane, it.cols);
+      finish_partition<T, D, Smem::kRows, kShare>(p, sm, it, groups, seq_np);
       __syncthreads();
       if (!has_next) break;
       cur = nxt;
@@ -712,13 +1079,13 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p, const 
       typename Path::State s;
       run_item(s);
       if (threadIdx.x == 0) sm.slot[k & 1] = nn;
-      Path::to_lds(s, sm, wave, lane, p.G);
-      finish_partition<T, D, Smem::kRows>(p, sm, it);
+      Path::to_lds(s, sm, wave, lane, it.cols);
+      finish_partition<T, D, Smem::kRows, kShare>(p, sm, it, groups, seq_np);
       __syncthreads();
       cur = rfl(sm.slot[k & 1]);
       if (cur >= total) break;
-      it = make_item(p, record(cur), cur % H, P, group, wave);
-      Path::load_q(q, p, it, lane);
+      it = item_at(cur);
+      load_q(q, it);
       st.begin(p, it.trow, it.start, it.u0, it.h);
       st.ids = st.fetch_ids(lane);
       prologue<PF, NCH>(st, f, ok, lane);
@@ -734,12 +1101,19 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(DecodeParams p) {
   const int lane = threadIdx.x & 63;
   const int pair = blockIdx.x * kMergeWaves + (threadIdx.x >> 6);
   if (pair >= p.S * p.Hq) return;
-  const int P = rfl(p.header[2]);
-  const int ctx = rfl(clamp_ctx(p, pair / p.Hq));
-  if (ctx <= P) return;  // written directly by the partition kernel
-  int np = (ctx + P - 1) / P;
-  np = np > p.max_parts ? p.max_parts : np;
-  const size_t e0 = static_cast<size_t>(pair) * p.max_parts;
+  // Partition states of this row: from the sharing plan's count, or one per
+  // P tokens of the context.  A row with one state was written directly.
+  int np;
+  if (p.share) {
+    np = rfl(p.seq_np[pair / p.Hq]);
+  } else {
+    const int P = rfl(p.header[2]);
+    const int ctx = rfl(clamp_ctx(p, pair / p.Hq));
+    np = (ctx + P - 1) / P;
+  }
+  if (np <= 1) return;
+  np = np > p.ws_stride ? p.ws_stride : np;
+  const size_t e0 = static_cast<size_t>(pair) * p.ws_stride;
   const float* ml = p.ws_ml + 2 * e0;
 
   constexpr int PER = D / 64;  // head_dim entries per lane
@@ -813,11 +1187,11 @@ __global__ __launch_bounds__(kMergeThreads) void merge_wide_kernel(DecodeParams 
   const int ctx = rfl(clamp_ctx(p, pair / p.Hq));
   if (ctx <= P) return;  // written directly by the partition kernel
   int np = (ctx + P - 1) / P;
-  np = np > p.max_parts ? p.max_parts : np;
+  np = np > p.ws_stride ? p.ws_stride : np;
   const int per = (np + kMergeWaves - 1) / kMergeWaves;
   const int j0 = wave * per;
   const int j1 = j0 + per < np ? j0 + per : np;
-  const size_t e0 = static_cast<size_t>(pair) * p.max_parts;
+  const size_t e0 = static_cast<size_t>(pair) * p.ws_stride;
   const float* ml = p.ws_ml + 2 * e0;
 
   // Rows eight at a time, the first eight requested with the (m, l) pairs.
@@ -960,22 +1334,57 @@ hipError_t launch_decode_kernel(DecodeParams p, hipStream_t stream) {
     if (e != hipSuccess) return e;
   }
   const int4* items = static_cast<const int4*>(p.items);
-  // Cached loads when the batch shares blocks (the shallow schedule only:
-  // shared prefixes come with automatic partitioning in practice).
   if (deep) {
-    hipLaunchKernelGGL((decode_kernel<Path, T, D, true, false>), dim3(grid), dim3(kThreads), 0, stream, p, items);
-  } else if (p.keep_in_cache) {
-    hipLaunchKernelGGL((decode_kernel<Path, T, D, false, true>), dim3(grid), dim3(kThreads), 0, stream, p, items);
+    hipLaunchKernelGGL((decode_kernel<Path, T, D, true, false>), dim3(grid), dim3(kThreads), 0, stream, p, items,
+                       p.groups, p.seq_np);
   } else {
-    hipLaunchKernelGGL((decode_kernel<Path, T, D, false, false>), dim3(grid), dim3(kThreads), 0, stream, p, items);
+    hipLaunchKernelGGL((decode_kernel<Path, T, D, false, false>), dim3(grid), dim3(kThreads), 0, stream, p, items,
+                       p.groups, p.seq_np);
   }
   return hipGetLastError();
 }
 
+#ifndef PA_SHARE_DEEP
+#define PA_SHARE_DEEP 1
+#endif
+constexpr bool kShareDeep = PA_SHARE_DEEP != 0;
+
+// Sharing plan and decode: the MFMA path with a 16-column tile for every G,
+// so that the query heads of up to four sequences that share a prefix fill
+// one score tile.
 template <typename T, int D>
-hipError_t launch_typed(const DecodeParams& p, hipStream_t stream) {
+hipError_t launch_share(DecodeParams p, hipStream_t stream) {
+  using Path = MfmaPath<T, D, 16>;
+  const void* k = reinterpret_cast<const void*>(&decode_kernel<Path, T, D, kShareDeep, true>);
+  int grid = persistent_grid(k);
+  if (grid <= 0) return hipErrorInvalidValue;
+  const int64_t work_bound = static_cast<int64_t>(p.S) * p.ws_stride * p.H;
+  if (grid > work_bound) grid = static_cast<int>(work_bound);
+  p.grid = grid;
+  p.first_taken = kShareDeep ? 2 * grid : grid;
+  p.group = 1;
+  p.direct = 0;
+  p.share_nmax = 16 / p.G < kShareMaxMembers ? 16 / p.G : kShareMaxMembers;
+  hipLaunchKernelGGL(plan_share_kernel, dim3(1), dim3(kPlanThreads), 0, stream, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((decode_kernel<Path, T, D, kShareDeep, true>), dim3(grid), dim3(kThreads), 0, stream, p,
+                     static_cast<const int4*>(p.items), p.groups, p.seq_np);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t launch_typed(DecodeParams p, hipStream_t stream) {
   hipError_t e;
-  if (p.G == 1) {
+  // Sharing detection: the block manager holds shared blocks, the partition
+  // size is automatic (the plan sizes items from the unique work) and the
+  // contexts can span partitions (the split at a shared prefix's end needs
+  // the partition-state workspace); small enough batches for the one-
+  // workgroup plan, and at least two sequences per 16-column tile.
+  p.share = (p.share && p.auto_partition && p.max_parts > 1 && p.S <= kShareMaxSeqs && p.G <= 8) ? 1 : 0;
+  if (p.share) {
+    e = launch_share<T, D>(p, stream);
+  } else if (p.G == 1) {
     e = launch_decode_kernel<ValuPath<T, D, 1>, T, D>(p, stream);
   } else if (p.G == 2) {
     e = launch_decode_kernel<ValuPath<T, D, 2>, T, D>(p, stream);

@@ -28,10 +28,7 @@ struct Frag {
 // The block ids of a piece of the run (at most 64 logical blocks) are held one
 // per lane and read out with v_readlane, so locating a unit is scalar
 // arithmetic with no memory access.
-// kKeep selects ordinary (cached) loads instead of streaming ones, for
-// batches whose sequences share blocks: the other readers of a shared block
-// then find it in L2 or the Infinity Cache.
-template <int D, int kBytes, bool kKeep = false>
+template <int D, int kBytes>
 struct UnitStream {
   const char* layer_base;  // pool base + layer offset (bytes)
   const int32_t* trow;     // block-table row of the sequence
@@ -88,9 +85,9 @@ struct UnitStream {
     const uint4* kp = reinterpret_cast<const uint4*>(kb + lane_off);
     const uint4* vp = reinterpret_cast<const uint4*>(vb + lane_off);
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) f.k[c] = kKeep ? kp[64 * c] : load_stream16(kp + 64 * c);
+    for (int c = 0; c < NCH; ++c) f.k[c] = load_stream16(kp + 64 * c);
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) f.v[c] = kKeep ? vp[64 * c] : load_stream16(vp + 64 * c);
+    for (int c = 0; c < NCH; ++c) f.v[c] = load_stream16(vp + 64 * c);
     return ok;
   }
 };

@@ -35,11 +35,17 @@ struct DecodeParams {
   int32_t direct;            // 1: one (sequence, kv head) per workgroup, no plan, no counter
                              //    (every context within one partition, S * H <= grid)
   int32_t max_parts;         // ceil(ctx_cap / P)
-  int32_t* header;           // [0] work items, [1] next work index, [2] P used (device)
-  int4* items;               // [S * max_parts] (sequence, partition, context, partitions), longest first
-  float* ws_o;               // [S, Hq, max_parts, D]
-  float* ws_ml;              // [S, Hq, max_parts, 2] (max in log2 units, sum)
-  int32_t keep_in_cache;     // 1: read K/V with cached loads (sequences share blocks)
+  int32_t ws_stride;         // partition-state slots per (sequence, query head) row: max_parts + 1
+  int32_t* header;           // [0] work items, [1] next work index, [2] P used, [3] shared groups (device)
+  int4* items;               // [S * ws_stride] work items, longest first; records:
+                             //   (sequence, partition, context, partitions) without sharing,
+                             //   (sequence or ~group, partition slot, first token, end token) with it
+  float* ws_o;               // [S, Hq, ws_stride, D]
+  float* ws_ml;              // [S, Hq, ws_stride, 2] (max in log2 units, sum)
+  int32_t share;             // 1: the plan groups sequences whose tables share leading blocks
+  int32_t share_nmax;        // sequences per shared work item (their G query heads each: <= 16 columns)
+  int32_t* seq_np;           // [S] partition states of each sequence (sharing mode)
+  int4* groups;              // [S / 2] member sequences of each shared group (-1 = none)
 };
 
 struct PrefillParams {
@@ -60,19 +66,27 @@ struct PrefillParams {
   int32_t tiles;               // row tiles per (sequence, kv head) in the grid (set at launch)
 };
 
-// Workspace of pa_decode: a small header, the work-item list, and (only when
-// some context spans several partitions) the float32 partition states.
+// Workspace of pa_decode: a small header, the work-item list, the sharing
+// plan's per-sequence partition counts and groups, and (only when some
+// context spans several partitions) the float32 partition states.
+// With several partitions per context, every (sequence, query head) row has
+// ws_stride = max_parts + 1 state slots: splitting a context at the end of a
+// prefix it shares with other sequences can add one partition.
 struct WsLayout {
-  size_t header_off, items_off, o_off, ml_off, total;
+  size_t header_off, items_off, np_off, groups_off, o_off, ml_off, total;
+  int stride;
 };
 
 inline WsLayout decode_ws_layout(int S, int Hq, int max_parts, int D) {
   auto align = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
   WsLayout w;
+  w.stride = max_parts > 1 ? max_parts + 1 : 1;
   w.header_off = 0;
   w.items_off = 256;
-  w.o_off = align(w.items_off + static_cast<size_t>(S) * max_parts * sizeof(int4));
-  const size_t parts = max_parts > 1 ? static_cast<size_t>(S) * Hq * max_parts : 0;
+  w.np_off = align(w.items_off + static_cast<size_t>(S) * w.stride * sizeof(int4));
+  w.groups_off = align(w.np_off + static_cast<size_t>(S) * sizeof(int32_t));
+  w.o_off = align(w.groups_off + static_cast<size_t>(S / 2 + 1) * sizeof(int4));
+  const size_t parts = max_parts > 1 ? static_cast<size_t>(S) * Hq * w.stride : 0;
   w.ml_off = align(w.o_off + parts * D * sizeof(float));
   w.total = align(w.ml_off + parts * 2 * sizeof(float));
   return w;

@@ -1,0 +1,330 @@
+"""Sharing-aware decode, called through the C ABI.
+
+When the block manager holds shared blocks, pa_decode looks for sequences of
+the batch whose tables begin with the same block, checks id by id how many
+full blocks each has in common with the group's lowest sequence, and reads a
+subgroup's common prefix once for all its members (their query heads fill one
+score tile).  Each member's remaining tokens are ordinary work items, and the
+states of both are merged by log-sum-exp weighting.
+
+Checked here, every output element against the oracle:
+
+* batches built by random fork / append / copy-on-write scripts on the
+  library's block manager (nested forks, branches of every length, sequences
+  in shuffled batch order), over dtypes, group sizes G = 1 ... 16, head_dim
+  and block sizes;
+* hand-built tables that begin alike and then differ, differ in one block and
+  agree again later, are identical, or whose whole context is the shared
+  prefix -- the plan must share exactly the verified prefix;
+* the number of shared subgroups the plan formed (word 3 of the workspace
+  header) against a plain restatement of the grouping rule below.
+
+Grouping rule (restated here, not taken from the library): sequences whose
+first full block is the same valid block form a group led by the lowest
+index; each member's common prefix is the number of leading full blocks
+(within both contexts) equal to the leader's; members are taken in index
+order in subgroups of min(4, 16 // G) (a lone remainder stays alone); a
+subgroup shares the minimum common prefix of its members (the leader's own
+full blocks if it is one) when that is at least 256 tokens.
+"""
+import numpy as np
+import pytest
+import torch
+
+pytestmark = pytest.mark.gpu
+
+import workloads as W  # noqa: E402
+from tests import gpu_util as U  # noqa: E402
+from oracle import attention as A  # noqa: E402
+from oracle import layout as LY  # noqa: E402
+
+MIN_SHARED_TOKENS = 256
+MAX_CMP_TASKS = 2048  # 64-entry table comparisons the plan makes per call
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU")
+    import paged_kv_cache_337_amd  # noqa: F401
+
+
+def expected_subgroups(tables, ctx, bs, N, G):
+    """Active shared subgroups under the grouping rule of the module docstring."""
+    nmax = min(4, 16 // G)
+    if nmax < 2:
+        return 0
+    S = len(ctx)
+    nfb = [int(c) // bs for c in ctx]
+    key = [int(tables[i][0]) if nfb[i] > 0 and 0 <= tables[i][0] < N else None for i in range(S)]
+    groups = {}
+    for i in range(S):
+        if key[i] is not None:
+            groups.setdefault(key[i], []).append(i)
+    # comparisons are 64-entry tasks laid out over the non-leaders in index
+    # order; only the first MAX_CMP_TASKS tasks are made
+    lead_of = {i: mem[0] for mem in groups.values() for i in mem}
+    verified, tb = {}, 0
+    for i in range(S):
+        if i in lead_of and lead_of[i] != i:
+            cap = min(nfb[i], nfb[lead_of[i]])
+            ntk = -(-cap // 64)
+            verified[i] = min(cap, max(min(tb + ntk, MAX_CMP_TASKS) - tb, 0) * 64)
+            tb += ntk
+    active = 0
+    for mem in groups.values():
+        lead = mem[0]
+        common = {lead: nfb[lead]}
+        for m in mem[1:]:
+            cap = verified[m]
+            k = 0
+            while k < cap and tables[m][k] == tables[lead][k]:
+                k += 1
+            common[m] = k
+        for s in range(0, len(mem), nmax):
+            sub = mem[s:s + nmax]
+            if len(sub) >= 2 and min(common[m] for m in sub) * bs >= MIN_SHARED_TOKENS:
+                active += 1
+    return active
+
+
+def decode_with_header(pool, q, t, c, max_ctx, scale):
+    S, Hq, _ = q.shape
+    ws = torch.empty(pool.workspace_bytes(S, Hq, max_ctx, 0), dtype=torch.uint8, device="cuda")
+    out = pool.decode(0, q, t, c, max_ctx, scale, 0, workspace=ws)
+    torch.cuda.synchronize()
+    return out, int(ws[:16].view(torch.int32)[3].item())
+
+
+def _kv(rng, n, H, D, dtype):
+    k = W.round_to_storage(rng.standard_normal((n, H, D), dtype=np.float32), dtype)
+    v = W.round_to_storage(rng.standard_normal((n, H, D), dtype=np.float32), dtype)
+    return k, v
+
+
+def _f64(x, dtype):
+    return A.to_f64(x, dtype)
+
+
+# --------------------------------------------------- block-manager scripts ---
+
+CASES = [
+    # dtype, Hq, Hkv, D, bs
+    ("bf16", 32, 8, 128, 16),
+    ("f16", 8, 8, 128, 16),     # G = 1: four branches per tile
+    ("bf16", 64, 8, 128, 32),   # G = 8: two per tile
+    ("f32", 12, 4, 64, 16),     # G = 3
+    ("f16", 8, 4, 64, 32),      # G = 2
+    ("bf16", 10, 2, 128, 16),   # G = 5: three per tile
+    ("bf16", 64, 4, 128, 16),   # G = 16: no sharing plan, plain decode
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: f"{c[0]}-G{c[1] // c[2]}-D{c[3]}-bs{c[4]}")
+def test_forked_branches_match_oracle(case):
+    import paged_kv_cache_337_amd as pa
+    dtype, Hq, Hkv, D, bs = case
+    G = Hq // Hkv
+    seed = 900 + 17 * G + D + bs + len(dtype)
+    rng = np.random.default_rng(seed)
+    N = 3000
+    pool = pa.Pool(1, N, bs, Hkv, D, dtype, free_order=rng.permutation(N).astype(np.int32))
+    U.poison(pool)
+    logical = {}
+
+    def write(seq, n):
+        slots, pairs = pool.seq_append(seq, n)
+        if pairs:
+            pool.copy_blocks(torch.tensor(pairs, dtype=torch.int32).cuda())
+        if n:
+            k, v = _kv(rng, n, Hkv, D, dtype)
+            pool.write_kv(0, U.dev_tensor(k, dtype), U.dev_tensor(v, dtype), torch.from_numpy(slots).cuda())
+            K, V = logical[seq]
+            logical[seq] = (np.concatenate([K, k]), np.concatenate([V, v]))
+
+    seqs = []
+    for grp in range(int(rng.integers(3, 6))):
+        s0 = pool.seq_create()
+        logical[s0] = _kv(rng, 0, Hkv, D, dtype)
+        write(s0, int(rng.integers(600, 1400)) if grp == 0 else int(rng.integers(200, 1400)))
+        members = [s0]
+        for _ in range(int(rng.integers(1, 8))):
+            parent = members[int(rng.integers(0, len(members)))]
+            child = pool.seq_fork(parent)
+            logical[child] = tuple(x.copy() for x in logical[parent])
+            members.append(child)
+            if rng.random() < 0.5:
+                write(child, int(rng.integers(0, 60)))  # diverge before later forks
+        seqs += members
+    for _ in range(2):  # sequences that share nothing
+        s = pool.seq_create()
+        logical[s] = _kv(rng, 0, Hkv, D, dtype)
+        write(s, int(rng.integers(1, 900)))
+        seqs.append(s)
+    for _ in range(3):  # decode-like appends, interleaved
+        for s in rng.permutation(seqs):
+            write(int(s), int(rng.integers(0, 120)))
+    torch.cuda.synchronize()
+    order = [int(x) for x in rng.permutation(seqs)]
+    S = len(order)
+    width = max(len(pool.seq_block_table(s)[0]) for s in order)
+    tables, ctx = pool.batch_tables(order, width)
+    assert all(ctx[i] == logical[s][0].shape[0] for i, s in enumerate(order))
+    q = W.round_to_storage(rng.standard_normal((S, Hq, D), dtype=np.float32), dtype)
+    scale = float(np.float32(1.0 / np.sqrt(D)))
+    U.log(f"[share script] {case} S={S} ctx={int(ctx.min())}..{int(ctx.max())} shared blocks "
+          f"{pool.stats()['shared_blocks']}")
+    max_ctx = int(ctx.max())
+    assert max_ctx > 512
+    out, nsub = decode_with_header(pool, U.dev_tensor(q, dtype), torch.from_numpy(tables).cuda(),
+                                   torch.from_numpy(ctx).cuda(), max_ctx, scale)
+    ref = np.stack([A.decode_one(_f64(q[i], dtype), _f64(logical[s][0], dtype), _f64(logical[s][1], dtype), scale)
+                    for i, s in enumerate(order)])
+    U.check_close(U.out_f64(out), ref, dtype, f"{case} every sequence")
+    exp = expected_subgroups(tables, ctx, bs, N, G)
+    U.log(f"  shared subgroups: plan {nsub if G <= 8 else '-'}, rule {exp}")
+    if G <= 8:
+        assert nsub == exp
+        assert exp > 0
+
+
+# ------------------------------------------------------- hand-built tables ---
+
+def _hand_tables(rng, bs, N):
+    """(tables, ctx): groups whose tables agree, differ, agree again, are
+    identical, or consist of the shared prefix alone; in shuffled order."""
+    rows = []
+    a = list(range(10, 40))                      # 30 blocks
+    rows.append((a, 30 * bs))                    # leader of group A
+    rows.append((a[:20] + [100, 101, 102, 103, 104] + a[25:30] + [105], 30 * bs + 7))  # differs at 20, agrees again
+    rows.append((a, 30 * bs))                    # identical to the leader
+    rows.append((a + [106, 107], 32 * bs - 3))   # leader's blocks plus two
+    rows.append((a[:5] + list(range(110, 140)), 35 * bs))  # first 5 common (below 256 tokens at bs 16)
+    b = list(range(200, 320))                    # 120 blocks: a long prefix
+    rows.append((b, 120 * bs))
+    for i in range(8):                           # 9 sequences share most of b
+        k = int(rng.integers(100, 120))
+        tail = list(range(330 + 40 * i, 330 + 40 * i + int(rng.integers(1, 30))))
+        rows.append((b[:k] + tail, (k + len(tail)) * bs - int(rng.integers(0, bs))))
+    c = list(range(700, 732))                    # whole contexts shared, ctx exactly 32 blocks
+    rows.append((c, 32 * bs))
+    rows.append((c, 32 * bs))
+    rows.append((c, 32 * bs))
+    rows.append((list(range(800, 860)), 60 * bs - 5))  # shares nothing
+    rows.append(([a[0]], 9))                     # first block of group A but no full block
+    perm = rng.permutation(len(rows))
+    rows = [rows[i] for i in perm]
+    width = max(len(r) for r, _ in rows)
+    tables = np.full((len(rows), width), -1, dtype=np.int32)
+    for i, (r, _) in enumerate(rows):
+        tables[i, :len(r)] = r
+    ctx = np.array([c_ for _, c_ in rows], dtype=np.int32)
+    assert tables.max() < N
+    return tables, ctx
+
+
+@pytest.mark.parametrize("dtype,Hq,Hkv,D,bs", [("bf16", 32, 8, 128, 16), ("f16", 16, 4, 64, 16),
+                                               ("bf16", 16, 8, 128, 16)])
+def test_hand_built_tables_share_exactly_the_verified_prefix(dtype, Hq, Hkv, D, bs):
+    import paged_kv_cache_337_amd as pa
+    G = Hq // Hkv
+    rng = np.random.default_rng(4242 + G)
+    N = 1200
+    pool = pa.Pool(1, N, bs, Hkv, D, dtype)
+    U.poison(pool)
+    # the block manager must hold a shared block for the plan to look for sharing
+    s = pool.seq_create()
+    pool.seq_append(s, 1)
+    pool.seq_fork(s)
+    assert pool.stats()["shared_blocks"] == 1
+    # every slot of every block gets its own K/V (device through pa_write_kv;
+    # the oracle's pool through its own layout code)
+    kb, vb = _kv(rng, N * bs, Hkv, D, dtype)
+    pool.write_kv(0, U.dev_tensor(kb, dtype), U.dev_tensor(vb, dtype),
+                  torch.arange(N * bs, dtype=torch.int32).cuda())
+    g = LY.Geometry(1, N, bs, Hkv, D, dtype)
+    host = np.zeros(g.num_elements, dtype=W.storage_numpy_dtype(dtype))
+    LY.scatter(host, g, 0, np.arange(N, dtype=np.int32), kb, vb)
+    tables, ctx = _hand_tables(rng, bs, N)
+    S = len(ctx)
+    q = W.round_to_storage(rng.standard_normal((S, Hq, D), dtype=np.float32), dtype)
+    scale = float(np.float32(1.0 / np.sqrt(D)))
+    out, nsub = decode_with_header(pool, U.dev_tensor(q, dtype), torch.from_numpy(tables).cuda(),
+                                   torch.from_numpy(ctx).cuda(), int(ctx.max()), scale)
+    ref = []
+    for i in range(S):
+        K, V = LY.gather(host, g, 0, tables[i], int(ctx[i]))
+        ref.append(A.decode_one(_f64(q[i], dtype), _f64(K, dtype), _f64(V, dtype), scale))
+    U.check_close(U.out_f64(out), np.stack(ref), dtype, f"hand-built tables {dtype} G={G}")
+    exp = expected_subgroups(tables, ctx, bs, N, G)
+    U.log(f"  shared subgroups: plan {nsub}, rule {exp}")
+    assert nsub == exp and exp >= 3
+
+
+def test_shared_result_independent_of_physical_ids():
+    """Relabelling every physical block (pool contents and tables alike)
+    leaves the sharing plan's output bit-identical: the grouping depends only
+    on which ids are equal."""
+    import paged_kv_cache_337_amd as pa
+    dtype, Hq, Hkv, D, bs = "bf16", 32, 8, 128, 16
+    rng = np.random.default_rng(77)
+    N = 1200
+    kb, vb = _kv(rng, N * bs, Hkv, D, dtype)
+    tables, ctx = _hand_tables(rng, bs, N)
+    pi = rng.permutation(N).astype(np.int32)
+    q = U.dev_tensor(W.round_to_storage(rng.standard_normal((len(ctx), Hq, D), dtype=np.float32), dtype), dtype)
+    outs = []
+    for relabel in (False, True):
+        pool = pa.Pool(1, N, bs, Hkv, D, dtype)
+        U.poison(pool)
+        s = pool.seq_create()
+        pool.seq_append(s, 1)
+        pool.seq_fork(s)
+        ids = pi if relabel else np.arange(N, dtype=np.int32)
+        slots = (ids[:, None].astype(np.int64) * bs + np.arange(bs)).reshape(-1).astype(np.int32)
+        pool.write_kv(0, U.dev_tensor(kb, dtype), U.dev_tensor(vb, dtype), torch.from_numpy(slots).cuda())
+        t = np.where(tables >= 0, ids[np.maximum(tables, 0)], -1).astype(np.int32)
+        out, nsub = decode_with_header(pool, q, torch.from_numpy(t).cuda(), torch.from_numpy(ctx).cuda(),
+                                       int(ctx.max()), 0.08838834764831845)
+        outs.append(out.cpu())
+        assert nsub >= 3
+    assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
+
+
+def test_comparison_bound_limits_sharing():
+    """1024 branches of one 2,560-token prefix (the largest batch the plan
+    examines): 3 comparison tasks per branch, more than the plan makes, so
+    the later branches share nothing and read their prefix themselves.
+    Every output still matches the oracle, and the subgroup count follows
+    the bound."""
+    import paged_kv_cache_337_amd as pa
+    dtype, Hq, Hkv, D, bs = "bf16", 32, 8, 128, 16
+    rng = np.random.default_rng(1024)
+    S, prefix = 1024, 2560
+    N = prefix // bs + 4 * S
+    pool = pa.Pool(1, N, bs, Hkv, D, dtype, free_order=rng.permutation(N).astype(np.int32))
+    U.poison(pool)
+    s0 = pool.seq_create()
+    slots, _ = pool.seq_append(s0, prefix)
+    pk, pv = _kv(rng, prefix, Hkv, D, dtype)
+    pool.write_kv(0, U.dev_tensor(pk, dtype), U.dev_tensor(pv, dtype), torch.from_numpy(slots).cuda())
+    seqs = [s0] + [pool.seq_fork(s0) for _ in range(S - 1)]
+    tails = [int(x) for x in rng.integers(1, 50, S)]
+    all_slots = np.concatenate([pool.seq_append(s, n)[0] for s, n in zip(seqs, tails)])
+    tk, tv = _kv(rng, int(sum(tails)), Hkv, D, dtype)
+    pool.write_kv(0, U.dev_tensor(tk, dtype), U.dev_tensor(tv, dtype), torch.from_numpy(all_slots).cuda())
+    torch.cuda.synchronize()
+    width = max(len(pool.seq_block_table(s)[0]) for s in seqs)
+    tables, ctx = pool.batch_tables(seqs, width)
+    q = W.round_to_storage(rng.standard_normal((S, Hq, D), dtype=np.float32), dtype)
+    scale = float(np.float32(1.0 / np.sqrt(D)))
+    out, nsub = decode_with_header(pool, U.dev_tensor(q, dtype), torch.from_numpy(tables).cuda(),
+                                   torch.from_numpy(ctx).cuda(), int(ctx.max()), scale)
+    offs = np.concatenate([[0], np.cumsum(tails)])
+    ref = np.stack([A.decode_one(_f64(q[i], dtype), _f64(np.concatenate([pk, tk[offs[i]:offs[i + 1]]]), dtype),
+                                 _f64(np.concatenate([pv, tv[offs[i]:offs[i + 1]]]), dtype), scale)
+                    for i in range(S)])
+    U.check_close(U.out_f64(out), ref, dtype, "1024 branches")
+    exp = expected_subgroups(tables, ctx, bs, N, Hq // Hkv)
+    U.log(f"  shared subgroups: plan {nsub}, rule {exp} (of {S // 4} without the bound)")
+    assert nsub == exp and 0 < exp < S // 4

@@ -10,9 +10,12 @@ and every token's K/V to pa_write_kv, one decode step at a time.  Checked:
   copy (so placement, copies and writes all agree);
 * the allocator state (tables, reference counts, free stack, statistics)
   equals the model's;
-* decode over the shared tables matches the oracle on every sequence, and is
-  bit-identical to decode over the same tokens laid out with no sharing
-  (sharing changes storage only).
+* decode over the shared tables matches the oracle on every sequence; the
+  plan reads each group's common prefix once (16 shared groups, word 3 of
+  the workspace header), and the result agrees, within the same tolerances,
+  with decode over the same tokens laid out with no sharing (sharing changes
+  storage only; reading a prefix once splits the context at the prefix's end,
+  which changes only float32 rounding).
 """
 import numpy as np
 import pytest
@@ -63,12 +66,16 @@ def test_shared_prefix_script_matches_oracle(mk, n_copies):
 
     # decode over the shared tables vs the oracle
     q, t, c = U.device_inputs(w, tables=tables, ctx=ctx)
-    out = pool.decode(1, q, t, c, int(ctx.max()), w.scale, 0)
+    ws = torch.empty(pool.workspace_bytes(w.num_seqs, w.num_q_heads, int(ctx.max()), 0), dtype=torch.uint8,
+                     device="cuda")
+    out = pool.decode(1, q, t, c, int(ctx.max()), w.scale, 0, workspace=ws)
     torch.cuda.synchronize()
+    assert int(ws[:16].view(torch.int32)[3].item()) == w.script["groups"]  # one shared item set per group
     got = U.out_f64(out)
-    U.check_close(got, U.oracle_rows(w, range(w.num_seqs)), w.dtype, f"{w.name} all seqs")
+    ref = U.oracle_rows(w, range(w.num_seqs))
+    U.check_close(got, ref, w.dtype, f"{w.name} all seqs")
 
-    # the same tokens with no sharing: bit-identical output
+    # the same tokens with no sharing: the same attention
     import paged_kv_cache_337_amd as pa
     nb = tables.shape[1]
     flat = np.arange(w.num_seqs * nb, dtype=np.int32).reshape(w.num_seqs, nb)
@@ -78,5 +85,6 @@ def test_shared_prefix_script_matches_oracle(mk, n_copies):
     q2, t2d, c2d = U.device_inputs(w, tables=flat, ctx=ctx)
     out2 = pool2.decode(0, q2, t2d, c2d, int(ctx.max()), w.scale, 0)
     torch.cuda.synchronize()
-    assert torch.equal(out.cpu().view(torch.int16), out2.cpu().view(torch.int16))
+    U.check_close(U.out_f64(out2), ref, w.dtype, f"{w.name} unshared layout")
+    U.check_close(got, U.out_f64(out2), w.dtype, f"{w.name} shared vs unshared")
     U.log(f"  {w.name}: shared blocks used {w.num_blocks} vs unshared {w.num_seqs * nb}")
