@@ -181,6 +181,26 @@ int pa_decode(const pa_pool* pool, int layer, const void* q, int num_seqs, int n
               int partition_tokens, void* workspace, size_t ws_bytes, void* out,
               void* stream);
 
+/* pa_decode without a caller workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments, result and errors as
+ * pa_decode, minus the workspace: the work list and partition states live
+ * in a static scratch array of pa_decode_noalloc_scratch_bytes() bytes
+ * (128 MiB) that each device holds from the first such call on it until the
+ * process ends.  Calls this entry point makes allocate nothing.  A decode
+ * whose workspace (pa_decode_workspace_bytes) exceeds the scratch is refused
+ * with BUFFER_TOO_SMALL before any launch.  All calls on one device share the
+ * scratch: calls that overlap on one device (on different streams or
+ * threads) race.  The current device must be the one q, out and the pool
+ * live on.  PA_DEBUG validation (a synchronising host copy) is not done
+ * here; pa_decode does it. */
+int pa_decode_noalloc(const pa_pool* pool, int layer, const void* q, int num_seqs, int num_q_heads,
+                      const int32_t* block_tables, int max_blocks_per_seq, const int32_t* context_lens,
+                      int max_context_len, float scale, int partition_tokens, void* out, void* stream);
+
+/* Bytes of pa_decode_noalloc's static scratch per device. */
+size_t pa_decode_noalloc_scratch_bytes(void);
+
 /* Causal prefill attention of each sequence's newest tokens over the paged
  * cache (standard causal attention per "How it works"; the new tokens' blocks
  * are reserved and written first, "How Paged Attention Works", Steps 2-3).

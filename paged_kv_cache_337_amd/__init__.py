@@ -31,7 +31,8 @@ ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2}
 # Every symbol include/pa.h declares, in declaration order.
 EXPORTS = [
     "pa_version", "pa_last_error", "pa_pool_required_bytes", "pa_alloc_pool", "pa_free",
-    "pa_write_kv", "pa_decode_workspace_bytes", "pa_decode", "pa_prefill", "pa_copy_blocks",
+    "pa_write_kv", "pa_decode_workspace_bytes", "pa_decode", "pa_decode_noalloc",
+    "pa_decode_noalloc_scratch_bytes", "pa_prefill", "pa_copy_blocks",
     "pa_seq_create", "pa_seq_append", "pa_prefix_cache_enable", "pa_seq_append_tokens",
     "pa_prefix_cache_stats", "pa_host_block_bytes", "pa_host_tier_init", "pa_seq_swap_out",
     "pa_seq_swap_in", "pa_swap_blocks", "pa_seq_fork", "pa_seq_release", "pa_seq_block_table",
@@ -80,6 +81,9 @@ def _load():
         "pa_decode_workspace_bytes": (c_sz, [vp, c_int, c_int, c_int, c_int]),
         "pa_decode": (c_int, [vp, c_int, vp, c_int, c_int, vp, c_int, vp, c_int, ctypes.c_float,
                               c_int, vp, c_sz, vp, vp]),
+        "pa_decode_noalloc": (c_int, [vp, c_int, vp, c_int, c_int, vp, c_int, vp, c_int, ctypes.c_float,
+                                      c_int, vp, vp]),
+        "pa_decode_noalloc_scratch_bytes": (c_sz, []),
         "pa_prefill": (c_int, [vp, c_int, vp, c_int, c_int, vp, c_int, c_int, vp, c_int, vp, c_int,
                                ctypes.c_float, vp, vp]),
         "pa_copy_blocks": (c_int, [vp, vp, c_int, vp]),
@@ -273,6 +277,25 @@ class Pool:
                              int(block_tables.shape[1]), _ptr(context_lens), int(max_context_len),
                              float(scale), int(partition_tokens), _ptr(workspace), wsb, _ptr(out),
                              _stream(stream)), "pa_decode")
+        return out
+
+    def decode_noalloc(self, layer: int, q: torch.Tensor, block_tables: torch.Tensor,
+                       context_lens: torch.Tensor, max_context_len: int, scale: float,
+                       out: torch.Tensor, partition_tokens: int = 0, stream=None) -> torch.Tensor:
+        """pa_decode on the library's static scratch: no workspace, and `out`
+        is the caller's (nothing is allocated on this path)."""
+        fn, dt = "pa_decode_noalloc", TORCH_DTYPE[self.dtype]
+        _need(q, fn, "q", dt, 3, self.D)
+        S, Hq, _ = q.shape
+        _need(block_tables, fn, "block_tables", torch.int32, 2, min_rows=S)
+        _need(context_lens, fn, "context_lens", torch.int32, 1, min_rows=S)
+        _need(out, fn, "out", dt, 3, self.D, Hq, S)
+        _on_device(fn, ("q", q), ("block_tables", block_tables), ("context_lens", context_lens), ("out", out))
+        self._need_device()
+        _check(lib.pa_decode_noalloc(self.handle, layer, _ptr(q), S, Hq, _ptr(block_tables),
+                                     int(block_tables.shape[1]), _ptr(context_lens), int(max_context_len),
+                                     float(scale), int(partition_tokens), _ptr(out), _stream(stream)),
+               "pa_decode_noalloc")
         return out
 
     def prefill(self, layer: int, q: torch.Tensor, query_start: torch.Tensor, max_query_len: int,

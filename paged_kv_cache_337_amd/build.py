@@ -25,6 +25,7 @@ SOURCES = [
     os.path.join(CSRC, "kernels", "decode.hip"),
     os.path.join(CSRC, "kernels", "prefill.hip"),
     os.path.join(CSRC, "kernels", "probe.hip"),
+    os.path.join(CSRC, "noalloc.hip"),
 ]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

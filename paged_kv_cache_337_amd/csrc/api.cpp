@@ -12,6 +12,7 @@
 #include <vector>
 
 #include "allocator.hpp"
+#include "api_internal.hpp"
 #include "launch.hpp"
 #include "pa.h"
 
@@ -203,6 +204,18 @@ int pa_decode(const pa_pool* pool, int layer, const void* q, int num_seqs, int n
               const int32_t* block_tables, int max_blocks_per_seq, const int32_t* context_lens,
               int max_context_len, float scale, int partition_tokens, void* workspace,
               size_t ws_bytes, void* out, void* stream) {
+  return pa::decode_call(pool, layer, q, num_seqs, num_q_heads, block_tables, max_blocks_per_seq, context_lens,
+                         max_context_len, scale, partition_tokens, workspace, ws_bytes, out, stream, false);
+}
+
+}  // extern "C"
+
+int pa::set_error(int code, const std::string& msg) { return fail(code, msg); }
+
+int pa::decode_call(const pa_pool* pool, int layer, const void* q, int num_seqs, int num_q_heads,
+                    const int32_t* block_tables, int max_blocks_per_seq, const int32_t* context_lens,
+                    int max_context_len, float scale, int partition_tokens, void* workspace, size_t ws_bytes,
+                    void* out, void* stream, bool noalloc) {
   return guarded([&]() -> int {
     if (!pool) return fail(PA_ERR_INVALID_ARG, "pool is NULL");
     const pa_pool_desc& d = pool->desc;
@@ -229,12 +242,16 @@ int pa_decode(const pa_pool* pool, int layer, const void* q, int num_seqs, int n
     const int ctx_cap = static_cast<int>(cap64);
     const int max_parts = static_cast<int>((cap64 + P - 1) / P);
     const pa::WsLayout wl = pa::decode_ws_layout(num_seqs, num_q_heads, max_parts, d.head_dim);
+    if (noalloc && wl.total > ws_bytes)
+      return fail(PA_ERR_BUFFER_TOO_SMALL, "this decode needs " + std::to_string(wl.total) +
+                                               " bytes of scratch; the static scratch of pa_decode_noalloc holds " +
+                                               std::to_string(ws_bytes) + " (use pa_decode with a caller workspace)");
     if (!workspace || ws_bytes < wl.total)
       return fail(PA_ERR_BUFFER_TOO_SMALL, "workspace needs " + std::to_string(wl.total) + " bytes");
     if (reinterpret_cast<uintptr_t>(workspace) & 255u)
       return fail(PA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (debug_enabled()) {
+    if (!noalloc && debug_enabled()) {
       std::vector<int32_t> hc(num_seqs), ht(static_cast<size_t>(num_seqs) * max_blocks_per_seq);
       hipError_t e = hipMemcpyAsync(hc.data(), context_lens, sizeof(int32_t) * num_seqs, hipMemcpyDeviceToHost, s);
       if (e == hipSuccess)
@@ -290,6 +307,8 @@ int pa_decode(const pa_pool* pool, int layer, const void* q, int num_seqs, int n
     return e == hipSuccess ? PA_OK : hip_fail(e, "decode launch");
   });
 }
+
+extern "C" {
 
 int pa_prefill(const pa_pool* pool, int layer, const void* q, int num_seqs, int num_q_heads,
                const int32_t* query_start, int num_query_tokens, int max_query_len,
