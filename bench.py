@@ -309,6 +309,11 @@ def main_prefill(args):
             "avg_launch_ms": round(pf_ms, 5),
         },
     }
+    if table_free is not None:
+        table_free["achieved"] = round(alg_bytes / (table_free["avg_launch_ms"] * 1e-3) / 1e9, 2)
+        table_free["kv_gbs_per_step"] = round(kv_bytes / (table_free["ms_per_step"] * 1e-3) / 1e9, 2)
+        table_free["table_cost_pct"] = round(100 * (dec_ms / table_free["avg_launch_ms"] - 1), 2)
+        res["table_free"] = table_free
     if args.copy_calib_blocks > 0:
         res["copy_calibration_bytes"] = copy_calibration(pool, w, L, args.copy_calib_blocks)
     if not args.no_cpu_baseline:
@@ -687,6 +692,35 @@ def main():
     call_ms = call_times(step, args.warmup + args.steps, args.steps, stream)
     dec_ms = float(np.mean(call_ms))
 
+    # Table-free comparison point on the same consecutive blocks: sequence
+    # i's blocks are host_tables[i, 0] + k, read with no table at all.
+    table_free = None
+    if args.contiguous and not shared:
+        first = torch.from_numpy(np.ascontiguousarray(host_tables[:, 0], dtype=np.int32)).cuda()
+
+        def step_flat(k, ev=None):
+            layer = k % L
+            pool.write_kv(layer, k_new, v_new, slot_new)
+            if ev is not None:
+                ev[0].record(stream)
+            pool.decode_contiguous(layer, q, first, ctx, max_ctx, w.scale, P, out=out, workspace=ws)
+            if ev is not None:
+                ev[1].record(stream)
+
+        out_tab = out.clone()
+        step_flat(0)
+        torch.cuda.synchronize()
+        step(0)
+        torch.cuda.synchronize()
+        if not torch.equal(out.view(torch.int16), out_tab.view(torch.int16)):
+            raise RuntimeError("table-free and table decode differ")
+        flat_ms = call_times(step_flat, args.warmup + 2 * args.steps, args.steps, stream)
+        flat_step_ms, _ = run_steps(step_flat, args.warmup + 3 * args.steps, args.steps, stream)
+        table_free = {"kernel": "pa_decode_contiguous (no block table; consecutive blocks from each first block)",
+                      "avg_launch_ms": round(float(np.mean(flat_ms)), 5),
+                      "median_launch_ms": round(float(np.median(flat_ms)), 5),
+                      "ms_per_step": round(flat_step_ms, 5)}
+
     # Warm calls: the same layer again and again (no rotation), so whatever
     # the Infinity Cache keeps between calls is found there.
     warm = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(20)]
@@ -770,6 +804,11 @@ def main():
             "frac_of_probe": round(achieved / probe_gbs, 4),
         },
     }
+    if table_free is not None:
+        table_free["achieved"] = round(alg_bytes / (table_free["avg_launch_ms"] * 1e-3) / 1e9, 2)
+        table_free["kv_gbs_per_step"] = round(kv_bytes / (table_free["ms_per_step"] * 1e-3) / 1e9, 2)
+        table_free["table_cost_pct"] = round(100 * (dec_ms / table_free["avg_launch_ms"] - 1), 2)
+        res["table_free"] = table_free
     if args.copy_calib_blocks > 0:
         res["copy_calibration_bytes"] = copy_calibration(pool, w, L, args.copy_calib_blocks)
     if not args.no_cpu_baseline:

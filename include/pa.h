@@ -181,6 +181,27 @@ int pa_decode(const pa_pool* pool, int layer, const void* q, int num_seqs, int n
               int partition_tokens, void* workspace, size_t ws_bytes, void* out,
               void* stream);
 
+/* Comparison point, no part of the paged method: pa_decode over sequences
+ * whose blocks are consecutive, with no block table at all -- sequence i's
+ * position p lies in physical block first_block[i] + p / bs, slot p % bs, as
+ * in a contiguous (virtually mapped) KV layout ("Where it bites: the
+ * vAttention critique" of "PagedAttention: paging the KV cache like an OS
+ * pages memory" and "Limitations" of "PagedAttention and KV Cache
+ * Compression" name the table indirection as paging's cost).  The same
+ * kernels, arithmetic and results as pa_decode with tables
+ * first_block[i] + 0, 1, 2, ...; only the addressing differs, so the two
+ * calls together measure what reading the table costs.
+ *   first_block  device int32 [num_seqs]; blocks first_block[i] ..
+ *                first_block[i] + ceil(ctx_i / bs) - 1 must lie in the pool
+ *                (out-of-range blocks are masked, reported under PA_DEBUG)
+ * Other arguments, workspace and errors as pa_decode (size the workspace
+ * with max_context_len).  Explicit small partitions run in the one-index-
+ * ahead schedule, and shared prefixes are not looked for. */
+int pa_decode_contiguous(const pa_pool* pool, int layer, const void* q, int num_seqs, int num_q_heads,
+                         const int32_t* first_block, const int32_t* context_lens, int max_context_len,
+                         float scale, int partition_tokens, void* workspace, size_t ws_bytes, void* out,
+                         void* stream);
+
 /* pa_decode without a caller workspace, for callers that cannot allocate
  * device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid allocation).  Same arguments, result and errors as

@@ -215,8 +215,9 @@ int pa::set_error(int code, const std::string& msg) { return fail(code, msg); }
 int pa::decode_call(const pa_pool* pool, int layer, const void* q, int num_seqs, int num_q_heads,
                     const int32_t* block_tables, int max_blocks_per_seq, const int32_t* context_lens,
                     int max_context_len, float scale, int partition_tokens, void* workspace, size_t ws_bytes,
-                    void* out, void* stream, bool noalloc) {
+                    void* out, void* stream, bool noalloc, bool flat) {
   return guarded([&]() -> int {
+    if (flat) max_blocks_per_seq = 1;
     if (!pool) return fail(PA_ERR_INVALID_ARG, "pool is NULL");
     const pa_pool_desc& d = pool->desc;
     if (layer < 0 || layer >= d.num_layers) return fail(PA_ERR_INVALID_ARG, "layer out of range");
@@ -238,7 +239,9 @@ int pa::decode_call(const pa_pool* pool, int layer, const void* q, int num_seqs,
     const bool automatic = P == 0;
     if (automatic) P = auto_partition(bs);
     if (P < 0 || P % bs || P % 16) return fail(PA_ERR_INVALID_ARG, "partition_tokens must be a multiple of block_size");
-    const int64_t cap64 = std::min<int64_t>(max_context_len, static_cast<int64_t>(max_blocks_per_seq) * bs);
+    // a flat sequence is bounded by the pool, a paged one by its table row
+    const int64_t cap64 = std::min<int64_t>(
+        max_context_len, static_cast<int64_t>(flat ? d.num_blocks : max_blocks_per_seq) * bs);
     const int ctx_cap = static_cast<int>(cap64);
     const int max_parts = static_cast<int>((cap64 + P - 1) / P);
     const pa::WsLayout wl = pa::decode_ws_layout(num_seqs, num_q_heads, max_parts, d.head_dim);
@@ -262,6 +265,11 @@ int pa::decode_call(const pa_pool* pool, int layer, const void* q, int num_seqs,
         if (hc[i] < 1 || hc[i] > ctx_cap)
           return fail(PA_ERR_INVALID_ARG, "context_lens[" + std::to_string(i) + "] out of range");
         const int nb = (hc[i] + bs - 1) / bs;
+        if (flat) {
+          if (ht[i] < 0 || static_cast<int64_t>(ht[i]) + nb > d.num_blocks)
+            return fail(PA_ERR_INVALID_ARG, "first_block[" + std::to_string(i) + "] range beyond the pool");
+          continue;
+        }
         for (int b = 0; b < nb; ++b) {
           const int32_t id = ht[static_cast<size_t>(i) * max_blocks_per_seq + b];
           if (id < 0 || id >= d.num_blocks)
@@ -302,13 +310,22 @@ int pa::decode_call(const pa_pool* pool, int layer, const void* q, int num_seqs,
     // same blocks and reads each such common prefix once for all of them;
     // otherwise it keeps the plain plan.  The plan itself verifies every
     // shared block id, so tables from any source stay correct either way.
-    p.share = pool->alloc.shared_blocks() > 0 ? 1 : 0;
+    p.share = !flat && pool->alloc.shared_blocks() > 0 ? 1 : 0;
+    p.flat = flat ? 1 : 0;
     hipError_t e = pa::launch_decode(p, d.dtype, d.head_dim, s);
     return e == hipSuccess ? PA_OK : hip_fail(e, "decode launch");
   });
 }
 
 extern "C" {
+
+int pa_decode_contiguous(const pa_pool* pool, int layer, const void* q, int num_seqs, int num_q_heads,
+                         const int32_t* first_block, const int32_t* context_lens, int max_context_len,
+                         float scale, int partition_tokens, void* workspace, size_t ws_bytes, void* out,
+                         void* stream) {
+  return pa::decode_call(pool, layer, q, num_seqs, num_q_heads, first_block, 1, context_lens, max_context_len,
+                         scale, partition_tokens, workspace, ws_bytes, out, stream, false, true);
+}
 
 int pa_prefill(const pa_pool* pool, int layer, const void* q, int num_seqs, int num_q_heads,
                const int32_t* query_start, int num_query_tokens, int max_query_len,

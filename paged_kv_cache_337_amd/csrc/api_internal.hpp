@@ -16,10 +16,12 @@ int set_error(int code, const std::string& msg);
 // The whole of pa_decode on a given workspace.  `noalloc` marks the entry
 // point that brings its own static scratch: it skips the PA_DEBUG checks
 // (which copy to pageable host memory and synchronise) and reports a
-// workspace beyond the scratch as a size limit of that entry point.
+// workspace beyond the scratch as a size limit of that entry point.  `flat`
+// marks the table-free comparison call: block_tables is then one first block
+// id per sequence and max_blocks_per_seq is ignored.
 int decode_call(const pa_pool* pool, int layer, const void* q, int num_seqs, int num_q_heads,
                 const int32_t* block_tables, int max_blocks_per_seq, const int32_t* context_lens,
                 int max_context_len, float scale, int partition_tokens, void* workspace, size_t ws_bytes,
-                void* out, void* stream, bool noalloc);
+                void* out, void* stream, bool noalloc, bool flat = false);
 
 }  // namespace pa

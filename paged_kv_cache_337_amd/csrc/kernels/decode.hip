@@ -982,7 +982,7 @@ struct ValuPath {
 // whichever workgroup finishes first (measured: holding two indices per
 // workgroup costs more in the tail than it saves between items there).
 // ---------------------------------------------------------------------------
-template <typename Path, typename T, int D, bool kDeep, bool kShare>
+template <typename Path, typename T, int D, bool kDeep, bool kShare, bool kFlat = false>
 __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p, const int4* __restrict__ items,
                                                           const int4* __restrict__ groups,
                                                           const int32_t* __restrict__ seq_np) {
@@ -1025,7 +1025,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p, const 
   Item it = item_at(cur);
   typename Path::Q q;
   load_q(q, it);
-  UnitStream<D, kBytes> st;
+  UnitStream<D, kBytes, kFlat> st;
   Frag<NCH> f[PF + 1];
   bool ok[PF + 1];
   st.begin(p, it.trow, it.start, it.u0, it.h);
@@ -1303,7 +1303,8 @@ constexpr int kMaxGroupedPartition = 1024;
 template <typename Path, typename T, int D>
 hipError_t launch_decode_kernel(DecodeParams p, hipStream_t stream) {
   const int64_t work_bound = static_cast<int64_t>(p.S) * p.max_parts * p.H;
-  const void* k_shallow = reinterpret_cast<const void*>(&decode_kernel<Path, T, D, false, false>);
+  const void* k_shallow = p.flat ? reinterpret_cast<const void*>(&decode_kernel<Path, T, D, false, false, true>)
+                                 : reinterpret_cast<const void*>(&decode_kernel<Path, T, D, false, false>);
   const void* k_deep = reinterpret_cast<const void*>(&decode_kernel<Path, T, D, true, false>);
   int grid = persistent_grid(k_shallow);
   if (grid <= 0) return hipErrorInvalidValue;
@@ -1311,7 +1312,8 @@ hipError_t launch_decode_kernel(DecodeParams p, hipStream_t stream) {
   // kv head) pair gets a workgroup of its own, so the work list is the
   // sequences in order and needs neither the plan kernel nor the counter.
   p.direct = (p.max_parts == 1 && work_bound <= grid) ? 1 : 0;
-  const bool deep = !p.direct && !p.auto_partition &&
+  // (the table-free comparison instance exists in the shallow schedule only)
+  const bool deep = !p.direct && !p.auto_partition && !p.flat &&
                     work_bound >= static_cast<int64_t>(kDeepItemsPerWorkgroup) * grid;
   if (deep) grid = persistent_grid(k_deep);
   if (grid <= 0) return hipErrorInvalidValue;
@@ -1337,6 +1339,9 @@ hipError_t launch_decode_kernel(DecodeParams p, hipStream_t stream) {
   if (deep) {
     hipLaunchKernelGGL((decode_kernel<Path, T, D, true, false>), dim3(grid), dim3(kThreads), 0, stream, p, items,
                        p.groups, p.seq_np);
+  } else if (p.flat) {
+    hipLaunchKernelGGL((decode_kernel<Path, T, D, false, false, true>), dim3(grid), dim3(kThreads), 0, stream, p,
+                       items, p.groups, p.seq_np);
   } else {
     hipLaunchKernelGGL((decode_kernel<Path, T, D, false, false>), dim3(grid), dim3(kThreads), 0, stream, p, items,
                        p.groups, p.seq_np);
@@ -1381,7 +1386,7 @@ hipError_t launch_typed(DecodeParams p, hipStream_t stream) {
   // contexts can span partitions (the split at a shared prefix's end needs
   // the partition-state workspace); small enough batches for the one-
   // workgroup plan, and at least two sequences per 16-column tile.
-  p.share = (p.share && p.auto_partition && p.max_parts > 1 && p.S <= kShareMaxSeqs && p.G <= 8) ? 1 : 0;
+  p.share = (p.share && !p.flat && p.auto_partition && p.max_parts > 1 && p.S <= kShareMaxSeqs && p.G <= 8) ? 1 : 0;
   if (p.share) {
     e = launch_share<T, D>(p, stream);
   } else if (p.G == 1) {

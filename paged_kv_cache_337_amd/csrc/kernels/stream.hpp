@@ -28,7 +28,10 @@ struct Frag {
 // The block ids of a piece of the run (at most 64 logical blocks) are held one
 // per lane and read out with v_readlane, so locating a unit is scalar
 // arithmetic with no memory access.
-template <int D, int kBytes>
+// kFlat: no block table -- the sequence's blocks are consecutive physical
+// blocks from its first one (a contiguous range, the comparison point for
+// what the table costs); `trow` then points at that first block id.
+template <int D, int kBytes, bool kFlat = false>
 struct UnitStream {
   const char* layer_base;  // pool base + layer offset (bytes)
   const int32_t* trow;     // block-table row of the sequence
@@ -54,8 +57,10 @@ struct UnitStream {
     lb_base = lb;
   }
 
-  // Block id of logical block lb_base + lane (-1 past the row).
+  // Block id of logical block lb_base + lane (-1 past the row); with kFlat,
+  // the sequence's first block id (uniform).
   __device__ __forceinline__ int32_t fetch_ids(int lane) const {
+    if constexpr (kFlat) return __builtin_amdgcn_readfirstlane(trow[0]);
     const int k = lb_base + lane;
     return k < max_blocks ? trow[k] : -1;
   }
@@ -64,7 +69,8 @@ struct UnitStream {
   // false for an invalid block id (the bases then point at block 0 of the
   // layer, a valid address; such a unit is masked).
   __device__ __forceinline__ bool locate(const char*& kp, const char*& vp) {
-    const int32_t b = __builtin_amdgcn_readlane(ids, lb - lb_base);
+    const int32_t b = kFlat ? static_cast<int32_t>(static_cast<uint32_t>(ids) + static_cast<uint32_t>(lb))
+                            : __builtin_amdgcn_readlane(ids, lb - lb_base);
     const int s = sub;
     if (++sub * 16 == bs) {
       sub = 0;

@@ -212,6 +212,37 @@ def test_contiguous_layout_equals_scattered():
     assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
 
 
+@pytest.mark.parametrize("dtype,hq,hkv,d,bs,P", [("bf16", 32, 8, 128, 16, 0), ("f16", 8, 8, 128, 16, 0),
+                                                  ("f32", 8, 4, 64, 16, 0), ("bf16", 64, 8, 128, 32, 64),
+                                                  ("f16", 24, 8, 64, 48, 0)])
+def test_table_free_layout_matches_oracle(dtype, hq, hkv, d, bs, P):
+    """pa_decode_contiguous reads sequence i's blocks as first_block[i] + k
+    with no table.  Every output element matches the oracle, and equals
+    pa_decode over the same consecutive blocks through tables bit for bit
+    (only the addressing differs)."""
+    w = W.custom("flat", 81 + bs + d, dtype, [1, 15, 16, 300, 777, 1500, 2600, 40], hq, hkv, d, bs,
+                 partition_tokens=P, extra_blocks=16)
+    ident = np.full_like(w.block_tables, -1)
+    first = np.zeros(w.num_seqs, dtype=np.int32)
+    off = 5  # start past block 0, with gaps between sequences
+    for i, n in enumerate(w.context_lens):
+        nb = SZ.blocks_required(int(n), w.block_size)
+        ident[i, :nb] = np.arange(off, off + nb)
+        first[i] = off
+        off += nb + 1
+    assert off <= w.num_blocks
+    pool = U.make_pool(w)
+    U.fill_pool(pool, w, tables=ident)
+    q, t, c = U.device_inputs(w, tables=ident)
+    U.log(f"[flat] {dtype} G={hq // hkv} D={d} bs={bs} P={P}")
+    out_flat = pool.decode_contiguous(0, q, torch.from_numpy(first).cuda(), c, w.max_context_len, w.scale, P)
+    out_tab = pool.decode(0, q, t, c, w.max_context_len, w.scale, P)
+    torch.cuda.synchronize()
+    U.check_close(U.out_f64(out_flat), U.oracle_rows(w, range(w.num_seqs)), dtype, "table-free")
+    bits = U.TORCH_BITS[dtype]
+    assert torch.equal(out_flat.cpu().view(bits), out_tab.cpu().view(bits))
+
+
 @pytest.mark.parametrize("dtype,hq,hkv,d", [("bf16", 32, 8, 128), ("f16", 8, 8, 128), ("f32", 4, 4, 64)])
 def test_direct_launch_equals_planned(dtype, hq, hkv, d):
     """Contexts within one partition and few enough (sequence, kv head) pairs
