@@ -575,12 +575,18 @@ def main_swap(args):
     print(json.dumps(res), flush=True)
 
 
+PROBE_FORMS = {0: "global_load_dwordx4 nt", 1: "global_load_dwordx4", 2: "buffer_load_dwordx4 nt",
+               3: "global_load_lds_dwordx4", 4: "global_load_lds_dwordx4 nt"}
+
+
 def main_probe(args):
     """HBM read rate of the decode kernel's access pattern (pa_probe_read_chunks:
-    whole 8 KiB chunks, 16-byte streaming loads, no arithmetic) over a 6 GiB
-    buffer, for chunk orders of growing contiguity: random 8 KiB chunks (one
-    (block, kv head) region of the pool), random runs of 4, 8 and 32 chunks,
-    and the identity order.  It bounds what any block placement could gain."""
+    whole 8 KiB chunks, 16 bytes per lane per load, no arithmetic) over a 6 GiB
+    buffer: by chunk order (random 8 KiB chunks -- one (block, kv head) region
+    of the pool --, random runs of 4, 8 and 32 chunks, the identity order) with
+    the decode kernel's loads, then random 8 KiB chunks with every load form
+    of the probe, workgroups per CU and chunks in flight.  It bounds what any
+    block placement, and any of these load forms, could gain."""
     import torch
     import paged_kv_cache_337_amd as pa
     nbytes = 6 << 30
@@ -597,20 +603,33 @@ def main_probe(args):
               "random_64KiB_runs": runs(8), "random_256KiB_runs": runs(32),
               "identity": np.arange(nchunks, dtype=np.int32)}
     stream = torch.cuda.current_stream()
-    rates = {}
-    for name, order in orders.items():
-        od = torch.from_numpy(order).cuda()
 
-        def step(_k, ev, od=od):
+    def rate(od, form=0, wg=2, infl=2):
+        def step(_k, ev):
             ev[0].record(stream)
-            pa.probe_read_chunks(buf, od, sink)
+            pa.probe_read_chunks(buf, od, sink, load_form=form, wg_per_cu=wg, in_flight=infl)
             ev[1].record(stream)
 
         ms = call_times(step, 0, 1 + max(args.steps // 20, 3), stream)
-        rates[name] = round(nbytes / (float(np.median(ms[1:])) * 1e-3) / 1e9, 1)  # first call warms up
-    print(json.dumps({"metric": "HBM read probe GB/s by chunk contiguity (pa_probe_read_chunks, 6 GiB)",
+        return round(nbytes / (float(np.median(ms[1:])) * 1e-3) / 1e9, 1)  # first call warms up
+
+    rates = {}
+    for name, order in orders.items():
+        rates[name] = rate(torch.from_numpy(order).cuda())
+        log(f"[probe] order {name}: {rates[name]} GB/s")
+    rnd = torch.from_numpy(orders["random_8KiB"]).cuda()
+    forms = []
+    for form, fname in PROBE_FORMS.items():
+        for wg in (1, 2, 3):
+            for infl in ((1, 2) if form >= 3 else (1, 2, 4)):
+                r = rate(rnd, form, wg, infl)
+                forms.append({"load_form": fname, "wg_per_cu": wg, "chunks_in_flight": infl, "gbs": r})
+                log(f"[probe] {fname} wg/CU {wg} in flight {infl}: {r} GB/s")
+    best = max(forms, key=lambda f: f["gbs"])
+    print(json.dumps({"metric": "HBM read probe GB/s by chunk contiguity and load form (pa_probe_read_chunks, 6 GiB)",
                       "value": rates["random_8KiB"], "unit": "GB/s", "n_gpus": 1, "higher_is_better": True,
-                      "data": "synthetic", "rates": rates, "peak": HBM_PEAK_GBS}), flush=True)
+                      "data": "synthetic", "rates": rates, "best_random_8KiB": best, "load_forms": forms,
+                      "peak": HBM_PEAK_GBS}), flush=True)
 
 
 def main():

@@ -385,13 +385,21 @@ int pa_pool_stats(const pa_pool* pool, pa_stats* stats);
 
 /* Measurement helper (no part of the method): read num_chunks 8 KiB chunks of
  * device buffer buf (buf_bytes long, 16-byte aligned) in the order of
- * chunk_ids (device int32 [num_chunks]; ids outside the buffer read chunk 0)
- * with the decode kernel's 16-byte streaming loads and launch shape of two
- * workgroups per CU, writing at most one word to sink (device, 4 bytes) so
- * the reads are kept.  Bracket it with events to get the HBM read rate paged
- * 8 KiB runs can reach, the practical ceiling for pa_decode.  Asynchronous. */
+ * chunk_ids (device int32 [num_chunks]; ids outside the buffer read chunk 0),
+ * 16 bytes per lane per load, in_flight chunks in flight per wave, wg_per_cu
+ * workgroups of four waves per CU, writing at most one word to sink (device,
+ * 4 bytes) so the reads are kept.  load_form picks the load instruction:
+ *   0  global_load_dwordx4, non-temporal (the decode kernel's loads)
+ *   1  global_load_dwordx4, ordinary
+ *   2  buffer_load_dwordx4, non-temporal
+ *   3  global_load_lds_dwordx4 (straight into LDS)
+ *   4  global_load_lds_dwordx4, non-temporal
+ * wg_per_cu 1-4; in_flight 1, 2 or 4 (1 or 2 for forms 3-4).  Bracket it with
+ * events to get the HBM read rate paged 8 KiB runs can reach, the practical
+ * ceiling for pa_decode.  Errors: UNSUPPORTED (form or shape), INVALID_ARG.
+ * Asynchronous. */
 int pa_probe_read_chunks(const void* buf, size_t buf_bytes, const int32_t* chunk_ids, int num_chunks,
-                         void* sink, void* stream);
+                         int load_form, int wg_per_cu, int in_flight, void* sink, void* stream);
 
 /* Host helper: global slot numbers for positions [pos_begin, pos_begin +
  * n_tokens) of every sequence of a batch, written sequence-major into host

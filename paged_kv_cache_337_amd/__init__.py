@@ -105,7 +105,7 @@ def _load():
         "pa_batch_tables": (c_int, [vp, intp, c_int, c_int, i32p, i32p]),
         "pa_pool_state": (c_int, [vp, i32p, i32p, intp]),
         "pa_pool_stats": (c_int, [vp, ctypes.POINTER(Stats)]),
-        "pa_probe_read_chunks": (c_int, [vp, c_sz, vp, c_int, vp, vp]),
+        "pa_probe_read_chunks": (c_int, [vp, c_sz, vp, c_int, c_int, c_int, c_int, vp, vp]),
         "pa_slots_for_positions": (c_int, [i32p, c_int, c_int, c_int, i32p, i32p, i32p]),
     }
     for name, (res, args) in sig.items():
@@ -464,7 +464,10 @@ class Pool:
         return {n: int(getattr(s, n)) for n, _ in Stats._fields_}
 
 
-def probe_read_chunks(buf: torch.Tensor, chunk_ids: torch.Tensor, sink: torch.Tensor, stream=None):
+def probe_read_chunks(buf: torch.Tensor, chunk_ids: torch.Tensor, sink: torch.Tensor, stream=None,
+                      load_form: int = 0, wg_per_cu: int = 2, in_flight: int = 2):
     """Read-bandwidth probe over a device buffer (see pa_probe_read_chunks)."""
+    _need(chunk_ids, "pa_probe_read_chunks", "chunk_ids", torch.int32, 1)
     _check(lib.pa_probe_read_chunks(_ptr(buf), buf.numel() * buf.element_size(), _ptr(chunk_ids),
-                                    int(chunk_ids.numel()), _ptr(sink), _stream(stream)), "pa_probe_read_chunks")
+                                    int(chunk_ids.numel()), int(load_form), int(wg_per_cu), int(in_flight),
+                                    _ptr(sink), _stream(stream)), "pa_probe_read_chunks")

@@ -485,17 +485,19 @@ int pa_swap_blocks(pa_pool* pool, const int32_t* pairs, int n, void* host_buf, s
   });
 }
 
-int pa_probe_read_chunks(const void* buf, size_t buf_bytes, const int32_t* chunk_ids, int num_chunks, void* sink,
-                         void* stream) {
+int pa_probe_read_chunks(const void* buf, size_t buf_bytes, const int32_t* chunk_ids, int num_chunks,
+                         int load_form, int wg_per_cu, int in_flight, void* sink, void* stream) {
   return guarded([&]() -> int {
     if (num_chunks < 0) return fail(PA_ERR_INVALID_ARG, "chunk count cannot be negative");
+    if (!pa::probe_supported(load_form, wg_per_cu, in_flight))
+      return fail(PA_ERR_UNSUPPORTED, "load_form 0-4, wg_per_cu 1-4, in_flight 1, 2 or 4 (1 or 2 into LDS)");
     if (num_chunks == 0) return PA_OK;
     if (!buf || !chunk_ids || !sink) return fail(PA_ERR_INVALID_ARG, "NULL device pointer");
     if (!aligned16(buf)) return fail(PA_ERR_INVALID_ARG, "buf must be 16-byte aligned");
     const int64_t nchunks_buf = static_cast<int64_t>(buf_bytes / 8192);
     if (nchunks_buf == 0) return fail(PA_ERR_INVALID_ARG, "buf holds no whole 8 KiB chunk");
-    hipError_t e = pa::launch_probe_read(buf, nchunks_buf, chunk_ids, num_chunks, sink,
-                                         static_cast<hipStream_t>(stream));
+    hipError_t e = pa::launch_probe_read(buf, nchunks_buf, chunk_ids, num_chunks, load_form, wg_per_cu, in_flight,
+                                         sink, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? PA_OK : hip_fail(e, "probe launch");
   });
 }

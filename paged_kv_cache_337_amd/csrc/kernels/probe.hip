@@ -1,9 +1,16 @@
 // Read-bandwidth probe: the access pattern of the decode kernel without its
 // arithmetic.  Each wave reads whole 8 KiB chunks (eight 16-byte loads per
-// lane, 1 KiB per instruction) in the order given by a chunk list, two chunks
-// in flight, and folds the data into one word so the loads stay live.  It
-// gives the HBM read rate that paged 8 KiB runs can reach on this GPU, the
-// practical ceiling the decode kernel is compared with.
+// lane, 1 KiB per instruction) in the order given by a chunk list, a fixed
+// number of chunks in flight, and folds the data into one word so the loads
+// stay live.  It gives the HBM read rate that paged 8 KiB runs can reach on
+// this GPU, the practical ceiling the decode kernel is compared with.
+//
+// Load forms (each gfx950 way of moving 16 bytes per lane from HBM):
+//   0  global_load_dwordx4, non-temporal (the decode kernel's form)
+//   1  global_load_dwordx4, ordinary (cached)
+//   2  buffer_load_dwordx4, non-temporal (buffer resource over the buffer)
+//   3  global_load_lds_dwordx4: straight into LDS, no VGPRs
+//   4  global_load_lds_dwordx4, non-temporal
 #include "../launch.hpp"
 #include "common.hpp"
 
@@ -12,27 +19,50 @@ namespace pa {
 namespace {
 
 constexpr int kProbeThreads = 256;
+constexpr int kProbeWaves = kProbeThreads / 64;
+constexpr int kMaxInFlight = 4;
+// cache-policy operand of the gfx950 load builtins: bit 1 = non-temporal
+constexpr int kPolicyNT = 2;
 
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ int probe_id(const int32_t* __restrict__ ids, int k, int n, int64_t nchunks_buf) {
+  int32_t id = k < n ? ids[k] : -1;
+  return (id >= 0 && id < nchunks_buf) ? id : 0;
+}
+
+// Forms 0-2: chunks land in registers.
+template <int kForm, int kInFlight>
 __global__ __launch_bounds__(kProbeThreads) void probe_read_kernel(const uint4* __restrict__ buf, int64_t nchunks_buf,
                                                                    const int32_t* __restrict__ ids, int n,
                                                                    uint32_t* __restrict__ sink) {
   const int lane = threadIdx.x & 63;
-  const int wave = static_cast<int>((blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x) >> 6);
-  const int W = static_cast<int>((static_cast<int64_t>(gridDim.x) * blockDim.x) >> 6);
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(blockIdx.x * kProbeWaves + (threadIdx.x >> 6)));
+  const int W = static_cast<int>(gridDim.x) * kProbeWaves;
   uint32_t acc = 0;
-  for (int c = wave; c < n; c += 2 * W) {
-    uint4 v[2][8];
+  for (int c = wave; c < n; c += kInFlight * W) {
+    uint4 v[kInFlight][8];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int k = c + u * W;
-      int32_t id = k < n ? ids[k] : -1;
-      id = (id >= 0 && id < nchunks_buf) ? id : 0;
+    for (int u = 0; u < kInFlight; ++u) {
+      const int id = probe_id(ids, c + u * W, n, nchunks_buf);
       const uint4* b = buf + static_cast<size_t>(id) * 512 + lane;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) v[u][j] = load_stream16(b + 64 * j);
+      for (int j = 0; j < 8; ++j) {
+        if constexpr (kForm == 0) {
+          v[u][j] = load_stream16(b + 64 * j);
+        } else if constexpr (kForm == 1) {
+          v[u][j] = b[64 * j];
+        } else {
+          // buffer offsets are 32-bit: the resource starts at this chunk
+          __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+              const_cast<uint4*>(buf + static_cast<size_t>(id) * 512), 0, 8192, 0x00020000);
+          const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(r, (lane + 64 * j) * 16, 0, kPolicyNT);
+          v[u][j] = make_uint4(x.x, x.y, x.z, x.w);
+        }
+      }
     }
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
+    for (int u = 0; u < kInFlight; ++u)
 #pragma unroll
       for (int j = 0; j < 8; ++j) acc ^= v[u][j].x ^ v[u][j].y ^ v[u][j].z ^ v[u][j].w;
   }
@@ -40,21 +70,74 @@ __global__ __launch_bounds__(kProbeThreads) void probe_read_kernel(const uint4* 
   if (acc == 0x9e3779b9u) sink[0] = acc;
 }
 
+// Forms 3-4: chunks land in LDS (each wave its own kInFlight x 8 KiB ring);
+// one word of each chunk is folded after its loads complete.
+template <int kForm, int kInFlight>
+__global__ __launch_bounds__(kProbeThreads) void probe_lds_kernel(const uint4* __restrict__ buf, int64_t nchunks_buf,
+                                                                  const int32_t* __restrict__ ids, int n,
+                                                                  uint32_t* __restrict__ sink) {
+  __shared__ uint4 ring[kProbeWaves][kInFlight][512];
+  const int lane = threadIdx.x & 63;
+  const int wl = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(blockIdx.x * kProbeWaves) + wl);
+  const int W = static_cast<int>(gridDim.x) * kProbeWaves;
+  uint32_t acc = 0;
+  for (int c = wave; c < n; c += kInFlight * W) {
+#pragma unroll
+    for (int u = 0; u < kInFlight; ++u) {
+      const int id = probe_id(ids, c + u * W, n, nchunks_buf);
+      const uint4* b = buf + static_cast<size_t>(id) * 512 + lane;
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        __builtin_amdgcn_global_load_lds(b + 64 * j,
+                                         (__attribute__((address_space(3))) void*)&ring[wl][u][64 * j], 16, 0,
+                                         kForm == 4 ? kPolicyNT : 0);
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // every load of this round in LDS
+#pragma unroll
+    for (int u = 0; u < kInFlight; ++u) acc ^= ring[wl][u][lane].x;
+  }
+  if (acc == 0x9e3779b9u) sink[0] = acc;
+}
+
+template <int kForm, int kInFlight>
+const void* probe_kernel() {
+  // the LDS ring holds at most two chunks per wave (64 KiB per workgroup)
+  if constexpr (kForm >= 3) return reinterpret_cast<const void*>(&probe_lds_kernel<kForm, kInFlight < 2 ? kInFlight : 2>);
+  else return reinterpret_cast<const void*>(&probe_read_kernel<kForm, kInFlight>);
+}
+
+template <int kForm>
+const void* probe_kernel_for(int in_flight) {
+  return in_flight == 1 ? probe_kernel<kForm, 1>() : in_flight == 2 ? probe_kernel<kForm, 2>()
+                                                                    : probe_kernel<kForm, 4>();
+}
+
 }  // namespace
 
-hipError_t launch_probe_read(const void* buf, int64_t nchunks_buf, const int32_t* ids, int n, void* sink,
-                             hipStream_t stream) {
+bool probe_supported(int load_form, int wg_per_cu, int in_flight) {
+  if (load_form < 0 || load_form > 4 || wg_per_cu < 1 || wg_per_cu > 4) return false;
+  if (load_form >= 3) return in_flight == 1 || in_flight == 2;
+  return in_flight == 1 || in_flight == 2 || in_flight == kMaxInFlight;
+}
+
+hipError_t launch_probe_read(const void* buf, int64_t nchunks_buf, const int32_t* ids, int n, int load_form,
+                             int wg_per_cu, int in_flight, void* sink, hipStream_t stream) {
   if (n <= 0) return hipSuccess;
+  if (!probe_supported(load_form, wg_per_cu, in_flight)) return hipErrorInvalidValue;
   int dev = 0, cus = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return e;
-  // Two workgroups of four waves per CU: the configuration that read paged
-  // 8 KiB chunks fastest on MI355X.
-  const int grid = 2 * cus;
-  hipLaunchKernelGGL(probe_read_kernel, dim3(grid), dim3(kProbeThreads), 0, stream, static_cast<const uint4*>(buf),
-                     nchunks_buf, ids, n, static_cast<uint32_t*>(sink));
-  return hipGetLastError();
+  const void* k = load_form == 0   ? probe_kernel_for<0>(in_flight)
+                  : load_form == 1 ? probe_kernel_for<1>(in_flight)
+                  : load_form == 2 ? probe_kernel_for<2>(in_flight)
+                  : load_form == 3 ? probe_kernel_for<3>(in_flight)
+                                   : probe_kernel_for<4>(in_flight);
+  const uint4* b = static_cast<const uint4*>(buf);
+  uint32_t* s = static_cast<uint32_t*>(sink);
+  void* args[] = {&b, &nchunks_buf, &ids, &n, &s};
+  return hipLaunchKernel(k, dim3(wg_per_cu * cus), dim3(kProbeThreads), args, 0, stream);
 }
 
 }  // namespace pa

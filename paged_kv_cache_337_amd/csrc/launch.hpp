@@ -109,9 +109,12 @@ hipError_t launch_decode(const DecodeParams& p, int dtype, int D, hipStream_t st
 
 bool decode_supported(int dtype, int D, int G);
 
-// Read probe: n chunks of 8 KiB of buf in the order of ids (device).
-hipError_t launch_probe_read(const void* buf, int64_t nchunks_buf, const int32_t* ids, int n, void* sink,
-                             hipStream_t stream);
+// Read probe: n chunks of 8 KiB of buf in the order of ids (device), with one
+// of the probe's load forms, wg_per_cu workgroups of four waves per CU and
+// in_flight chunks in flight per wave.
+bool probe_supported(int load_form, int wg_per_cu, int in_flight);
+hipError_t launch_probe_read(const void* buf, int64_t nchunks_buf, const int32_t* ids, int n, int load_form,
+                             int wg_per_cu, int in_flight, void* sink, hipStream_t stream);
 
 // Causal prefill of the newest tokens of each sequence (same shape support as
 // decode).  Returns hipErrorInvalidValue when the grid would exceed its limit.

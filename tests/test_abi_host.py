@@ -263,3 +263,11 @@ def test_binding_rejects_mismatched_tensors_before_any_launch():
     assert "query_start" in msg(lambda: pool.prefill(0, q, qs.long(), 3, t[:2], c[:2], 16, 0.1))
     assert "device tensor" in msg(lambda: pool.prefill(0, torch.zeros(5, 4, 64, dtype=bf), qs, 3, t[:2], c[:2], 16, 0.1))
     assert "pairs" in msg(lambda: pool.copy_blocks(torch.zeros(2, 3, dtype=torch.int32)))
+
+
+def test_probe_rejects_unknown_load_forms_without_a_device():
+    import ctypes as C
+    for form, wg, infl in ((5, 2, 2), (-1, 2, 2), (0, 0, 2), (0, 5, 2), (0, 2, 3), (3, 2, 4)):
+        rc = pa.lib.pa_probe_read_chunks(None, 0, None, 0, form, wg, infl, None, None)
+        assert pa.STATUS.get(rc) == "UNSUPPORTED", (form, wg, infl)
+    assert pa.lib.pa_probe_read_chunks(None, 0, None, 0, 4, 2, 2, None, None) == 0  # nothing to read
