@@ -46,6 +46,9 @@ def parse():
     ap.add_argument("--contiguous", action="store_true",
                     help="place every sequence's blocks side by side in logical order (a "
                          "contiguous-cache control for the same kernel)")
+    ap.add_argument("--separate-calls", action="store_true",
+                    help="decode workloads: a step is pa_write_kv then pa_decode (two calls) instead of "
+                         "pa_decode_step (one call, the write beside the plan)")
     ap.add_argument("--layers", type=int, default=4)
     ap.add_argument("--partition-tokens", type=int, default=-1,
                     help="-1: the workload's own setting (0 = library default)")
@@ -690,8 +693,18 @@ def main():
     stream = torch.cuda.current_stream()
     max_ctx = w.max_context_len
 
+    fused = not args.separate_calls
+
     def step(k, ev=None):
         layer = k % L
+        if fused:  # the new tokens' write beside the decode's plan, in one call
+            if ev is not None:
+                ev[0].record(stream)
+            pool.decode_step(layer, k_new, v_new, slot_new, q, tables, ctx, max_ctx, w.scale, P, out=out,
+                             workspace=ws)
+            if ev is not None:
+                ev[1].record(stream)
+            return
         pool.write_kv(layer, k_new, v_new, slot_new)
         if ev is not None:
             ev[0].record(stream)
@@ -774,6 +787,8 @@ def main():
     unique_kv_bytes = len(slots_read) * tok_bytes
     qo_bytes = 2 * w.num_seqs * w.num_q_heads * w.head_dim * eb
     alg_bytes = kv_bytes + qo_bytes + 4 * nblk + 4 * w.num_seqs
+    if fused:  # the new tokens read from their rows and written to their slots, and the slots
+        alg_bytes += 2 * w.num_seqs * tok_bytes + 4 * w.num_seqs
     value = kv_bytes / (ms_per_step * 1e-3) / 1e9
     achieved = alg_bytes / (dec_ms * 1e-3) / 1e9
     res = {
@@ -797,7 +812,8 @@ def main():
             "max_context_len": max_ctx,
             "partition_tokens": P if P else "automatic (at least 512, chosen on the device)",
             "layer_slots_rotated": L,
-            "step": "pa_write_kv (1 new token/seq) + pa_decode",
+            "step": ("pa_decode_step (1 new token/seq written, then decode, one call)" if fused
+                     else "pa_write_kv (1 new token/seq) + pa_decode"),
         },
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "kv_bytes_logical": kv_bytes,
@@ -807,7 +823,8 @@ def main():
         "event_ms_per_step": round(ev_ms, 5),
         "roofline": {
             "bound": "hbm",
-            "kernel": "pa_decode call (plan_kernel + decode kernel + merge_kernel)",
+            "kernel": ("pa_decode_step call (prologue: the write beside the plan; decode kernel; merge kernel)"
+                       if fused else "pa_decode call (plan_kernel + decode kernel + merge_kernel)"),
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",

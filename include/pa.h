@@ -181,6 +181,18 @@ int pa_decode(const pa_pool* pool, int layer, const void* q, int num_seqs, int n
               int partition_tokens, void* workspace, size_t ws_bytes, void* out,
               void* stream);
 
+/* One decode step: pa_write_kv of the new tokens, then pa_decode, in one call
+ * ("How Paged Attention Works", Steps 2-4: the new token's K/V go into its
+ * slot, then attention reads the sequence through its table).  Results, pool
+ * contents and errors are those of the two calls in that order; the write
+ * runs in the same launch as the decode's plan (which reads no K/V), which
+ * saves a launch and the plan's time.  k, v, slot_mapping, num_tokens as for
+ * pa_write_kv (num_tokens = 0: no write); the rest as for pa_decode. */
+int pa_decode_step(pa_pool* pool, int layer, const void* k, const void* v, const int32_t* slot_mapping,
+                   int num_tokens, const void* q, int num_seqs, int num_q_heads, const int32_t* block_tables,
+                   int max_blocks_per_seq, const int32_t* context_lens, int max_context_len, float scale,
+                   int partition_tokens, void* workspace, size_t ws_bytes, void* out, void* stream);
+
 /* Comparison point, no part of the paged method: pa_decode over sequences
  * whose blocks are consecutive, with no block table at all -- sequence i's
  * position p lies in physical block first_block[i] + p / bs, slot p % bs, as

@@ -31,7 +31,8 @@ ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2}
 # Every symbol include/pa.h declares, in declaration order.
 EXPORTS = [
     "pa_version", "pa_last_error", "pa_pool_required_bytes", "pa_alloc_pool", "pa_free",
-    "pa_write_kv", "pa_decode_workspace_bytes", "pa_decode", "pa_decode_contiguous", "pa_decode_noalloc",
+    "pa_write_kv", "pa_decode_workspace_bytes", "pa_decode", "pa_decode_step", "pa_decode_contiguous",
+    "pa_decode_noalloc",
     "pa_decode_noalloc_scratch_bytes", "pa_prefill", "pa_copy_blocks",
     "pa_seq_create", "pa_seq_append", "pa_prefix_cache_enable", "pa_seq_append_tokens",
     "pa_prefix_cache_stats", "pa_host_block_bytes", "pa_host_tier_init", "pa_seq_swap_out",
@@ -81,6 +82,8 @@ def _load():
         "pa_decode_workspace_bytes": (c_sz, [vp, c_int, c_int, c_int, c_int]),
         "pa_decode": (c_int, [vp, c_int, vp, c_int, c_int, vp, c_int, vp, c_int, ctypes.c_float,
                               c_int, vp, c_sz, vp, vp]),
+        "pa_decode_step": (c_int, [vp, c_int, vp, vp, vp, c_int, vp, c_int, c_int, vp, c_int, vp, c_int,
+                                   ctypes.c_float, c_int, vp, c_sz, vp, vp]),
         "pa_decode_contiguous": (c_int, [vp, c_int, vp, c_int, c_int, vp, vp, c_int, ctypes.c_float, c_int,
                                          vp, c_sz, vp, vp]),
         "pa_decode_noalloc": (c_int, [vp, c_int, vp, c_int, c_int, vp, c_int, vp, c_int, ctypes.c_float,
@@ -279,6 +282,43 @@ class Pool:
                              int(block_tables.shape[1]), _ptr(context_lens), int(max_context_len),
                              float(scale), int(partition_tokens), _ptr(workspace), wsb, _ptr(out),
                              _stream(stream)), "pa_decode")
+        return out
+
+    def decode_step(self, layer: int, k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor,
+                    q: torch.Tensor, block_tables: torch.Tensor, context_lens: torch.Tensor,
+                    max_context_len: int, scale: float, partition_tokens: int = 0,
+                    out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                    stream=None) -> torch.Tensor:
+        """write_kv(k, v, slot_mapping) then decode(...), in one call (pa_decode_step)."""
+        fn, dt = "pa_decode_step", TORCH_DTYPE[self.dtype]
+        _need(slot_mapping, fn, "slot_mapping", torch.int32, 1)
+        n = int(slot_mapping.shape[0])
+        for name, t in (("k", k), ("v", v)):
+            _need(t, fn, name, dt, 3, self.D, self.H, n)
+        _need(q, fn, "q", dt, 3, self.D)
+        S, Hq, _ = q.shape
+        _need(block_tables, fn, "block_tables", torch.int32, 2, min_rows=S)
+        _need(context_lens, fn, "context_lens", torch.int32, 1, min_rows=S)
+        if out is not None:
+            _need(out, fn, "out", dt, 3, self.D, Hq, S)
+        if workspace is not None:
+            _need(workspace, fn, "workspace")
+        _on_device(fn, ("k", k), ("v", v), ("slot_mapping", slot_mapping), ("q", q),
+                   ("block_tables", block_tables), ("context_lens", context_lens), ("out", out),
+                   ("workspace", workspace))
+        self._need_device()
+        if out is None:
+            out = torch.empty_like(q)
+        if workspace is None:
+            need = self.workspace_bytes(S, Hq, max_context_len, partition_tokens)
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+            if stream is not None:
+                workspace.record_stream(stream)
+        _check(lib.pa_decode_step(self.handle, layer, _ptr(k), _ptr(v), _ptr(slot_mapping), n, _ptr(q), S, Hq,
+                                  _ptr(block_tables), int(block_tables.shape[1]), _ptr(context_lens),
+                                  int(max_context_len), float(scale), int(partition_tokens), _ptr(workspace),
+                                  workspace.numel() * workspace.element_size(), _ptr(out), _stream(stream)),
+               "pa_decode_step")
         return out
 
     def decode_contiguous(self, layer: int, q: torch.Tensor, first_block: torch.Tensor,

@@ -105,6 +105,25 @@ int guarded(F&& f) {
   }
 }
 
+// PA_DEBUG check of a write's slot mapping: copied to the host (synchronising
+// the stream), every slot in range or -1, no slot twice.
+int check_slots_debug(const pa_pool* pool, const int32_t* slot_mapping, int num_tokens, hipStream_t s) {
+  std::vector<int32_t> h(num_tokens);
+  hipError_t e = hipMemcpyAsync(h.data(), slot_mapping, sizeof(int32_t) * num_tokens, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e, "PA_DEBUG slot readback");
+  const int64_t nslots = static_cast<int64_t>(pool->desc.num_blocks) * pool->desc.block_size;
+  std::vector<int32_t> sorted;
+  for (int32_t x : h) {
+    if (x < -1 || x >= nslots) return fail(PA_ERR_INVALID_ARG, "slot " + std::to_string(x) + " out of range");
+    if (x >= 0) sorted.push_back(x);
+  }
+  std::sort(sorted.begin(), sorted.end());
+  if (std::adjacent_find(sorted.begin(), sorted.end()) != sorted.end())
+    return fail(PA_ERR_INVALID_ARG, "slot_mapping holds a repeated slot");
+  return PA_OK;
+}
+
 int alloc_status(pa::AllocResult r, const std::string& msg) {
   switch (r) {
     case pa::AllocResult::Ok:
@@ -172,20 +191,8 @@ int pa_write_kv(pa_pool* pool, int layer, const void* k, const void* v,
     if (!aligned16(k) || !aligned16(v)) return fail(PA_ERR_INVALID_ARG, "k and v must be 16-byte aligned");
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (debug_enabled()) {
-      std::vector<int32_t> h(num_tokens);
-      hipError_t e = hipMemcpyAsync(h.data(), slot_mapping, sizeof(int32_t) * num_tokens,
-                                    hipMemcpyDeviceToHost, s);
-      if (e == hipSuccess) e = hipStreamSynchronize(s);
-      if (e != hipSuccess) return hip_fail(e, "PA_DEBUG slot readback");
-      const int64_t nslots = static_cast<int64_t>(pool->desc.num_blocks) * pool->desc.block_size;
-      std::vector<int32_t> sorted;
-      for (int32_t x : h) {
-        if (x < -1 || x >= nslots) return fail(PA_ERR_INVALID_ARG, "slot " + std::to_string(x) + " out of range");
-        if (x >= 0) sorted.push_back(x);
-      }
-      std::sort(sorted.begin(), sorted.end());
-      if (std::adjacent_find(sorted.begin(), sorted.end()) != sorted.end())
-        return fail(PA_ERR_INVALID_ARG, "slot_mapping holds a repeated slot");
+      const int rc = check_slots_debug(pool, slot_mapping, num_tokens, s);
+      if (rc != PA_OK) return rc;
     }
     hipError_t e = pa::launch_write_kv(geom_of(pool), layer, k, v, slot_mapping, num_tokens, s);
     return e == hipSuccess ? PA_OK : hip_fail(e, "write_kv launch");
@@ -215,9 +222,16 @@ int pa::set_error(int code, const std::string& msg) { return fail(code, msg); }
 int pa::decode_call(const pa_pool* pool, int layer, const void* q, int num_seqs, int num_q_heads,
                     const int32_t* block_tables, int max_blocks_per_seq, const int32_t* context_lens,
                     int max_context_len, float scale, int partition_tokens, void* workspace, size_t ws_bytes,
-                    void* out, void* stream, bool noalloc, bool flat) {
+                    void* out, void* stream, bool noalloc, bool flat, const NewTokens* write) {
   return guarded([&]() -> int {
     if (flat) max_blocks_per_seq = 1;
+    if (write && write->num_tokens < 0) return fail(PA_ERR_INVALID_ARG, "token count cannot be negative");
+    if (write && write->num_tokens > 0) {
+      if (!write->k || !write->v || !write->slot_mapping) return fail(PA_ERR_INVALID_ARG, "NULL device pointer");
+      if (!aligned16(write->k) || !aligned16(write->v))
+        return fail(PA_ERR_INVALID_ARG, "k and v must be 16-byte aligned");
+      if (pool && pool->desc.num_kv_heads > 65535) return fail(PA_ERR_UNSUPPORTED, "at most 65535 kv heads");
+    }
     if (!pool) return fail(PA_ERR_INVALID_ARG, "pool is NULL");
     const pa_pool_desc& d = pool->desc;
     if (layer < 0 || layer >= d.num_layers) return fail(PA_ERR_INVALID_ARG, "layer out of range");
@@ -254,6 +268,10 @@ int pa::decode_call(const pa_pool* pool, int layer, const void* q, int num_seqs,
     if (reinterpret_cast<uintptr_t>(workspace) & 255u)
       return fail(PA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
     hipStream_t s = static_cast<hipStream_t>(stream);
+    if (!noalloc && debug_enabled() && write && write->num_tokens > 0) {
+      const int rc = check_slots_debug(pool, write->slot_mapping, write->num_tokens, s);
+      if (rc != PA_OK) return rc;
+    }
     if (!noalloc && debug_enabled()) {
       std::vector<int32_t> hc(num_seqs), ht(static_cast<size_t>(num_seqs) * max_blocks_per_seq);
       hipError_t e = hipMemcpyAsync(hc.data(), context_lens, sizeof(int32_t) * num_seqs, hipMemcpyDeviceToHost, s);
@@ -312,12 +330,30 @@ int pa::decode_call(const pa_pool* pool, int layer, const void* q, int num_seqs,
     // shared block id, so tables from any source stay correct either way.
     p.share = !flat && pool->alloc.shared_blocks() > 0 ? 1 : 0;
     p.flat = flat ? 1 : 0;
+    if (write && write->num_tokens > 0) {
+      p.w_k = write->k;
+      p.w_v = write->v;
+      p.w_slots = write->slot_mapping;
+      p.w_tokens = write->num_tokens;
+    }
     hipError_t e = pa::launch_decode(p, d.dtype, d.head_dim, s);
     return e == hipSuccess ? PA_OK : hip_fail(e, "decode launch");
   });
 }
 
 extern "C" {
+
+int pa_decode_step(pa_pool* pool, int layer, const void* k, const void* v, const int32_t* slot_mapping,
+                   int num_tokens, const void* q, int num_seqs, int num_q_heads, const int32_t* block_tables,
+                   int max_blocks_per_seq, const int32_t* context_lens, int max_context_len, float scale,
+                   int partition_tokens, void* workspace, size_t ws_bytes, void* out, void* stream) {
+  const pa::NewTokens w{k, v, slot_mapping, num_tokens};
+  if (num_seqs == 0 && num_tokens > 0)  // nothing to decode: the write alone
+    return pa_write_kv(pool, layer, k, v, slot_mapping, num_tokens, stream);
+  return pa::decode_call(pool, layer, q, num_seqs, num_q_heads, block_tables, max_blocks_per_seq, context_lens,
+                         max_context_len, scale, partition_tokens, workspace, ws_bytes, out, stream, false, false,
+                         &w);
+}
 
 int pa_decode_contiguous(const pa_pool* pool, int layer, const void* q, int num_seqs, int num_q_heads,
                          const int32_t* first_block, const int32_t* context_lens, int max_context_len,

@@ -19,9 +19,17 @@ int set_error(int code, const std::string& msg);
 // workspace beyond the scratch as a size limit of that entry point.  `flat`
 // marks the table-free comparison call: block_tables is then one first block
 // id per sequence and max_blocks_per_seq is ignored.
+// New tokens to write before the decode (pa_decode_step).
+struct NewTokens {
+  const void* k;
+  const void* v;
+  const int32_t* slot_mapping;
+  int num_tokens;
+};
+
 int decode_call(const pa_pool* pool, int layer, const void* q, int num_seqs, int num_q_heads,
                 const int32_t* block_tables, int max_blocks_per_seq, const int32_t* context_lens,
                 int max_context_len, float scale, int partition_tokens, void* workspace, size_t ws_bytes,
-                void* out, void* stream, bool noalloc, bool flat = false);
+                void* out, void* stream, bool noalloc, bool flat = false, const NewTokens* write = nullptr);
 
 }  // namespace pa

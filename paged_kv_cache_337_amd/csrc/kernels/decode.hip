@@ -62,6 +62,7 @@
 #include "../launch.hpp"
 #include "common.hpp"
 #include "stream.hpp"
+#include "write.hpp"
 
 namespace pa {
 
@@ -284,7 +285,7 @@ __device__ __forceinline__ int clamp_ctx(const DecodeParams& p, int i) {
 constexpr int kItemsPerWorkgroup = PA_ITEMS_PER_WG;
 constexpr int kMaxAutoPartition = 4096;
 
-__global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeParams p) {
+__device__ __forceinline__ void plan_plain(const DecodeParams& p) {
   __shared__ int cnt[kPlanBins];
   __shared__ int off[kPlanBins];
   __shared__ int wsum[kPlanThreads / 64];
@@ -454,7 +455,7 @@ __device__ __forceinline__ int block_scan(int v, int* wsum, int& total) {
   return before + x - v;
 }
 
-__global__ __launch_bounds__(kPlanThreads) void plan_share_kernel(DecodeParams p) {
+__device__ __forceinline__ void plan_share(const DecodeParams& p) {
   __shared__ int hk[kShareHash];          // first block ids (-1 = empty), then size bins
   __shared__ int hv[kShareHash];          // lowest sequence per first block, then bin offsets
   __shared__ int lead[kShareMaxSeqs];     // lowest sequence of each sequence's group
@@ -673,6 +674,57 @@ __global__ __launch_bounds__(kPlanThreads) void plan_share_kernel(DecodeParams p
     }
     if (srem > 0) p.items[atomicAdd(&off[bin_of(srem)], 1)] = make_int4(~sid, sfull, sfull * P, Ls);
   }
+}
+
+__global__ __launch_bounds__(kPlanThreads) void plan_kernel(DecodeParams p) { plan_plain(p); }
+
+__global__ __launch_bounds__(kPlanThreads) void plan_share_kernel(DecodeParams p) { plan_share(p); }
+
+// Prologue of pa_decode_step: workgroup 0 plans the decode while the others
+// write the new tokens' K/V (one wave per group of four tokens and kv head,
+// as the write kernel does).  The plan reads no K/V, so the two are
+// independent; the decode kernel that follows sees both.
+// Write tasks per prologue workgroup: the others of its 16 waves exit at
+// once, so the write spreads over many CUs.  Measured on MI355X (cfg3 step,
+// 256 new tokens x 8 kv heads): 16 tasks per workgroup 250.3 us per step, 4
+// tasks 247.9, 2 tasks 247.8, 1 task 247.5.
+#ifndef PA_PROLOGUE_WRITE_WAVES
+#define PA_PROLOGUE_WRITE_WAVES 2
+#endif
+constexpr int kWriteWaves = PA_PROLOGUE_WRITE_WAVES;
+
+template <int kBytes, int D, bool kShare>
+__global__ __launch_bounds__(kPlanThreads) void prologue_kernel(DecodeParams p) {
+  if (blockIdx.x == 0) {
+    if constexpr (kShare) plan_share(p);
+    else plan_plain(p);
+    return;
+  }
+  if (static_cast<int>(threadIdx.x >> 6) >= kWriteWaves) return;
+  const int task = (blockIdx.x - 1) * kWriteWaves + static_cast<int>(threadIdx.x >> 6);
+  const int groups = (p.w_tokens + 3) / 4;
+  if (task >= groups * p.H) return;
+  char* base = static_cast<char*>(const_cast<void*>(p.pool)) + p.layer_off * kBytes;
+  write_token_group<kBytes>(static_cast<const uint4*>(p.w_k), static_cast<const uint4*>(p.w_v), p.w_slots,
+                            p.w_tokens, base, p.N, p.H, p.bs, D, task / p.H, task % p.H, threadIdx.x & 63);
+}
+
+// Plan of a decode call, with the new tokens' write beside it when the call
+// carries one (pa_decode_step).
+template <int kBytes, int D, bool kShare>
+hipError_t launch_plan(const DecodeParams& p, hipStream_t stream) {
+  if (p.w_tokens > 0) {
+    const int64_t tasks = static_cast<int64_t>((p.w_tokens + 3) / 4) * p.H;
+    const int64_t blocks = 1 + (tasks + kWriteWaves - 1) / kWriteWaves;
+    if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((prologue_kernel<kBytes, D, kShare>), dim3(static_cast<unsigned>(blocks)), dim3(kPlanThreads),
+                       0, stream, p);
+  } else if constexpr (kShare) {
+    hipLaunchKernelGGL(plan_share_kernel, dim3(1), dim3(kPlanThreads), 0, stream, p);
+  } else {
+    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, p);
+  }
+  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
@@ -1331,8 +1383,11 @@ hipError_t launch_decode_kernel(DecodeParams p, hipStream_t stream) {
   // times as many states and took 7% longer.
   p.group = (deep && p.P <= kMaxGroupedPartition) ? kWaves : 1;
   if (!p.direct) {
-    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, p);
-    hipError_t e = hipGetLastError();
+    hipError_t e = launch_plan<T::kBytes, D, false>(p, stream);
+    if (e != hipSuccess) return e;
+  } else if (p.w_tokens > 0) {  // no plan to run beside: the write kernel first
+    PoolGeom g{const_cast<void*>(p.pool), 1, p.N, p.bs, p.H, D, 0, T::kBytes};
+    hipError_t e = launch_write_kv(g, 0, p.w_k, p.w_v, p.w_slots, p.w_tokens, stream, p.layer_off * T::kBytes);
     if (e != hipSuccess) return e;
   }
   const int4* items = static_cast<const int4*>(p.items);
@@ -1370,8 +1425,7 @@ hipError_t launch_share(DecodeParams p, hipStream_t stream) {
   p.group = 1;
   p.direct = 0;
   p.share_nmax = 16 / p.G < kShareMaxMembers ? 16 / p.G : kShareMaxMembers;
-  hipLaunchKernelGGL(plan_share_kernel, dim3(1), dim3(kPlanThreads), 0, stream, p);
-  hipError_t e = hipGetLastError();
+  hipError_t e = launch_plan<T::kBytes, D, true>(p, stream);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((decode_kernel<Path, T, D, kShareDeep, true>), dim3(grid), dim3(kThreads), 0, stream, p,
                      static_cast<const int4*>(p.items), p.groups, p.seq_np);

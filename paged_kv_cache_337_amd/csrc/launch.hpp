@@ -48,6 +48,11 @@ struct DecodeParams {
   int4* groups;              // [S / 2] member sequences of each shared group (-1 = none)
   int32_t flat;              // 1: no block table; tables[i] (max_blocks = 1) is sequence i's first
                              //    block and its blocks are consecutive (contiguous-layout comparison)
+  // new tokens written before the decode (pa_decode_step; w_tokens = 0: none)
+  const void* w_k;           // [w_tokens, H, D] pool dtype
+  const void* w_v;
+  const int32_t* w_slots;    // [w_tokens] global slots, -1 = skip
+  int32_t w_tokens;
 };
 
 struct PrefillParams {
@@ -94,8 +99,10 @@ inline WsLayout decode_ws_layout(int S, int Hq, int max_parts, int D) {
   return w;
 }
 
+// The write kernel over layer `layer`, or (layer_byte_off >= 0) over the
+// layer that starts layer_byte_off bytes into the pool.
 hipError_t launch_write_kv(const PoolGeom& g, int layer, const void* k, const void* v,
-                           const int32_t* slots, int num_tokens, hipStream_t stream);
+                           const int32_t* slots, int num_tokens, hipStream_t stream, int64_t layer_byte_off = -1);
 
 hipError_t launch_copy_blocks(const PoolGeom& g, const int32_t* pairs, int n, hipStream_t stream);
 

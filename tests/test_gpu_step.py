@@ -1,0 +1,135 @@
+"""pa_decode_step (write the new tokens, then decode, in one call) against
+pa_write_kv followed by pa_decode, through the C ABI.
+
+Each pool starts with every cached token except each sequence's newest one;
+the step writes the newest tokens and decodes.  Checked: the outputs and the
+whole pool equal those of the two separate calls bit for bit, and every output
+element matches the oracle (which attends to the newest token too, so a decode
+that ran before the write would fail).  Cases: the plain plan (several
+partitions, automatic size), a direct launch (no plan), explicit small
+partitions (grouped items), the sharing plan (forked branches), a skipped
+(-1) slot, and a step with no new tokens.
+"""
+import numpy as np
+import pytest
+import torch
+
+pytestmark = pytest.mark.gpu
+
+import workloads as W  # noqa: E402
+from tests import gpu_util as U  # noqa: E402
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU")
+    import paged_kv_cache_337_amd  # noqa: F401
+
+
+def _fill_all_but_last(pool, w, tables):
+    import paged_kv_cache_337_amd as pa
+    ks, vs = [], []
+    for i in range(w.num_seqs):
+        K, V = w.seq_kv(i)
+        ks.append(K[:-1])
+        vs.append(V[:-1])
+    slots = pa.slots_for_positions(tables, w.block_size, np.zeros(w.num_seqs), w.context_lens - 1)
+    if len(slots):
+        pool.write_kv(0, U.dev_tensor(np.concatenate(ks), w.dtype), U.dev_tensor(np.concatenate(vs), w.dtype),
+                      torch.from_numpy(slots).cuda())
+    torch.cuda.synchronize()
+
+
+def _new_tokens(w, tables, skip=()):
+    import paged_kv_cache_337_amd as pa
+    last = w.context_lens - 1
+    kn = np.stack([w.seq_kv(i)[0][last[i]] for i in range(w.num_seqs)])
+    vn = np.stack([w.seq_kv(i)[1][last[i]] for i in range(w.num_seqs)])
+    slots = pa.slots_for_positions(tables, w.block_size, last, np.ones(w.num_seqs)).astype(np.int32)
+    for i in skip:
+        slots[i] = -1
+    return U.dev_tensor(kn, w.dtype), U.dev_tensor(vn, w.dtype), torch.from_numpy(slots).cuda()
+
+
+CASES = {
+    "planned": lambda: W.scaled_down(W.llama3_8b(), 40, 2500),
+    "direct": lambda: W.custom("step_direct", 61, "f16", [5, 100, 300, 511, 64], 8, 8, 128, 16),
+    "grouped": lambda: W.custom("step_grouped", 62, "bf16", [3000, 900, 2047, 4096] * 8, 64, 8, 128, 32,
+                                partition_tokens=64),
+    "f32": lambda: W.custom("step_f32", 63, "f32", [17, 600, 1300, 40, 999], 8, 4, 64, 16),
+}
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_step_equals_write_then_decode(name):
+    w = CASES[name]()
+    pools, outs = [], []
+    for fused in (False, True):
+        pool = U.make_pool(w)
+        _fill_all_but_last(pool, w, w.block_tables)
+        q, t, c = U.device_inputs(w)
+        kn, vn, sl = _new_tokens(w, w.block_tables)
+        if fused:
+            out = pool.decode_step(0, kn, vn, sl, q, t, c, w.max_context_len, w.scale, w.partition_tokens)
+        else:
+            pool.write_kv(0, kn, vn, sl)
+            out = pool.decode(0, q, t, c, w.max_context_len, w.scale, w.partition_tokens)
+        torch.cuda.synchronize()
+        pools.append(U.pool_bits(pool))
+        outs.append(out.cpu())
+    U.log(f"[step] {name}: S={w.num_seqs} max_ctx={w.max_context_len} P={w.partition_tokens}")
+    bits = U.TORCH_BITS[w.dtype]
+    assert torch.equal(outs[0].view(bits), outs[1].view(bits))
+    assert np.array_equal(pools[0], pools[1])
+    U.check_close(U.out_f64(outs[1]), U.oracle_rows(w, range(w.num_seqs)), w.dtype, f"step {name}")
+
+
+def test_step_with_sharing_plan_and_skipped_slot():
+    """Forked branches (the block manager holds shared blocks, so the sharing
+    plan runs in the step's prologue); one branch's newest token is skipped
+    (-1), so its output must equal attention over its context without it."""
+    import paged_kv_cache_337_amd as pa
+    w = W.shared()
+    pool = pa.Pool(1, w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim, w.dtype,
+                   free_order=w.script["free_order"])
+    U.poison(pool)
+    from paged_kv_cache_337_amd import staging as S
+    S.run_shared_script(pool, w, W.shared_prefix_kv, W.private_kv, layers=(0,))
+    width = max(len(pool.seq_block_table(s)[0]) for s in range(w.num_seqs))
+    tables, ctx = pool.batch_tables(list(range(w.num_seqs)), width)
+    q, t, c = U.device_inputs(w, tables=tables, ctx=ctx)
+    # rewrite every newest token with new values through the step, except branch 5
+    rng = np.random.default_rng(9)
+    kn = W.round_to_storage(rng.standard_normal((w.num_seqs, w.num_kv_heads, w.head_dim), dtype=np.float32), "bf16")
+    vn = W.round_to_storage(rng.standard_normal((w.num_seqs, w.num_kv_heads, w.head_dim), dtype=np.float32), "bf16")
+    slots = pa.slots_for_positions(tables, w.block_size, ctx - 1, np.ones(w.num_seqs)).astype(np.int32)
+    slots[5] = -1
+    ws = torch.empty(pool.workspace_bytes(w.num_seqs, w.num_q_heads, int(ctx.max()), 0), dtype=torch.uint8,
+                     device="cuda")
+    out = pool.decode_step(0, U.dev_tensor(kn, "bf16"), U.dev_tensor(vn, "bf16"), torch.from_numpy(slots).cuda(),
+                           q, t, c, int(ctx.max()), w.scale, 0, workspace=ws)
+    torch.cuda.synchronize()
+    assert int(ws[:16].view(torch.int32)[3].item()) == w.script["groups"]
+    from oracle import attention as A
+    ref = []
+    for i in range(w.num_seqs):
+        K, V = w.seq_kv(i)
+        K, V = K.copy(), V.copy()
+        if i != 5:
+            K[-1], V[-1] = kn[i], vn[i]
+        ref.append(A.decode_one(A.to_f64(w.q[i], "bf16"), A.to_f64(K, "bf16"), A.to_f64(V, "bf16"), w.scale))
+    U.check_close(U.out_f64(out), np.stack(ref), "bf16", "step with the sharing plan")
+
+
+def test_step_without_new_tokens_is_a_decode():
+    w = W.scaled_down(W.llama3_8b(), 12, 1500, seed_offset=77)
+    pool = U.make_pool(w)
+    U.fill_pool(pool, w)
+    q, t, c = U.device_inputs(w)
+    empty_kv = torch.empty(0, w.num_kv_heads, w.head_dim, dtype=torch.bfloat16, device="cuda")
+    out = pool.decode_step(0, empty_kv, empty_kv, torch.empty(0, dtype=torch.int32, device="cuda"), q, t, c,
+                           w.max_context_len, w.scale)
+    ref = pool.decode(0, q, t, c, w.max_context_len, w.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
