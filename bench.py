@@ -122,17 +122,23 @@ def copy_calibration(pool, w, layers, blocks):
     return nbytes
 
 
-def counter_traffic(record: str, workload: str):
+# committed rocprofv3 counter records of the decode workloads
+PROFILE_RECORDS = {"llama3_8b": "decode_llama3_8b_b256", "opt13b": "decode_opt13b_b64",
+                   "long_ctx": "decode_long_ctx_b8", "shared": "decode_shared_b64"}
+
+
+def counter_traffic(record: str, workload: str, call: str):
     """HBM bytes per call from a committed rocprofv3 counter record
     (profiles/<record>.traffic.json: FETCH_SIZE + WRITE_SIZE, scaled by a copy
-    of known size), or None when the record is for another workload or any of
-    the kernel's sources changed since it was taken."""
+    of known size), or None when the record is for another workload or call,
+    or any of the kernels' sources changed since it was taken."""
     rec = os.path.join(ROOT, "profiles", record + ".traffic.json")
     if not os.path.exists(rec):
         return None
     with open(rec) as f:
         r = json.load(f)
-    if r.get("workload") != workload or r.get("sources_sha256") != sources_sha256(r["kernel_sources"]):
+    if (r.get("workload") != workload or r.get("call") != call
+            or r.get("sources_sha256") != sources_sha256(r["kernel_sources"])):
         return None
     return int(r["traffic_bytes_per_call"])
 
@@ -829,8 +835,10 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": (counter_traffic("decode_llama3_8b_b256", w.name)
-                        if P == w.partition_tokens and L == 4 and not args.contiguous else None),
+            "traffic": (counter_traffic(PROFILE_RECORDS[w.name], w.name,
+                                        "pa_decode_step" if fused else "pa_decode")
+                        if w.name in PROFILE_RECORDS and P == w.partition_tokens and L == 4
+                        and not args.contiguous else None),
             "alg_bytes_per_launch": alg_bytes,
             "avg_launch_ms": round(dec_ms, 5),
             "median_launch_ms": round(float(np.median(call_ms)), 5),
