@@ -127,17 +127,18 @@ PROFILE_RECORDS = {"llama3_8b": "decode_llama3_8b_b256", "opt13b": "decode_opt13
                    "long_ctx": "decode_long_ctx_b8", "shared": "decode_shared_b64"}
 
 
-def counter_traffic(record: str, workload: str, call: str):
+def counter_traffic(record: str, workload: str, call: str | None = None):
     """HBM bytes per call from a committed rocprofv3 counter record
     (profiles/<record>.traffic.json: FETCH_SIZE + WRITE_SIZE, scaled by a copy
-    of known size), or None when the record is for another workload or call,
+    of known size), or None when the record is for another workload or call
+    (when one is named),
     or any of the kernels' sources changed since it was taken."""
     rec = os.path.join(ROOT, "profiles", record + ".traffic.json")
     if not os.path.exists(rec):
         return None
     with open(rec) as f:
         r = json.load(f)
-    if (r.get("workload") != workload or r.get("call") != call
+    if (r.get("workload") != workload or (call is not None and r.get("call") != call)
             or r.get("sources_sha256") != sources_sha256(r["kernel_sources"])):
         return None
     return int(r["traffic_bytes_per_call"])
@@ -318,11 +319,6 @@ def main_prefill(args):
             "avg_launch_ms": round(pf_ms, 5),
         },
     }
-    if table_free is not None:
-        table_free["achieved"] = round(alg_bytes / (table_free["avg_launch_ms"] * 1e-3) / 1e9, 2)
-        table_free["kv_gbs_per_step"] = round(kv_bytes / (table_free["ms_per_step"] * 1e-3) / 1e9, 2)
-        table_free["table_cost_pct"] = round(100 * (dec_ms / table_free["avg_launch_ms"] - 1), 2)
-        res["table_free"] = table_free
     if args.copy_calib_blocks > 0:
         res["copy_calibration_bytes"] = copy_calibration(pool, w, L, args.copy_calib_blocks)
     if not args.no_cpu_baseline:

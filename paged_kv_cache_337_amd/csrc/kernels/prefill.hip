@@ -30,6 +30,7 @@
 // caller declared, table reads stay inside the row and block ids outside
 // [0, N) read block 0 and are masked.
 #include <algorithm>
+#include <type_traits>
 
 #include "../launch.hpp"
 #include "common.hpp"
@@ -263,12 +264,12 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillParams 
 // position and inside the context take no mask, and the row sums come from
 // one more MFMA of P against ones.
 // ---------------------------------------------------------------------------
-template <int D, int NP>
+template <int D, int NP, int NBUF = 2>
 struct PrefillLds {
   static constexpr int NCH = D / 32;
   static constexpr int NT = D / 16;
-  uint4 k[2][2 * NP][NCH][64];  // [buffer][unit][chunk][lane]
-  uint2 v[2][NP][NT][64][2];    // [buffer][pair][head_dim tile][lane][unit of the pair]
+  uint4 k[NBUF][2 * NP][NCH][64];  // [buffer][unit][chunk][lane]
+  uint2 v[NBUF][NP][NT][64][2];    // [buffer][pair][head_dim tile][lane][unit of the pair]
 };
 
 // Zero the 16-bit entries of tokens >= valid in a V chunk: lane group grp
@@ -280,8 +281,18 @@ __device__ __forceinline__ uint4 zero_v_tail(uint4 x, int grp, int valid) {
   return make_uint4(x.x & m01, x.y & m23, x.z & m01, x.w & m23);
 }
 
+#ifndef PA_PREFILL_PIPE
+#define PA_PREFILL_PIPE 0
+#endif
+#ifndef PA_PREFILL_PIPE_SCHED
+#define PA_PREFILL_PIPE_SCHED 0
+#endif
+#ifndef PA_PREFILL_WAVES_PER_EU
+#define PA_PREFILL_WAVES_PER_EU 2
+#endif
 template <typename T, int D, int NW, int NB, int NP>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4))) void prefill_lds_kernel(
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(PA_PREFILL_WAVES_PER_EU,
+                                                                         PA_PREFILL_WAVES_PER_EU))) void prefill_lds_kernel(
     PrefillParams p, const int32_t* __restrict__ tables) {
   static_assert(T::kBytes == 2, "16-bit pools only");
   constexpr int NCH = D / 32;  // 1 KiB chunks per sub-tile
@@ -290,9 +301,11 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
   constexpr int kKeys = 16 * kUnits;     // keys per stage
   constexpr int kRowsWave = 16 * NB;
   constexpr int kRowsWG = kRowsWave * NW;
-  constexpr int kLoads = 2 * kUnits * NCH / NW;  // chunk loads per wave per stage
-  static_assert(kLoads >= 1 && kLoads <= NCH && NCH % kLoads == 0 && (2 * kUnits * NCH) % NW == 0,
-                "each wave loads a part of one sub-tile");
+  // Sub-tiles (the K or the V of one unit) per wave per stage: one (eight
+  // waves), or the K and the V of one unit (four waves).
+  constexpr int kSPW = 2 * kUnits / NW;
+  static_assert(kSPW * NW == 2 * kUnits && (kSPW == 1 || kSPW == 2), "whole sub-tiles per wave");
+  constexpr int kLoads = kSPW * NCH;  // chunk loads per wave per stage
   using B = typename T::bits;
   __shared__ PrefillLds<D, NP> sm;
 
@@ -354,12 +367,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
     m_ref[b] = kNegInfP;
   }
 
-  // Load assignment: sub-tile `sub` (unit sub >> 1, K or V by sub & 1),
-  // chunks [c0, c0 + kLoads).
-  const int sub = (wave * kLoads) / NCH;
-  const int unit = sub >> 1;
-  const bool is_v = sub & 1;
-  const int c0 = (wave * kLoads) % NCH;
+  // Load assignment: sub-tiles wave * kSPW .. (unit = sub-tile >> 1, K or V
+  // by its low bit), every chunk of each.
+  const int unit = (wave * kSPW) >> 1;
+  auto sub_is_v = [&](int j) { return kSPW == 2 ? j == 1 : (wave & 1) == 1; };
   // The table row is read with scalar loads (a __restrict__ argument), so
   // that locating a unit never waits on the vector loads in flight.
   const int32_t* trow = tables + static_cast<size_t>(i) * p.max_blocks;
@@ -376,39 +387,47 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
     const int32_t bid = my_lb < p.max_blocks ? trow[my_lb] : -1;
     const bool ok = bid >= 0 && bid < p.N;
     const size_t region = (static_cast<size_t>(ok ? bid : 0) * p.H + h) * (2 * static_cast<size_t>(p.bs) * D);
-    const char* src = layer_base + (region + (is_v ? static_cast<size_t>(p.bs) * D : 0) +
-                                    static_cast<size_t>(my_sub) * 16 * D) * 2;
+    const char* kv = layer_base + (region + static_cast<size_t>(my_sub) * 16 * D) * 2;
     my_sub += kUnits;
     while (my_sub >= subs) {
       my_sub -= subs;
       ++my_lb;
     }
-    const uint4* sp = reinterpret_cast<const uint4*>(src) + lane;
 #pragma unroll
-    for (int j = 0; j < kLoads; ++j) r[j] = sp[64 * (c0 + j)];
+    for (int j = 0; j < kSPW; ++j) {
+      const uint4* sp = reinterpret_cast<const uint4*>(kv + (sub_is_v(j) ? static_cast<size_t>(p.bs) * D * 2 : 0)) +
+                        lane;
+#pragma unroll
+      for (int cc = 0; cc < NCH; ++cc) r[j * NCH + cc] = sp[64 * cc];
+    }
     const int left = c - s * kKeys - unit * 16;
     valid = !ok ? 0 : (left < 0 ? 0 : (left < 16 ? left : 16));
   };
   auto to_lds = [&](uint4 (&r)[kLoads], int valid, int buf) {
-    if (valid < 16) {  // wave-uniform: the context's last unit, or an invalid block
+#pragma unroll
+    for (int j = 0; j < kSPW; ++j) {
+      uint4* rj = r + j * NCH;
+      const bool is_v = sub_is_v(j);
+      if (valid < 16) {  // wave-uniform: the context's last unit, or an invalid block
+        if (is_v) {
+#pragma unroll
+          for (int cc = 0; cc < NCH; ++cc) rj[cc] = zero_v_tail(rj[cc], grp, valid);
+        } else {
+#pragma unroll
+          for (int cc = 0; cc < NCH; ++cc)
+            if (col >= valid) rj[cc] = make_uint4(0, 0, 0, 0);
+        }
+      }
       if (is_v) {
 #pragma unroll
-        for (int j = 0; j < kLoads; ++j) r[j] = zero_v_tail(r[j], grp, valid);
+        for (int cc = 0; cc < NCH; ++cc) {
+          sm.v[buf][unit >> 1][2 * cc][lane][unit & 1] = make_uint2(rj[cc].x, rj[cc].y);
+          sm.v[buf][unit >> 1][2 * cc + 1][lane][unit & 1] = make_uint2(rj[cc].z, rj[cc].w);
+        }
       } else {
 #pragma unroll
-        for (int j = 0; j < kLoads; ++j)
-          if (col >= valid) r[j] = make_uint4(0, 0, 0, 0);
+        for (int cc = 0; cc < NCH; ++cc) sm.k[buf][unit][cc][lane] = rj[cc];
       }
-    }
-    if (is_v) {
-#pragma unroll
-      for (int j = 0; j < kLoads; ++j) {
-        sm.v[buf][unit >> 1][2 * (c0 + j)][lane][unit & 1] = make_uint2(r[j].x, r[j].y);
-        sm.v[buf][unit >> 1][2 * (c0 + j) + 1][lane][unit & 1] = make_uint2(r[j].z, r[j].w);
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < kLoads; ++j) sm.k[buf][unit][c0 + j][lane] = r[j];
     }
   };
 
@@ -553,6 +572,285 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
   }
 }
 
+// ---------------------------------------------------------------------------
+// 16-bit pools, pipelined across stages: the same workgroup shape, LDS layout
+// and MFMA forms as prefill_lds_kernel, but three LDS buffers, so that a wave
+// computes the scores of stage s while the P.V product of stage s - 1 (its V
+// still in its buffer, its weights in registers) runs beside stage s's
+// softmax.  Each iteration issues stage s's score MFMAs, then stage s - 1's
+// P.V MFMAs interleaved with the VALU work of stage s's reference, mask and
+// exponentials; a raised reference rescales the accumulators only after that
+// P.V has landed (they then hold every stage up to s - 1, all relative to the
+// old reference), so the softmax is unchanged.  Stage s + 1 is written to the
+// third buffer meanwhile; one barrier per stage publishes it.
+// ---------------------------------------------------------------------------
+template <typename T, int D, int NW, int NB, int NP>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(PA_PREFILL_WAVES_PER_EU,
+                                                                         PA_PREFILL_WAVES_PER_EU))) void prefill_pipe_kernel(
+    PrefillParams p, const int32_t* __restrict__ tables) {
+  static_assert(T::kBytes == 2, "16-bit pools only");
+  constexpr int NCH = D / 32;  // 1 KiB chunks per sub-tile
+  constexpr int NT = D / 16;
+  constexpr int kUnits = 2 * NP;         // units per stage
+  constexpr int kKeys = 16 * kUnits;     // keys per stage
+  constexpr int kRowsWave = 16 * NB;
+  constexpr int kRowsWG = kRowsWave * NW;
+  constexpr int kSPW = 2 * kUnits / NW;
+  static_assert(kSPW * NW == 2 * kUnits && (kSPW == 1 || kSPW == 2), "whole sub-tiles per wave");
+  constexpr int kLoads = kSPW * NCH;
+  constexpr int kBuf = 3;
+  using B = typename T::bits;
+  __shared__ PrefillLds<D, NP, kBuf> sm;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = rfl(threadIdx.x >> 6);
+  // Workgroup -> (sequence, kv head, row tile), XCD-aware as in prefill_lds_kernel.
+  const int xcd = blockIdx.x & 7;
+  const int slot = blockIdx.x >> 3;
+  const int pair = (slot / p.tiles) * 8 + xcd;
+  const int y = slot - (slot / p.tiles) * p.tiles;
+  if (pair >= p.S * p.H) return;  // whole workgroup
+  const int i = pair / p.H;
+  const int h = pair - i * p.H;
+  const int G = p.G;
+  const int qs = clampi(p.query_start[i], 0, p.num_q_tokens);
+  const int qe = clampi(p.query_start[i + 1], qs, p.num_q_tokens);
+  const int c = clampi(p.ctx[i], 0, p.ctx_cap);
+  int n = qe - qs;
+  n = n < p.max_query_len ? n : p.max_query_len;
+  n = n < c ? n : c;
+  const int rows = rfl(n * G);
+  const int ntiles = (rows + kRowsWG - 1) / kRowsWG;
+  const int tile = ntiles - 1 - y;
+  if (tile < 0) return;  // whole workgroup
+  const int first_pos = c - n;
+  const int wg_last_row = (tile * kRowsWG + kRowsWG < rows ? tile * kRowsWG + kRowsWG : rows) - 1;
+  const int nst = (first_pos + wg_last_row / G + kKeys) / kKeys;
+  const int r0 = tile * kRowsWG + wave * kRowsWave;
+  const bool active = r0 < rows;
+  const int last_row = (r0 + kRowsWave < rows ? r0 + kRowsWave : rows) - 1;
+  const int kmax = active ? first_pos + last_row / G : -1;
+
+  const int col = lane & 15, grp = lane >> 4;
+  uint4 qb[NB][NCH];
+  f32x4_t acc[NB][NT];
+  f32x4_t lsum[NB];
+  float m_ref[NB];
+  int qpos[NB];
+  int qmin[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    const int row = r0 + 16 * b + col;
+    const bool valid = row < rows;
+    const int k = row / G, g = row - (row / G) * G;
+    qpos[b] = valid ? first_pos + k : -1;
+    qmin[b] = first_pos + (r0 + 16 * b) / G;
+    const char* qbase = static_cast<const char*>(p.q) +
+                        ((static_cast<size_t>(qs) + (valid ? k : 0)) * p.Hq + static_cast<size_t>(h) * G + g) * D * 2;
+#pragma unroll
+    for (int cc = 0; cc < NCH; ++cc)
+      qb[b][cc] = valid ? *reinterpret_cast<const uint4*>(qbase + (cc * 4 + grp) * 16) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[b][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    lsum[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    m_ref[b] = kNegInfP;
+  }
+
+  const int unit = (wave * kSPW) >> 1;
+  auto sub_is_v = [&](int j) { return kSPW == 2 ? j == 1 : (wave & 1) == 1; };
+  const int32_t* trow = tables + static_cast<size_t>(i) * p.max_blocks;
+  const char* layer_base = static_cast<const char*>(p.pool) + p.layer_off * 2;
+  uint4 stg[kLoads];
+  int valid_st;
+  const int subs = p.bs >> 4;
+  int my_lb = unit / subs, my_sub = unit - (unit / subs) * subs;
+  auto issue = [&](int s, uint4 (&r)[kLoads], int& valid) {
+    const int32_t bid = my_lb < p.max_blocks ? trow[my_lb] : -1;
+    const bool ok = bid >= 0 && bid < p.N;
+    const size_t region = (static_cast<size_t>(ok ? bid : 0) * p.H + h) * (2 * static_cast<size_t>(p.bs) * D);
+    const char* kv = layer_base + (region + static_cast<size_t>(my_sub) * 16 * D) * 2;
+    my_sub += kUnits;
+    while (my_sub >= subs) {
+      my_sub -= subs;
+      ++my_lb;
+    }
+#pragma unroll
+    for (int j = 0; j < kSPW; ++j) {
+      const uint4* sp = reinterpret_cast<const uint4*>(kv + (sub_is_v(j) ? static_cast<size_t>(p.bs) * D * 2 : 0)) +
+                        lane;
+#pragma unroll
+      for (int cc = 0; cc < NCH; ++cc) r[j * NCH + cc] = sp[64 * cc];
+    }
+    const int left = c - s * kKeys - unit * 16;
+    valid = !ok ? 0 : (left < 0 ? 0 : (left < 16 ? left : 16));
+  };
+  auto to_lds = [&](uint4 (&r)[kLoads], int valid, int buf) {
+#pragma unroll
+    for (int j = 0; j < kSPW; ++j) {
+      uint4* rj = r + j * NCH;
+      const bool is_v = sub_is_v(j);
+      if (valid < 16) {
+        if (is_v) {
+#pragma unroll
+          for (int cc = 0; cc < NCH; ++cc) rj[cc] = zero_v_tail(rj[cc], grp, valid);
+        } else {
+#pragma unroll
+          for (int cc = 0; cc < NCH; ++cc)
+            if (col >= valid) rj[cc] = make_uint4(0, 0, 0, 0);
+        }
+      }
+      if (is_v) {
+#pragma unroll
+        for (int cc = 0; cc < NCH; ++cc) {
+          sm.v[buf][unit >> 1][2 * cc][lane][unit & 1] = make_uint2(rj[cc].x, rj[cc].y);
+          sm.v[buf][unit >> 1][2 * cc + 1][lane][unit & 1] = make_uint2(rj[cc].z, rj[cc].w);
+        }
+      } else {
+#pragma unroll
+        for (int cc = 0; cc < NCH; ++cc) sm.k[buf][unit][cc][lane] = rj[cc];
+      }
+    }
+  };
+
+  const float sl2 = p.scale_log2;
+  const uint4 ones = make_uint4(ones2<T>(), ones2<T>(), ones2<T>(), ones2<T>());
+  uint4 pbp[NB][NP];  // weights of the previous stage, waiting for its P.V
+  auto pv_prev = [&](int vb) {
+#pragma unroll
+    for (int q = 0; q < NP; ++q) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const uint4 vv = *reinterpret_cast<const uint4*>(&sm.v[vb][q][t][lane][0]);
+#pragma unroll
+        for (int b = 0; b < NB; ++b) acc[b][t] = mfma_k32<T>(vv, pbp[b][q], acc[b][t]);
+      }
+#pragma unroll
+      for (int b = 0; b < NB; ++b) lsum[b] = mfma_k32<T>(ones, pbp[b][q], lsum[b]);
+    }
+  };
+  // Stage from K buffer kb (keys key0 ..), with (kPV) the previous stage's
+  // P.V from V buffer vb beside its softmax.
+  auto stage = [&](auto kPV, int kb, int vb, int key0, bool masked) {
+    f32x4_t sc[NB][kUnits];
+    // Scores, one unit's K fragments at a time (each used by every row tile).
+#pragma unroll
+    for (int u = 0; u < kUnits; ++u) {
+      uint4 kf[NCH];
+#pragma unroll
+      for (int cc = 0; cc < NCH; ++cc) kf[cc] = sm.k[kb][u][cc][lane];
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        sc[b][u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int cc = 0; cc < NCH; ++cc) sc[b][u] = mfma_k32<T>(kf[cc], qb[b][cc], sc[b][u]);
+      }
+    }
+    if constexpr (decltype(kPV)::value) pv_prev(vb);
+    // This stage's reference, mask and weights (the rescale of the
+    // accumulators waits until the previous stage's P.V is in them).
+    float alpha[NB];
+    bool resc[NB];
+    uint4 pbn[NB][NP];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      if (masked && key0 + kKeys - 1 > qmin[b]) {
+        asm volatile("");
+        const int lim = qpos[b] - key0 - 4 * grp;
+#pragma unroll
+        for (int u = 0; u < kUnits; ++u)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) sc[b][u][r] = 16 * u + r <= lim ? sc[b][u][r] : kNegInfP;
+      }
+      float mraw = kNegInfP;
+#pragma unroll
+      for (int u = 0; u < kUnits; ++u)
+        mraw = fmaxf(mraw, fmaxf(fmaxf(sc[b][u][0], sc[b][u][1]), fmaxf(sc[b][u][2], sc[b][u][3])));
+      const float mloc = mraw * sl2;
+      resc[b] = wave_any(mloc > m_ref[b] + kRescaleLog2P);
+      float mx = fmaxf(mloc, __shfl_xor(mloc, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_new = resc[b] ? fmaxf(m_ref[b], mx) : m_ref[b];
+      alpha[b] = (m_new == kNegInfP || m_new == m_ref[b]) ? 1.f : fast_exp2(m_ref[b] - m_new);
+      m_ref[b] = m_new;
+      const float nm = m_new == kNegInfP ? 0.f : -m_new;
+#pragma unroll
+      for (int q = 0; q < NP; ++q) {
+        float e[8];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          e[r] = fast_exp2(fmaf(sc[b][2 * q][r], sl2, nm));
+          e[4 + r] = fast_exp2(fmaf(sc[b][2 * q + 1][r], sl2, nm));
+        }
+        pbn[b][q] = make_uint4(pack2<T>(e[0], e[1]), pack2<T>(e[2], e[3]), pack2<T>(e[4], e[5]), pack2<T>(e[6], e[7]));
+      }
+    }
+#if PA_PREFILL_PIPE_SCHED
+    if constexpr (decltype(kPV)::value) {
+      // The P.V products (and their V reads) interleaved with the VALU work above.
+#pragma unroll
+      for (int k = 0; k < NP * NT; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, NB, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 2 * NB, 0);
+      }
+    }
+#endif
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      if (resc[b]) {
+        lsum[b] *= alpha[b];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) acc[b][t] *= alpha[b];
+      }
+#pragma unroll
+      for (int q = 0; q < NP; ++q) pbp[b][q] = pbn[b][q];
+    }
+  };
+
+  // Pipeline: stage s reads buffer s % 3, stage s - 1's V is in (s - 1) % 3,
+  // stage s + 1 is written to (s + 1) % 3 after this wave's compute of s.
+  const int kfull = active ? qmin[0] - kKeys + 1 : -1;
+  issue(0, stg, valid_st);
+  to_lds(stg, valid_st, 0);
+  __syncthreads();
+  bool pending = false;  // the weights in pbp still wait for their P.V
+  int pend_buf = 0;
+  for (int s = 0, b = 0; s < nst; ++s, b = b == kBuf - 1 ? 0 : b + 1) {
+    if (s + 1 < nst) issue(s + 1, stg, valid_st);
+    const int key0 = s * kKeys;
+    if (key0 <= kmax) {
+      if (pending) stage(std::true_type{}, b, pend_buf, key0, key0 > kfull);
+      else stage(std::false_type{}, b, pend_buf, key0, key0 > kfull);
+      pending = true;
+      pend_buf = b;
+    } else if (pending) {
+      pv_prev(pend_buf);
+      pending = false;
+    }
+    if (s + 1 < nst) to_lds(stg, valid_st, b == kBuf - 1 ? 0 : b + 1);
+    __syncthreads();
+  }
+  if (pending) pv_prev(pend_buf);
+
+  if (!active) return;
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    const int row = r0 + 16 * b + col;
+    if (row < rows) {
+      const float L = lsum[b][0];
+      const float inv = L > 0.f ? 1.f / L : 0.f;
+      const int k = row / G, g = row - (row / G) * G;
+      B* orow = static_cast<B*>(p.out) + ((static_cast<size_t>(qs) + k) * p.Hq + static_cast<size_t>(h) * G + g) * D;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const uint2 w = make_uint2(pack2<T>(acc[b][t][0] * inv, acc[b][t][1] * inv),
+                                   pack2<T>(acc[b][t][2] * inv, acc[b][t][3] * inv));
+        *reinterpret_cast<uint2*>(orow + t * 16 + 4 * grp) = w;
+      }
+    }
+  }
+}
+
 #ifndef PA_PREFILL_LDS_WAVES
 #define PA_PREFILL_LDS_WAVES 8
 #endif
@@ -581,8 +879,13 @@ hipError_t launch_prefill_typed(const PrefillParams& p, hipStream_t stream) {
     const int64_t pairs8 = (static_cast<int64_t>(p.S) * p.H + 7) / 8;
     const int64_t wgs = 8 * pairs8 * tiles;
     if (wgs > INT32_MAX) return hipErrorInvalidValue;
+#if PA_PREFILL_PIPE
+    hipLaunchKernelGGL((prefill_pipe_kernel<T, D, kLdsWaves, kLdsTiles, kLdsPairs>), dim3(static_cast<unsigned>(wgs)),
+                       dim3(64 * kLdsWaves), 0, stream, q, p.tables);
+#else
     hipLaunchKernelGGL((prefill_lds_kernel<T, D, kLdsWaves, kLdsTiles, kLdsPairs>), dim3(static_cast<unsigned>(wgs)),
                        dim3(64 * kLdsWaves), 0, stream, q, p.tables);
+#endif
   } else {
     hipLaunchKernelGGL((prefill_kernel<T, D, kTilesPerWave, kPrefillPrefetch>), grid, dim3(kPrefillThreads), 0,
                        stream, p);
