@@ -264,12 +264,12 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillParams 
 // position and inside the context take no mask, and the row sums come from
 // one more MFMA of P against ones.
 // ---------------------------------------------------------------------------
-template <int D, int NP, int NBUF = 2>
+template <int D, int NP>
 struct PrefillLds {
   static constexpr int NCH = D / 32;
   static constexpr int NT = D / 16;
-  uint4 k[NBUF][2 * NP][NCH][64];  // [buffer][unit][chunk][lane]
-  uint2 v[NBUF][NP][NT][64][2];    // [buffer][pair][head_dim tile][lane][unit of the pair]
+  uint4 k[2][2 * NP][NCH][64];  // [buffer][unit][chunk][lane]
+  uint2 v[2][NP][NT][64][2];    // [buffer][pair][head_dim tile][lane][unit of the pair]
 };
 
 // Zero the 16-bit entries of tokens >= valid in a V chunk: lane group grp
@@ -281,11 +281,146 @@ __device__ __forceinline__ uint4 zero_v_tail(uint4 x, int grp, int valid) {
   return make_uint4(x.x & m01, x.y & m23, x.z & m01, x.w & m23);
 }
 
-#ifndef PA_PREFILL_PIPE
-#define PA_PREFILL_PIPE 0
-#endif
-#ifndef PA_PREFILL_PIPE_SCHED
-#define PA_PREFILL_PIPE_SCHED 0
+// Heaviest-first order of the 16-bit kernel's workgroups.  Its work items
+// are the (sequence, row tile) pairs, each run once per kv head; an item
+// costs about as many stages as its last row has keys / stage.  The hardware
+// hands workgroups to the CUs in grid order as they free up, so a grid in
+// plain order can end with a few long items on few CUs (prompts of very
+// different lengths, or short chunks over very different contexts).  Every
+// workgroup computes the same order in LDS (a counting sort of the items by
+// stage count, heaviest first, ties in item order) and takes its own entry:
+// rank r of that order, kv head h.  Workgroups past the last non-empty item
+// exit at once.
+constexpr int kLptMaxItems = 4096;  // sequences x row tiles; more: plain order
+// With more row tiles per (sequence, kv head) pair than this (long prompts)
+// the plain order is kept: it already runs each pair's tiles heaviest first,
+// back to back on one XCD (sharing its L2), and a grid sized for the longest
+// prompt holds many empty slots that would each pay for the sort.  Fewer
+// tiles per pair (chunks of new tokens over cached contexts) leave the
+// spread of context lengths to decide the finishing time: sorted there.
+constexpr int kLptMaxTiles = 8;
+constexpr int kLptKeys = 1024;      // sort keys: 1023 - min(stages, 1023)
+
+struct LptLds {
+  int start[kLptKeys];         // items per key, then the first rank of each key
+  uint16_t key[kLptMaxItems];  // key of each item
+  int wsum[16];                // per-wave sums
+  int pick;                    // the item chosen for this workgroup
+};
+
+// Stages of item (sequence i, grid row y) in prefill_lds_kernel; 0: no rows.
+template <int kRowsWG, int kKeys>
+__device__ __forceinline__ int item_stages(const PrefillParams& p, int i, int y) {
+  const int qs = clampi(p.query_start[i], 0, p.num_q_tokens);
+  const int qe = clampi(p.query_start[i + 1], qs, p.num_q_tokens);
+  const int c = clampi(p.ctx[i], 0, p.ctx_cap);
+  int n = qe - qs;
+  n = n < p.max_query_len ? n : p.max_query_len;
+  n = n < c ? n : c;
+  const int rows = n * p.G;
+  const int tile = (rows + kRowsWG - 1) / kRowsWG - 1 - y;
+  if (tile < 0) return 0;
+  const int last_row = (tile * kRowsWG + kRowsWG < rows ? tile * kRowsWG + kRowsWG : rows) - 1;
+  return (c - n + last_row / p.G + kKeys) / kKeys;
+}
+
+// This workgroup's (sequence, kv head, grid row) in heaviest-first order;
+// false when it has none.  With H a multiple of 8, consecutive workgroups go
+// to the eight XCDs in turn and XCD x runs kv heads x, x + 8, ... of every
+// item, so all XCDs see the same order and the workgroups of one (sequence,
+// kv head) pair share an L2.  Called by every thread of the workgroup.
+template <int NW, int kRowsWG, int kKeys>
+__device__ bool lpt_item(const PrefillParams& p, LptLds& L, int& i, int& h, int& y) {
+  constexpr int kThreads = 64 * NW;
+  constexpr int kRun = kLptKeys / kThreads;
+  static_assert(kRun * kThreads == kLptKeys && NW <= 16, "key runs");
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int U = p.S * p.tiles;
+  for (int k = tid; k < kLptKeys; k += kThreads) L.start[k] = 0;
+  if (tid == 0) L.pick = -1;
+  __syncthreads();
+  for (int u = tid; u < U; u += kThreads) {
+    const int si = u / p.tiles;
+    const int st = item_stages<kRowsWG, kKeys>(p, si, u - si * p.tiles);
+    const int key = kLptKeys - 1 - (st < kLptKeys - 1 ? st : kLptKeys - 1);
+    L.key[u] = static_cast<uint16_t>(key);
+    atomicAdd(&L.start[key], 1);
+  }
+  __syncthreads();
+  // Exclusive scan of the key counts: thread t owns keys t*kRun .. t*kRun+kRun-1.
+  int run[kRun];
+  int tot = 0;
+#pragma unroll
+  for (int r = 0; r < kRun; ++r) {
+    run[r] = L.start[tid * kRun + r];
+    tot += run[r];
+  }
+  int inc = tot;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int v = __shfl_up(inc, o);
+    if (lane >= o) inc += v;
+  }
+  if (lane == 63) L.wsum[wave] = inc;
+  __syncthreads();
+  int ex = inc - tot;
+  for (int w = 0; w < wave; ++w) ex += L.wsum[w];
+#pragma unroll
+  for (int r = 0; r < kRun; ++r) {
+    L.start[tid * kRun + r] = ex;
+    ex += run[r];
+  }
+  __syncthreads();
+  const int nonempty = L.start[kLptKeys - 1];  // items with stages sort before the empty key
+  int rank, hh;
+  if ((p.H & 7) == 0) {
+    const int hx = p.H >> 3, j = blockIdx.x >> 3;
+    rank = j / hx;
+    hh = (j - rank * hx) * 8 + (blockIdx.x & 7);
+  } else {
+    rank = blockIdx.x / p.H;
+    hh = blockIdx.x - rank * p.H;
+  }
+  if (rank >= nonempty) return false;  // whole workgroup
+  // The key holding this rank: the last key whose first rank is <= rank.
+  int lo = 0, hi = kLptKeys - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (L.start[mid] <= rank) lo = mid;
+    else hi = mid - 1;
+  }
+  const int kb = lo;
+  int want = rank - L.start[kb];
+  // The want-th item with key kb, in item order.
+  for (int c0 = 0; c0 < U; c0 += kThreads) {
+    const int u = c0 + tid;
+    const bool f = u < U && L.key[u] == kb;
+    const uint64_t m = __builtin_amdgcn_ballot_w64(f);
+    const int below = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
+                                                __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0));
+    if (lane == 0) L.wsum[wave] = __popcll(m);
+    __syncthreads();
+    int before = 0, total = 0;
+    for (int w = 0; w < NW; ++w) {
+      const int v = L.wsum[w];
+      total += v;
+      before += w < wave ? v : 0;
+    }
+    if (f && before + below == want) L.pick = u;
+    __syncthreads();
+    if (want < total) break;  // uniform: every thread read the same sums
+    want -= total;
+  }
+  const int u = L.pick;
+  if (u < 0 || u >= U) return false;  // not reached: the counts above place every rank
+  i = u / p.tiles;
+  y = u - i * p.tiles;
+  h = hh;
+  return true;
+}
+
+#ifndef PA_PREFILL_LPT
+#define PA_PREFILL_LPT 1
 #endif
 #ifndef PA_PREFILL_WAVES_PER_EU
 #define PA_PREFILL_WAVES_PER_EU 2
@@ -311,18 +446,28 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(PA_PREF
 
   const int lane = threadIdx.x & 63;
   const int wave = rfl(threadIdx.x >> 6);
-  // Workgroup -> (sequence, kv head, row tile).  Consecutive workgroups go to
-  // the eight XCDs in turn; XCD x runs the (sequence, kv head) pairs
-  // x, x + 8, x + 16, ... one after the other, each pair's row tiles
-  // back to back and the last (heaviest) first, so the workgroups that run at
-  // the same time on an XCD read the same K/V through its L2.
-  const int xcd = blockIdx.x & 7;
-  const int slot = blockIdx.x >> 3;
-  const int pair = (slot / p.tiles) * 8 + xcd;
-  const int y = slot - (slot / p.tiles) * p.tiles;
-  if (pair >= p.S * p.H) return;  // whole workgroup
-  const int i = pair / p.H;
-  const int h = pair - i * p.H;
+  // Workgroup -> (sequence, kv head, row tile).  In plain order consecutive
+  // workgroups go to the eight XCDs in turn; XCD x runs the (sequence, kv
+  // head) pairs x, x + 8, x + 16, ... one after the other, each pair's row
+  // tiles back to back and the last (heaviest) first, so the workgroups that
+  // run at the same time on an XCD read the same K/V through its L2.  The
+  // heaviest-first order (lpt_item) keeps the XCD of each pair.
+  int i, h, y;
+  if (p.lpt) {
+    __shared__ LptLds lpt;
+    if (!lpt_item<NW, kRowsWG, kKeys>(p, lpt, i, h, y)) return;  // whole workgroup
+  } else {
+    const int xcd = blockIdx.x & 7;
+    const int slot = blockIdx.x >> 3;
+    const int pair = (slot / p.tiles) * 8 + xcd;
+    y = slot - (slot / p.tiles) * p.tiles;
+    if (pair >= p.S * p.H) return;  // whole workgroup
+    i = pair / p.H;
+    h = pair - i * p.H;
+  }
+  i = rfl(i);
+  h = rfl(h);
+  y = rfl(y);
   const int G = p.G;
   const int qs = clampi(p.query_start[i], 0, p.num_q_tokens);
   const int qe = clampi(p.query_start[i + 1], qs, p.num_q_tokens);
@@ -572,285 +717,6 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(PA_PREF
   }
 }
 
-// ---------------------------------------------------------------------------
-// 16-bit pools, pipelined across stages: the same workgroup shape, LDS layout
-// and MFMA forms as prefill_lds_kernel, but three LDS buffers, so that a wave
-// computes the scores of stage s while the P.V product of stage s - 1 (its V
-// still in its buffer, its weights in registers) runs beside stage s's
-// softmax.  Each iteration issues stage s's score MFMAs, then stage s - 1's
-// P.V MFMAs interleaved with the VALU work of stage s's reference, mask and
-// exponentials; a raised reference rescales the accumulators only after that
-// P.V has landed (they then hold every stage up to s - 1, all relative to the
-// old reference), so the softmax is unchanged.  Stage s + 1 is written to the
-// third buffer meanwhile; one barrier per stage publishes it.
-// ---------------------------------------------------------------------------
-template <typename T, int D, int NW, int NB, int NP>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(PA_PREFILL_WAVES_PER_EU,
-                                                                         PA_PREFILL_WAVES_PER_EU))) void prefill_pipe_kernel(
-    PrefillParams p, const int32_t* __restrict__ tables) {
-  static_assert(T::kBytes == 2, "16-bit pools only");
-  constexpr int NCH = D / 32;  // 1 KiB chunks per sub-tile
-  constexpr int NT = D / 16;
-  constexpr int kUnits = 2 * NP;         // units per stage
-  constexpr int kKeys = 16 * kUnits;     // keys per stage
-  constexpr int kRowsWave = 16 * NB;
-  constexpr int kRowsWG = kRowsWave * NW;
-  constexpr int kSPW = 2 * kUnits / NW;
-  static_assert(kSPW * NW == 2 * kUnits && (kSPW == 1 || kSPW == 2), "whole sub-tiles per wave");
-  constexpr int kLoads = kSPW * NCH;
-  constexpr int kBuf = 3;
-  using B = typename T::bits;
-  __shared__ PrefillLds<D, NP, kBuf> sm;
-
-  const int lane = threadIdx.x & 63;
-  const int wave = rfl(threadIdx.x >> 6);
-  // Workgroup -> (sequence, kv head, row tile), XCD-aware as in prefill_lds_kernel.
-  const int xcd = blockIdx.x & 7;
-  const int slot = blockIdx.x >> 3;
-  const int pair = (slot / p.tiles) * 8 + xcd;
-  const int y = slot - (slot / p.tiles) * p.tiles;
-  if (pair >= p.S * p.H) return;  // whole workgroup
-  const int i = pair / p.H;
-  const int h = pair - i * p.H;
-  const int G = p.G;
-  const int qs = clampi(p.query_start[i], 0, p.num_q_tokens);
-  const int qe = clampi(p.query_start[i + 1], qs, p.num_q_tokens);
-  const int c = clampi(p.ctx[i], 0, p.ctx_cap);
-  int n = qe - qs;
-  n = n < p.max_query_len ? n : p.max_query_len;
-  n = n < c ? n : c;
-  const int rows = rfl(n * G);
-  const int ntiles = (rows + kRowsWG - 1) / kRowsWG;
-  const int tile = ntiles - 1 - y;
-  if (tile < 0) return;  // whole workgroup
-  const int first_pos = c - n;
-  const int wg_last_row = (tile * kRowsWG + kRowsWG < rows ? tile * kRowsWG + kRowsWG : rows) - 1;
-  const int nst = (first_pos + wg_last_row / G + kKeys) / kKeys;
-  const int r0 = tile * kRowsWG + wave * kRowsWave;
-  const bool active = r0 < rows;
-  const int last_row = (r0 + kRowsWave < rows ? r0 + kRowsWave : rows) - 1;
-  const int kmax = active ? first_pos + last_row / G : -1;
-
-  const int col = lane & 15, grp = lane >> 4;
-  uint4 qb[NB][NCH];
-  f32x4_t acc[NB][NT];
-  f32x4_t lsum[NB];
-  float m_ref[NB];
-  int qpos[NB];
-  int qmin[NB];
-#pragma unroll
-  for (int b = 0; b < NB; ++b) {
-    const int row = r0 + 16 * b + col;
-    const bool valid = row < rows;
-    const int k = row / G, g = row - (row / G) * G;
-    qpos[b] = valid ? first_pos + k : -1;
-    qmin[b] = first_pos + (r0 + 16 * b) / G;
-    const char* qbase = static_cast<const char*>(p.q) +
-                        ((static_cast<size_t>(qs) + (valid ? k : 0)) * p.Hq + static_cast<size_t>(h) * G + g) * D * 2;
-#pragma unroll
-    for (int cc = 0; cc < NCH; ++cc)
-      qb[b][cc] = valid ? *reinterpret_cast<const uint4*>(qbase + (cc * 4 + grp) * 16) : make_uint4(0, 0, 0, 0);
-#pragma unroll
-    for (int t = 0; t < NT; ++t) acc[b][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    lsum[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    m_ref[b] = kNegInfP;
-  }
-
-  const int unit = (wave * kSPW) >> 1;
-  auto sub_is_v = [&](int j) { return kSPW == 2 ? j == 1 : (wave & 1) == 1; };
-  const int32_t* trow = tables + static_cast<size_t>(i) * p.max_blocks;
-  const char* layer_base = static_cast<const char*>(p.pool) + p.layer_off * 2;
-  uint4 stg[kLoads];
-  int valid_st;
-  const int subs = p.bs >> 4;
-  int my_lb = unit / subs, my_sub = unit - (unit / subs) * subs;
-  auto issue = [&](int s, uint4 (&r)[kLoads], int& valid) {
-    const int32_t bid = my_lb < p.max_blocks ? trow[my_lb] : -1;
-    const bool ok = bid >= 0 && bid < p.N;
-    const size_t region = (static_cast<size_t>(ok ? bid : 0) * p.H + h) * (2 * static_cast<size_t>(p.bs) * D);
-    const char* kv = layer_base + (region + static_cast<size_t>(my_sub) * 16 * D) * 2;
-    my_sub += kUnits;
-    while (my_sub >= subs) {
-      my_sub -= subs;
-      ++my_lb;
-    }
-#pragma unroll
-    for (int j = 0; j < kSPW; ++j) {
-      const uint4* sp = reinterpret_cast<const uint4*>(kv + (sub_is_v(j) ? static_cast<size_t>(p.bs) * D * 2 : 0)) +
-                        lane;
-#pragma unroll
-      for (int cc = 0; cc < NCH; ++cc) r[j * NCH + cc] = sp[64 * cc];
-    }
-    const int left = c - s * kKeys - unit * 16;
-    valid = !ok ? 0 : (left < 0 ? 0 : (left < 16 ? left : 16));
-  };
-  auto to_lds = [&](uint4 (&r)[kLoads], int valid, int buf) {
-#pragma unroll
-    for (int j = 0; j < kSPW; ++j) {
-      uint4* rj = r + j * NCH;
-      const bool is_v = sub_is_v(j);
-      if (valid < 16) {
-        if (is_v) {
-#pragma unroll
-          for (int cc = 0; cc < NCH; ++cc) rj[cc] = zero_v_tail(rj[cc], grp, valid);
-        } else {
-#pragma unroll
-          for (int cc = 0; cc < NCH; ++cc)
-            if (col >= valid) rj[cc] = make_uint4(0, 0, 0, 0);
-        }
-      }
-      if (is_v) {
-#pragma unroll
-        for (int cc = 0; cc < NCH; ++cc) {
-          sm.v[buf][unit >> 1][2 * cc][lane][unit & 1] = make_uint2(rj[cc].x, rj[cc].y);
-          sm.v[buf][unit >> 1][2 * cc + 1][lane][unit & 1] = make_uint2(rj[cc].z, rj[cc].w);
-        }
-      } else {
-#pragma unroll
-        for (int cc = 0; cc < NCH; ++cc) sm.k[buf][unit][cc][lane] = rj[cc];
-      }
-    }
-  };
-
-  const float sl2 = p.scale_log2;
-  const uint4 ones = make_uint4(ones2<T>(), ones2<T>(), ones2<T>(), ones2<T>());
-  uint4 pbp[NB][NP];  // weights of the previous stage, waiting for its P.V
-  auto pv_prev = [&](int vb) {
-#pragma unroll
-    for (int q = 0; q < NP; ++q) {
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const uint4 vv = *reinterpret_cast<const uint4*>(&sm.v[vb][q][t][lane][0]);
-#pragma unroll
-        for (int b = 0; b < NB; ++b) acc[b][t] = mfma_k32<T>(vv, pbp[b][q], acc[b][t]);
-      }
-#pragma unroll
-      for (int b = 0; b < NB; ++b) lsum[b] = mfma_k32<T>(ones, pbp[b][q], lsum[b]);
-    }
-  };
-  // Stage from K buffer kb (keys key0 ..), with (kPV) the previous stage's
-  // P.V from V buffer vb beside its softmax.
-  auto stage = [&](auto kPV, int kb, int vb, int key0, bool masked) {
-    f32x4_t sc[NB][kUnits];
-    // Scores, one unit's K fragments at a time (each used by every row tile).
-#pragma unroll
-    for (int u = 0; u < kUnits; ++u) {
-      uint4 kf[NCH];
-#pragma unroll
-      for (int cc = 0; cc < NCH; ++cc) kf[cc] = sm.k[kb][u][cc][lane];
-#pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        sc[b][u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int cc = 0; cc < NCH; ++cc) sc[b][u] = mfma_k32<T>(kf[cc], qb[b][cc], sc[b][u]);
-      }
-    }
-    if constexpr (decltype(kPV)::value) pv_prev(vb);
-    // This stage's reference, mask and weights (the rescale of the
-    // accumulators waits until the previous stage's P.V is in them).
-    float alpha[NB];
-    bool resc[NB];
-    uint4 pbn[NB][NP];
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      if (masked && key0 + kKeys - 1 > qmin[b]) {
-        asm volatile("");
-        const int lim = qpos[b] - key0 - 4 * grp;
-#pragma unroll
-        for (int u = 0; u < kUnits; ++u)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) sc[b][u][r] = 16 * u + r <= lim ? sc[b][u][r] : kNegInfP;
-      }
-      float mraw = kNegInfP;
-#pragma unroll
-      for (int u = 0; u < kUnits; ++u)
-        mraw = fmaxf(mraw, fmaxf(fmaxf(sc[b][u][0], sc[b][u][1]), fmaxf(sc[b][u][2], sc[b][u][3])));
-      const float mloc = mraw * sl2;
-      resc[b] = wave_any(mloc > m_ref[b] + kRescaleLog2P);
-      float mx = fmaxf(mloc, __shfl_xor(mloc, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = resc[b] ? fmaxf(m_ref[b], mx) : m_ref[b];
-      alpha[b] = (m_new == kNegInfP || m_new == m_ref[b]) ? 1.f : fast_exp2(m_ref[b] - m_new);
-      m_ref[b] = m_new;
-      const float nm = m_new == kNegInfP ? 0.f : -m_new;
-#pragma unroll
-      for (int q = 0; q < NP; ++q) {
-        float e[8];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          e[r] = fast_exp2(fmaf(sc[b][2 * q][r], sl2, nm));
-          e[4 + r] = fast_exp2(fmaf(sc[b][2 * q + 1][r], sl2, nm));
-        }
-        pbn[b][q] = make_uint4(pack2<T>(e[0], e[1]), pack2<T>(e[2], e[3]), pack2<T>(e[4], e[5]), pack2<T>(e[6], e[7]));
-      }
-    }
-#if PA_PREFILL_PIPE_SCHED
-    if constexpr (decltype(kPV)::value) {
-      // The P.V products (and their V reads) interleaved with the VALU work above.
-#pragma unroll
-      for (int k = 0; k < NP * NT; ++k) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, NB, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 2 * NB, 0);
-      }
-    }
-#endif
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      if (resc[b]) {
-        lsum[b] *= alpha[b];
-#pragma unroll
-        for (int t = 0; t < NT; ++t) acc[b][t] *= alpha[b];
-      }
-#pragma unroll
-      for (int q = 0; q < NP; ++q) pbp[b][q] = pbn[b][q];
-    }
-  };
-
-  // Pipeline: stage s reads buffer s % 3, stage s - 1's V is in (s - 1) % 3,
-  // stage s + 1 is written to (s + 1) % 3 after this wave's compute of s.
-  const int kfull = active ? qmin[0] - kKeys + 1 : -1;
-  issue(0, stg, valid_st);
-  to_lds(stg, valid_st, 0);
-  __syncthreads();
-  bool pending = false;  // the weights in pbp still wait for their P.V
-  int pend_buf = 0;
-  for (int s = 0, b = 0; s < nst; ++s, b = b == kBuf - 1 ? 0 : b + 1) {
-    if (s + 1 < nst) issue(s + 1, stg, valid_st);
-    const int key0 = s * kKeys;
-    if (key0 <= kmax) {
-      if (pending) stage(std::true_type{}, b, pend_buf, key0, key0 > kfull);
-      else stage(std::false_type{}, b, pend_buf, key0, key0 > kfull);
-      pending = true;
-      pend_buf = b;
-    } else if (pending) {
-      pv_prev(pend_buf);
-      pending = false;
-    }
-    if (s + 1 < nst) to_lds(stg, valid_st, b == kBuf - 1 ? 0 : b + 1);
-    __syncthreads();
-  }
-  if (pending) pv_prev(pend_buf);
-
-  if (!active) return;
-#pragma unroll
-  for (int b = 0; b < NB; ++b) {
-    const int row = r0 + 16 * b + col;
-    if (row < rows) {
-      const float L = lsum[b][0];
-      const float inv = L > 0.f ? 1.f / L : 0.f;
-      const int k = row / G, g = row - (row / G) * G;
-      B* orow = static_cast<B*>(p.out) + ((static_cast<size_t>(qs) + k) * p.Hq + static_cast<size_t>(h) * G + g) * D;
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const uint2 w = make_uint2(pack2<T>(acc[b][t][0] * inv, acc[b][t][1] * inv),
-                                   pack2<T>(acc[b][t][2] * inv, acc[b][t][3] * inv));
-        *reinterpret_cast<uint2*>(orow + t * 16 + 4 * grp) = w;
-      }
-    }
-  }
-}
-
 #ifndef PA_PREFILL_LDS_WAVES
 #define PA_PREFILL_LDS_WAVES 8
 #endif
@@ -876,16 +742,12 @@ hipError_t launch_prefill_typed(const PrefillParams& p, hipStream_t stream) {
     // One dimension: eight XCD lanes of ceil(S * H / 8) pairs x tiles slots.
     PrefillParams q = p;
     q.tiles = static_cast<int32_t>(tiles);
+    q.lpt = PA_PREFILL_LPT && tiles <= kLptMaxTiles && static_cast<int64_t>(p.S) * tiles <= kLptMaxItems;
     const int64_t pairs8 = (static_cast<int64_t>(p.S) * p.H + 7) / 8;
     const int64_t wgs = 8 * pairs8 * tiles;
     if (wgs > INT32_MAX) return hipErrorInvalidValue;
-#if PA_PREFILL_PIPE
-    hipLaunchKernelGGL((prefill_pipe_kernel<T, D, kLdsWaves, kLdsTiles, kLdsPairs>), dim3(static_cast<unsigned>(wgs)),
-                       dim3(64 * kLdsWaves), 0, stream, q, p.tables);
-#else
     hipLaunchKernelGGL((prefill_lds_kernel<T, D, kLdsWaves, kLdsTiles, kLdsPairs>), dim3(static_cast<unsigned>(wgs)),
                        dim3(64 * kLdsWaves), 0, stream, q, p.tables);
-#endif
   } else {
     hipLaunchKernelGGL((prefill_kernel<T, D, kTilesPerWave, kPrefillPrefetch>), grid, dim3(kPrefillThreads), 0,
                        stream, p);

@@ -71,6 +71,7 @@ struct PrefillParams {
   int32_t ctx_cap;             // min(max_context_len, max_blocks * bs)
   float scale_log2;            // scale * log2(e)
   int32_t tiles;               // row tiles per (sequence, kv head) in the grid (set at launch)
+  int32_t lpt;                 // 1: heaviest-first workgroup order (set at launch)
 };
 
 // Workspace of pa_decode: a small header, the work-item list, the sharing

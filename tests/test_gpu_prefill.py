@@ -46,6 +46,12 @@ SMALL = {
     "long_pieces": lambda: CP("plong", 78, "bf16", [1500, 1100], [1500, 37], 8, 2, 128, 16),
     "many_ragged": lambda: CP("pmany", 79, "f16", list(range(3, 400, 23)),
                               [min(c, 1 + (c * 37) % 151) for c in range(3, 400, 23)], 8, 4, 64, 16),
+    # 300 sequences x 15 row tiles: past the heaviest-first sort's limits
+    # (8 row tiles per pair, 4096 items), so the workgroups run in plain grid
+    # order; the other small cases and the chunked batch run sorted.
+    "plain_order": lambda: CP("pplain", 80, "bf16", [900] + [1 + (k * 13) % 40 for k in range(299)],
+                              [900] + [1 + (k * 7) % 9 if 1 + (k * 7) % 9 <= 1 + (k * 13) % 40 else 1
+                                       for k in range(299)], 8, 2, 128, 16),
 }
 
 
