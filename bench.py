@@ -124,7 +124,8 @@ def copy_calibration(pool, w, layers, blocks):
 
 # committed rocprofv3 counter records of the decode workloads
 PROFILE_RECORDS = {"llama3_8b": "decode_llama3_8b_b256", "opt13b": "decode_opt13b_b64",
-                   "long_ctx": "decode_long_ctx_b8", "shared": "decode_shared_b64"}
+                   "long_ctx": "decode_long_ctx_b8", "shared": "decode_shared_b64",
+                   "prefill_llama3_8b": "prefill_llama3_8b", "chunked_llama3_8b": "prefill_chunked_llama3_8b"}
 
 
 def counter_traffic(record: str, workload: str, call: str | None = None):
@@ -312,7 +313,8 @@ def main_prefill(args):
             "peak": peak,
             "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4),
-            "traffic": counter_traffic("prefill_llama3_8b", w.name) if L == 4 else None,
+            "traffic": (counter_traffic(PROFILE_RECORDS[w.name], w.name)
+                        if w.name in PROFILE_RECORDS and L == 4 else None),
             "traffic_unit": "bytes per launch (HBM)",
             "alg_flops_per_launch": flops,
             "kv_bytes_per_launch": w.total_tokens * 2 * w.num_kv_heads * w.head_dim * eb,
@@ -788,9 +790,15 @@ def main():
                            + pos % w.block_size).tolist())
     unique_kv_bytes = len(slots_read) * tok_bytes
     qo_bytes = 2 * w.num_seqs * w.num_q_heads * w.head_dim * eb
-    alg_bytes = kv_bytes + qo_bytes + 4 * nblk + 4 * w.num_seqs
+    # The roofline counts each physical K/V byte once: a block that several
+    # sequences share needs to be read from HBM only once (the logical bytes,
+    # every sequence's whole context, are `value`'s measure and the
+    # alg_bytes_logical field).  Without shared blocks the two are equal.
+    other_bytes = qo_bytes + 4 * nblk + 4 * w.num_seqs
     if fused:  # the new tokens read from their rows and written to their slots, and the slots
-        alg_bytes += 2 * w.num_seqs * tok_bytes + 4 * w.num_seqs
+        other_bytes += 2 * w.num_seqs * tok_bytes + 4 * w.num_seqs
+    alg_bytes = unique_kv_bytes + other_bytes
+    alg_bytes_logical = kv_bytes + other_bytes
     value = kv_bytes / (ms_per_step * 1e-3) / 1e9
     achieved = alg_bytes / (dec_ms * 1e-3) / 1e9
     res = {
@@ -836,6 +844,7 @@ def main():
                         if w.name in PROFILE_RECORDS and P == w.partition_tokens and L == 4
                         and not args.contiguous else None),
             "alg_bytes_per_launch": alg_bytes,
+            "alg_bytes_logical": alg_bytes_logical,
             "avg_launch_ms": round(dec_ms, 5),
             "median_launch_ms": round(float(np.median(call_ms)), 5),
             "warm_median_launch_ms": round(warm_ms, 5),
