@@ -201,6 +201,8 @@ struct MergeSmem {
   float m[kWaves][GMAX];
   float l[kWaves][GMAX];
   float o[kWaves][GMAX][D];
+  float wt[kWaves][GMAX];  // each wave's weight in a column's merged output (2^(m_w - M) / L)
+  float cm[GMAX], cl[GMAX];  // a column's merged maximum and sum
   int slot[4];
 };
 
@@ -227,19 +229,34 @@ __device__ __forceinline__ void finish_partition(const DecodeParams& p, MergeSme
   __syncthreads();
   const int G = p.G;
   const int rows = kShare ? it.cols : G;
-  for (int idx = threadIdx.x; idx < rows * D; idx += kThreads) {
-    const int c = idx / D, d = idx - c * D;
+  // Per column (one thread each): the merged maximum and sum, and each
+  // wave's weight in the merged output; then every (column, head_dim) entry
+  // is one weighted sum of the four waves' entries.
+  if (threadIdx.x < rows) {
+    const int c = threadIdx.x;
     float M = sm.m[0][c];
 #pragma unroll
     for (int w = 1; w < kWaves; ++w) M = fmaxf(M, sm.m[w][c]);
-    float L = 0.f, O = 0.f;
+    float f[kWaves], L = 0.f;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
       const float mw = sm.m[w][c];
-      const float f = (mw == kNegInf) ? 0.f : fast_exp2(mw - M);
-      L += f * sm.l[w][c];
-      O += f * sm.o[w][c][d];
+      f[w] = (mw == kNegInf) ? 0.f : fast_exp2(mw - M);
+      L += f[w] * sm.l[w][c];
     }
+    const float inv = (L > 0.f) ? 1.f / L : 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) sm.wt[w][c] = f[w] * inv;
+    sm.cm[c] = M;
+    sm.cl[c] = L;
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < rows * D; idx += kThreads) {
+    const int c = idx / D, d = idx - c * D;
+    float o = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) o = fmaf(sm.wt[w][c], sm.o[w][c][d], o);
+    const float M = sm.cm[c], L = sm.cl[c];
     int seq = it.i, np = it.np, g = c;
     if constexpr (kShare) {
       const int m = c / G;
@@ -248,7 +265,6 @@ __device__ __forceinline__ void finish_partition(const DecodeParams& p, MergeSme
       np = m == 0 ? mnp.x : m == 1 ? mnp.y : m == 2 ? mnp.z : mnp.w;
     }
     const size_t row = static_cast<size_t>(seq) * p.Hq + it.h * G + g;
-    const float o = (L > 0.f) ? O / L : 0.f;
     if (np == 1) {
       store_out<T>(p, row, d, D, o);
     } else {
