@@ -20,6 +20,7 @@ pa_write_kv) and runs pa_prefill over them; value = causal-attention TFLOP/s.
 from __future__ import annotations
 
 import argparse
+import gc
 import json
 import os
 import sys
@@ -413,23 +414,34 @@ def main_prefix(args):
         return 4 * w.head_dim * w.num_q_heads * tot
 
     # block-manager cost alone (host-only pool, no device work): one
-    # pa_seq_append_tokens per request, without and with the cache
-    hp = pa.Pool(1, N, bs, w.num_kv_heads, w.head_dim, w.dtype, device=None)
+    # pa_seq_append_tokens per request, without and with the cache; the
+    # median of three passes, with Python's cyclic collector paused (a full
+    # collection of the interpreter's heap takes tens of milliseconds)
     ids_all = [w.request_ids(r) for r in reqs]
-    t0 = time.perf_counter()
-    hs = [hp.seq_create() for _ in reqs]
-    for sq, ids in zip(hs, ids_all):
-        hp.seq_append_tokens(sq, ids)
-    host_plain = time.perf_counter() - t0
-    for sq in hs:
-        hp.seq_release(sq)
-    hp.enable_prefix_cache(True)
-    hp.seq_append_tokens(hp.seq_create(), w.prompt_ids)
-    t0 = time.perf_counter()
-    hs = [hp.seq_create() for _ in reqs]
-    for sq, ids in zip(hs, ids_all):
-        hp.seq_append_tokens(sq, ids)
-    host_cached = time.perf_counter() - t0
+    plain_t, cached_t = [], []
+    for _ in range(3):
+        hp = pa.Pool(1, N, bs, w.num_kv_heads, w.head_dim, w.dtype, device=None)
+        gc.disable()
+        try:
+            t0 = time.perf_counter()
+            hs = [hp.seq_create() for _ in reqs]
+            for sq, ids in zip(hs, ids_all):
+                hp.seq_append_tokens(sq, ids)
+            plain_t.append(time.perf_counter() - t0)
+            for sq in hs:
+                hp.seq_release(sq)
+            hp.enable_prefix_cache(True)
+            hp.seq_append_tokens(hp.seq_create(), w.prompt_ids)
+            t0 = time.perf_counter()
+            hs = [hp.seq_create() for _ in reqs]
+            for sq, ids in zip(hs, ids_all):
+                hp.seq_append_tokens(sq, ids)
+            cached_t.append(time.perf_counter() - t0)
+        finally:
+            gc.enable()
+        del hp
+    host_plain = float(np.median(plain_t))
+    host_cached = float(np.median(cached_t))
 
     f_c = flops(cached)
     peak = MFMA_PEAK_TFLOPS[w.dtype]
@@ -460,7 +472,8 @@ def main_prefix(args):
         "speedup_vs_no_cache": round(ms_p / ms_c, 3),
         "host_block_manager_us_per_request": {
             "cached": round(host_cached * 1e6 / R, 2), "no_cache": round(host_plain * 1e6 / R, 2),
-            "note": "pa_seq_create + pa_seq_append_tokens through ctypes, host-only pool"},
+            "note": "pa_seq_create + pa_seq_append_tokens through ctypes, host-only pool; median of 3 passes, "
+                    "Python garbage collection paused"},
         "prefix_cache_stats": pool.prefix_cache_stats(),
         "roofline": {
             "bound": "mfma",
