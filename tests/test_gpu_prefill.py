@@ -46,6 +46,10 @@ SMALL = {
     "long_pieces": lambda: CP("plong", 78, "bf16", [1500, 1100], [1500, 37], 8, 2, 128, 16),
     "many_ragged": lambda: CP("pmany", 79, "f16", list(range(3, 400, 23)),
                               [min(c, 1 + (c * 37) % 151) for c in range(3, 400, 23)], 8, 4, 64, 16),
+    # 8 kv heads (a multiple of 8: XCD x runs kv heads x, x + 8, ... of every
+    # item) and at most 3 row tiles per pair: heaviest-first order, every row
+    # checked.
+    "sorted_h8": lambda: CP("psort8", 81, "bf16", [300, 40, 900, 129, 77], [60, 40, 7, 129, 77], 32, 8, 128, 16),
     # 300 sequences x 15 row tiles: past the heaviest-first sort's limits
     # (8 row tiles per pair, 4096 items), so the workgroups run in plain grid
     # order; the other small cases and the chunked batch run sorted.
