@@ -419,6 +419,62 @@ __device__ bool lpt_item(const PrefillParams& p, LptLds& L, int& i, int& h, int&
   return true;
 }
 
+// Row tiles of sequence i's new tokens (rows = new tokens x G) in the 16-bit
+// kernel's workgroups of kRowsWG rows.
+template <int kRowsWG>
+__device__ __forceinline__ int seq_tiles(const PrefillParams& p, int i) {
+  const int qs = clampi(p.query_start[i], 0, p.num_q_tokens);
+  const int qe = clampi(p.query_start[i + 1], qs, p.num_q_tokens);
+  const int c = clampi(p.ctx[i], 0, p.ctx_cap);
+  int n = qe - qs;
+  n = n < p.max_query_len ? n : p.max_query_len;
+  n = n < c ? n : c;
+  return (n * p.G + kRowsWG - 1) / kRowsWG;
+}
+
+// Plain order over the row tiles that hold rows: consecutive workgroups go
+// to the eight XCDs in turn, and slot s of XCD x is the s-th (pair, tile)
+// among the (sequence, kv head) pairs x, x + 8, x + 16, ..., each pair's
+// tiles heaviest first.  The grid is sized for the longest prompt; its slots
+// past the real tiles come last and exit at once, instead of sitting between
+// the real ones.  Each wave computes the mapping alone (a scan of the XCD's
+// pairs, 64 per step), so no barrier is needed.  False: no tile.
+template <int kRowsWG>
+__device__ bool compact_item(const PrefillParams& p, int& i, int& h, int& y) {
+  const int lane = threadIdx.x & 63;
+  const int xcd = blockIdx.x & 7;
+  const int s = static_cast<int>(blockIdx.x >> 3);
+  const int npairs = p.S * p.H;
+  const int nk = npairs > xcd ? (npairs - xcd + 7) / 8 : 0;  // pairs of this XCD
+  int base = 0;
+  for (int k0 = 0; k0 < nk; k0 += 64) {
+    const int k = k0 + lane;
+    const int nt = k < nk ? seq_tiles<kRowsWG>(p, (xcd + 8 * k) / p.H) : 0;
+    int inc = nt;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int v = __shfl_up(inc, o);
+      if (lane >= o) inc += v;
+    }
+    const int tot = __shfl(inc, 63);
+    if (s < base + tot) {
+      // the first lane whose run ends past s holds it (that lane has tiles)
+      const int L = static_cast<int>(__builtin_ctzll(__builtin_amdgcn_ballot_w64(s < base + inc)));
+      const int first = base + __shfl(inc - nt, L);
+      const int pair = xcd + 8 * (k0 + L);
+      i = pair / p.H;
+      h = pair - i * p.H;
+      y = s - first;
+      return true;
+    }
+    base += tot;
+  }
+  return false;
+}
+
+#ifndef PA_PREFILL_COMPACT
+#define PA_PREFILL_COMPACT 1
+#endif
 #ifndef PA_PREFILL_LPT
 #define PA_PREFILL_LPT 1
 #endif
@@ -457,6 +513,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(PA_PREF
     __shared__ LptLds lpt;
     if (!lpt_item<NW, kRowsWG, kKeys>(p, lpt, i, h, y)) return;  // whole workgroup
   } else {
+#if PA_PREFILL_COMPACT
+    if (!compact_item<kRowsWG>(p, i, h, y)) return;  // whole workgroup (every wave finds the same)
+#else
     const int xcd = blockIdx.x & 7;
     const int slot = blockIdx.x >> 3;
     const int pair = (slot / p.tiles) * 8 + xcd;
@@ -464,6 +523,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(PA_PREF
     if (pair >= p.S * p.H) return;  // whole workgroup
     i = pair / p.H;
     h = pair - i * p.H;
+#endif
   }
   i = rfl(i);
   h = rfl(h);
