@@ -46,6 +46,8 @@ SMALL = {
     "long_pieces": lambda: CP("plong", 78, "bf16", [1500, 1100], [1500, 37], 8, 2, 128, 16),
     "many_ragged": lambda: CP("pmany", 79, "f16", list(range(3, 400, 23)),
                               [min(c, 1 + (c * 37) % 151) for c in range(3, 400, 23)], 8, 4, 64, 16),
+    # the largest block size (16 sub-tiles per block)
+    "g4_bf16_bs256": lambda: CP("pbs256", 82, "bf16", [300, 700, 40], [300, 64, 40], 8, 2, 128, 256),
     # 8 kv heads (a multiple of 8: XCD x runs kv heads x, x + 8, ... of every
     # item) and at most 3 row tiles per pair: heaviest-first order, every row
     # checked.
