@@ -328,3 +328,43 @@ def test_comparison_bound_limits_sharing():
     exp = expected_subgroups(tables, ctx, bs, N, Hq // Hkv)
     U.log(f"  shared subgroups: plan {nsub}, rule {exp} (of {S // 4} without the bound)")
     assert nsub == exp and 0 < exp < S // 4
+
+
+def test_batch_beyond_the_plan_limit_decodes_without_sharing():
+    """1,100 forked branches of one 300-token prefix: more sequences than the
+    sharing plan examines (1,024), so the decode takes the plain plan over the
+    shared tables; every output still matches the oracle."""
+    import paged_kv_cache_337_amd as pa
+    dtype, Hq, Hkv, D, bs = "f16", 16, 4, 64, 16
+    rng = np.random.default_rng(1100)
+    S, prefix = 1100, 300
+    N = -(-prefix // bs) + 3 * S
+    pool = pa.Pool(1, N, bs, Hkv, D, dtype, free_order=rng.permutation(N).astype(np.int32))
+    U.poison(pool)
+    s0 = pool.seq_create()
+    slots, _ = pool.seq_append(s0, prefix)
+    pk, pv = _kv(rng, prefix, Hkv, D, dtype)
+    pool.write_kv(0, U.dev_tensor(pk, dtype), U.dev_tensor(pv, dtype), torch.from_numpy(slots).cuda())
+    seqs = [s0] + [pool.seq_fork(s0) for _ in range(S - 1)]
+    tails = [int(x) for x in rng.integers(1, 20, S)]
+    parts = []
+    for s, n in zip(seqs, tails):
+        sl, cow = pool.seq_append(s, n)
+        if len(cow):
+            pool.copy_blocks(torch.from_numpy(np.asarray(cow, dtype=np.int32).reshape(-1, 2)).cuda())
+        parts.append(sl)
+    all_slots = np.concatenate(parts)
+    tk, tv = _kv(rng, int(sum(tails)), Hkv, D, dtype)
+    pool.write_kv(0, U.dev_tensor(tk, dtype), U.dev_tensor(tv, dtype), torch.from_numpy(all_slots).cuda())
+    torch.cuda.synchronize()
+    width = max(len(pool.seq_block_table(s)[0]) for s in seqs)
+    tables, ctx = pool.batch_tables(seqs, width)
+    q = W.round_to_storage(rng.standard_normal((S, Hq, D), dtype=np.float32), dtype)
+    scale = float(np.float32(1.0 / np.sqrt(D)))
+    out, _ = decode_with_header(pool, U.dev_tensor(q, dtype), torch.from_numpy(tables).cuda(),
+                                torch.from_numpy(ctx).cuda(), int(ctx.max()), scale)
+    offs = np.concatenate([[0], np.cumsum(tails)])
+    ref = np.stack([A.decode_one(_f64(q[i], dtype), _f64(np.concatenate([pk, tk[offs[i]:offs[i + 1]]]), dtype),
+                                 _f64(np.concatenate([pv, tv[offs[i]:offs[i + 1]]]), dtype), scale)
+                    for i in range(S)])
+    U.check_close(U.out_f64(out), ref, dtype, "1100 branches, plain plan")
