@@ -50,6 +50,9 @@ def parse():
     ap.add_argument("--separate-calls", action="store_true",
                     help="decode workloads: a step is pa_write_kv then pa_decode (two calls) instead of "
                          "pa_decode_step (one call, the write beside the plan)")
+    ap.add_argument("--share-plan", choices=["host", "device"], default="host",
+                    help="shared-prefix workloads: the sharing groups come from the block manager on the "
+                         "host (pa_batch_share_plan, pa_decode_step_shared) or are found by the device plan")
     ap.add_argument("--layers", type=int, default=4)
     ap.add_argument("--partition-tokens", type=int, default=-1,
                     help="-1: the workload's own setting (0 = library default)")
@@ -711,6 +714,19 @@ def main():
     max_ctx = w.max_context_len
 
     fused = not args.separate_calls
+    # Sharing groups from the block manager: made on the host beside the
+    # tables (median of 5 host timings) and resident on the device like them.
+    share_plan, host_plan_us = None, None
+    if shared and args.share_plan == "host" and fused:
+        rows = list(range(w.num_seqs))
+        host_us = []
+        for _ in range(5):
+            t1 = time.perf_counter()
+            plan_np = pool.batch_share_plan(rows, w.num_q_heads)
+            host_us.append((time.perf_counter() - t1) * 1e6)
+        host_plan_us = round(float(np.median(host_us)), 1)
+        share_plan = torch.from_numpy(plan_np).cuda()
+        log(f"[bench] host sharing plan: {int(plan_np[0])} subgroups in {host_plan_us} us")
 
     def step(k, ev=None):
         layer = k % L
@@ -718,7 +734,7 @@ def main():
             if ev is not None:
                 ev[0].record(stream)
             pool.decode_step(layer, k_new, v_new, slot_new, q, tables, ctx, max_ctx, w.scale, P, out=out,
-                             workspace=ws)
+                             workspace=ws, share_plan=share_plan)
             if ev is not None:
                 ev[1].record(stream)
             return
@@ -836,7 +852,10 @@ def main():
             "partition_tokens": P if P else "automatic (at least 512, chosen on the device)",
             "layer_slots_rotated": L,
             "step": ("pa_decode_step (1 new token/seq written, then decode, one call)" if fused
-                     else "pa_write_kv (1 new token/seq) + pa_decode"),
+                     else "pa_write_kv (1 new token/seq) + pa_decode")
+                    if share_plan is None else
+                    "pa_decode_step_shared (1 new token/seq written, then decode, one call; sharing groups "
+                    "from the block manager)",
         },
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "kv_bytes_logical": kv_bytes,
@@ -846,14 +865,17 @@ def main():
         "event_ms_per_step": round(ev_ms, 5),
         "roofline": {
             "bound": "hbm",
-            "kernel": ("pa_decode_step call (prologue: the write beside the plan; decode kernel; merge kernel)"
+            "kernel": ("pa_decode_step_shared call (prologue: the write beside the plan, which takes the "
+                       "sharing groups from the host; decode kernel; merge kernel)" if share_plan is not None
+                       else "pa_decode_step call (prologue: the write beside the plan; decode kernel; merge kernel)"
                        if fused else "pa_decode call (plan_kernel + decode kernel + merge_kernel)"),
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": (counter_traffic(PROFILE_RECORDS[w.name], w.name,
-                                        "pa_decode_step" if fused else "pa_decode")
+                                        "pa_decode_step_shared" if share_plan is not None
+                                        else "pa_decode_step" if fused else "pa_decode")
                         if w.name in PROFILE_RECORDS and P == w.partition_tokens and L == 4
                         and not args.contiguous else None),
             "alg_bytes_per_launch": alg_bytes,
@@ -866,6 +888,8 @@ def main():
             "frac_of_probe": round(achieved / probe_gbs, 4),
         },
     }
+    if host_plan_us is not None:
+        res["host_share_plan_us"] = host_plan_us
     if table_free is not None:
         table_free["achieved"] = round(alg_bytes / (table_free["avg_launch_ms"] * 1e-3) / 1e9, 2)
         table_free["kv_gbs_per_step"] = round(kv_bytes / (table_free["ms_per_step"] * 1e-3) / 1e9, 2)

@@ -193,6 +193,47 @@ int pa_decode_step(pa_pool* pool, int layer, const void* k, const void* v, const
                    int max_blocks_per_seq, const int32_t* context_lens, int max_context_len, float scale,
                    int partition_tokens, void* workspace, size_t ws_bytes, void* out, void* stream);
 
+/* Host words of a batch's sharing plan: pa_share_plan_words(n) int32. */
+size_t pa_share_plan_words(int num_seqs);
+
+/* The sharing groups of a batch, from the block manager's own tables ("Support
+ * for Prefix Sharing": forked sequences hold the same blocks; "KV-Cache Block
+ * Manager": the manager keeps every sequence's mapping), by the rule
+ * pa_decode applies on the device: sequences whose first full block is the
+ * same block form a group led by its lowest batch index; each member shares
+ * the leading full blocks whose ids equal the leader's; members are taken in
+ * batch order in subgroups of min(4, 16 / G) (a lone remainder stays alone),
+ * and a subgroup shares the shortest of its members' common prefixes when
+ * that is at least 256 tokens.
+ *   seqs        host [num_seqs] sequence ids, in the batch order of the tables
+ *   num_q_heads query heads (G = num_q_heads / num_kv_heads)
+ *   plan_out    host int32 [pa_share_plan_words(num_seqs)]:
+ *                 [0]                number of subgroups K
+ *                 [1 + i]            subgroup of batch row i, -1 for none
+ *                 [1 + S + i]        tokens row i shares with its subgroup
+ *                 [1 + 2S + 4k + m]  member m of subgroup k (batch rows, -1 padded)
+ * Host only, synchronous.  Errors: INVALID_ARG (unknown, released or
+ * swapped-out sequence, num_q_heads not a multiple of num_kv_heads). */
+int pa_batch_share_plan(const pa_pool* pool, const int* seqs, int num_seqs, int num_q_heads,
+                        int32_t* plan_out);
+
+/* pa_decode_step with the sharing plan of the batch computed on the host by
+ * pa_batch_share_plan (for the same sequences in the same order) instead of
+ * on the device: the device then skips the grouping and the id-by-id check
+ * and only builds the work list.  share_plan: device copy of those words
+ * (NULL: exactly pa_decode_step).  The plan is trusted as the tables are:
+ * a plan from another batch gives wrong attention, though every access stays
+ * within the pool, q and out (subgroup ids, members and shared lengths are
+ * clamped on the device).  The plan is used where pa_decode_step would use
+ * its own (automatic partition size, several partitions possible,
+ * num_seqs <= 1024, G <= 8); otherwise the call is pa_decode_step's.  The
+ * rest as for pa_decode_step. */
+int pa_decode_step_shared(pa_pool* pool, int layer, const void* k, const void* v, const int32_t* slot_mapping,
+                          int num_tokens, const void* q, int num_seqs, int num_q_heads,
+                          const int32_t* block_tables, int max_blocks_per_seq, const int32_t* context_lens,
+                          int max_context_len, float scale, int partition_tokens, void* workspace,
+                          size_t ws_bytes, void* out, void* stream, const int32_t* share_plan);
+
 /* Comparison point, no part of the paged method: pa_decode over sequences
  * whose blocks are consecutive, with no block table at all -- sequence i's
  * position p lies in physical block first_block[i] + p / bs, slot p % bs, as

@@ -31,7 +31,8 @@ ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2}
 # Every symbol include/pa.h declares, in declaration order.
 EXPORTS = [
     "pa_version", "pa_last_error", "pa_pool_required_bytes", "pa_alloc_pool", "pa_free",
-    "pa_write_kv", "pa_decode_workspace_bytes", "pa_decode", "pa_decode_step", "pa_decode_contiguous",
+    "pa_write_kv", "pa_decode_workspace_bytes", "pa_decode", "pa_decode_step", "pa_share_plan_words",
+    "pa_batch_share_plan", "pa_decode_step_shared", "pa_decode_contiguous",
     "pa_decode_noalloc",
     "pa_decode_noalloc_scratch_bytes", "pa_prefill", "pa_copy_blocks",
     "pa_seq_create", "pa_seq_append", "pa_prefix_cache_enable", "pa_seq_append_tokens",
@@ -84,6 +85,10 @@ def _load():
                               c_int, vp, c_sz, vp, vp]),
         "pa_decode_step": (c_int, [vp, c_int, vp, vp, vp, c_int, vp, c_int, c_int, vp, c_int, vp, c_int,
                                    ctypes.c_float, c_int, vp, c_sz, vp, vp]),
+        "pa_share_plan_words": (c_sz, [c_int]),
+        "pa_batch_share_plan": (c_int, [vp, intp, c_int, c_int, i32p]),
+        "pa_decode_step_shared": (c_int, [vp, c_int, vp, vp, vp, c_int, vp, c_int, c_int, vp, c_int, vp, c_int,
+                                          ctypes.c_float, c_int, vp, c_sz, vp, vp, vp]),
         "pa_decode_contiguous": (c_int, [vp, c_int, vp, c_int, c_int, vp, vp, c_int, ctypes.c_float, c_int,
                                          vp, c_sz, vp, vp]),
         "pa_decode_noalloc": (c_int, [vp, c_int, vp, c_int, c_int, vp, c_int, vp, c_int, ctypes.c_float,
@@ -288,8 +293,11 @@ class Pool:
                     q: torch.Tensor, block_tables: torch.Tensor, context_lens: torch.Tensor,
                     max_context_len: int, scale: float, partition_tokens: int = 0,
                     out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
-                    stream=None) -> torch.Tensor:
-        """write_kv(k, v, slot_mapping) then decode(...), in one call (pa_decode_step)."""
+                    stream=None, share_plan: torch.Tensor | None = None) -> torch.Tensor:
+        """write_kv(k, v, slot_mapping) then decode(...), in one call (pa_decode_step).
+
+        share_plan: device copy of batch_share_plan(...) for these rows
+        (pa_decode_step_shared); None lets the device find the groups."""
         fn, dt = "pa_decode_step", TORCH_DTYPE[self.dtype]
         _need(slot_mapping, fn, "slot_mapping", torch.int32, 1)
         n = int(slot_mapping.shape[0])
@@ -303,9 +311,11 @@ class Pool:
             _need(out, fn, "out", dt, 3, self.D, Hq, S)
         if workspace is not None:
             _need(workspace, fn, "workspace")
+        if share_plan is not None:
+            _need(share_plan, fn, "share_plan", torch.int32, 1, min_rows=int(lib.pa_share_plan_words(S)))
         _on_device(fn, ("k", k), ("v", v), ("slot_mapping", slot_mapping), ("q", q),
                    ("block_tables", block_tables), ("context_lens", context_lens), ("out", out),
-                   ("workspace", workspace))
+                   ("workspace", workspace), ("share_plan", share_plan))
         self._need_device()
         if out is None:
             out = torch.empty_like(q)
@@ -314,11 +324,14 @@ class Pool:
             workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
             if stream is not None:
                 workspace.record_stream(stream)
-        _check(lib.pa_decode_step(self.handle, layer, _ptr(k), _ptr(v), _ptr(slot_mapping), n, _ptr(q), S, Hq,
-                                  _ptr(block_tables), int(block_tables.shape[1]), _ptr(context_lens),
-                                  int(max_context_len), float(scale), int(partition_tokens), _ptr(workspace),
-                                  workspace.numel() * workspace.element_size(), _ptr(out), _stream(stream)),
-               "pa_decode_step")
+        args = (self.handle, layer, _ptr(k), _ptr(v), _ptr(slot_mapping), n, _ptr(q), S, Hq, _ptr(block_tables),
+                int(block_tables.shape[1]), _ptr(context_lens), int(max_context_len), float(scale),
+                int(partition_tokens), _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(out),
+                _stream(stream))
+        if share_plan is None:
+            _check(lib.pa_decode_step(*args), "pa_decode_step")
+        else:
+            _check(lib.pa_decode_step_shared(*args, _ptr(share_plan)), "pa_decode_step_shared")
         return out
 
     def decode_contiguous(self, layer: int, q: torch.Tensor, first_block: torch.Tensor,
@@ -490,6 +503,15 @@ class Pool:
         _check(lib.pa_batch_tables(self.handle, s.ctypes.data_as(ctypes.POINTER(ctypes.c_int)), len(s),
                                    max_blocks, _i32(tables), _i32(ctx)), "pa_batch_tables")
         return tables, ctx
+
+    def batch_share_plan(self, seqs, num_q_heads: int) -> np.ndarray:
+        """The batch's sharing groups from the block manager's tables
+        (pa_batch_share_plan): int32 words, see include/pa.h."""
+        s = np.ascontiguousarray(seqs, dtype=np.int32)
+        plan = np.empty(int(lib.pa_share_plan_words(len(s))), dtype=np.int32)
+        _check(lib.pa_batch_share_plan(self.handle, s.ctypes.data_as(ctypes.POINTER(ctypes.c_int)), len(s),
+                                       int(num_q_heads), _i32(plan)), "pa_batch_share_plan")
+        return plan
 
     def state(self):
         rc = np.empty(max(self.N, 1), dtype=np.int32)

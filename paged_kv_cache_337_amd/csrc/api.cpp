@@ -9,6 +9,7 @@
 #include <exception>
 #include <new>
 #include <string>
+#include <unordered_map>
 #include <vector>
 
 #include "allocator.hpp"
@@ -222,7 +223,8 @@ int pa::set_error(int code, const std::string& msg) { return fail(code, msg); }
 int pa::decode_call(const pa_pool* pool, int layer, const void* q, int num_seqs, int num_q_heads,
                     const int32_t* block_tables, int max_blocks_per_seq, const int32_t* context_lens,
                     int max_context_len, float scale, int partition_tokens, void* workspace, size_t ws_bytes,
-                    void* out, void* stream, bool noalloc, bool flat, const NewTokens* write) {
+                    void* out, void* stream, bool noalloc, bool flat, const NewTokens* write,
+                    const int32_t* share_plan) {
   return guarded([&]() -> int {
     if (flat) max_blocks_per_seq = 1;
     if (write && write->num_tokens < 0) return fail(PA_ERR_INVALID_ARG, "token count cannot be negative");
@@ -329,6 +331,7 @@ int pa::decode_call(const pa_pool* pool, int layer, const void* q, int num_seqs,
     // otherwise it keeps the plain plan.  The plan itself verifies every
     // shared block id, so tables from any source stay correct either way.
     p.share = !flat && pool->alloc.shared_blocks() > 0 ? 1 : 0;
+    p.host_plan = p.share ? share_plan : nullptr;
     p.flat = flat ? 1 : 0;
     if (write && write->num_tokens > 0) {
       p.w_k = write->k;
@@ -353,6 +356,100 @@ int pa_decode_step(pa_pool* pool, int layer, const void* k, const void* v, const
   return pa::decode_call(pool, layer, q, num_seqs, num_q_heads, block_tables, max_blocks_per_seq, context_lens,
                          max_context_len, scale, partition_tokens, workspace, ws_bytes, out, stream, false, false,
                          &w);
+}
+
+int pa_decode_step_shared(pa_pool* pool, int layer, const void* k, const void* v, const int32_t* slot_mapping,
+                          int num_tokens, const void* q, int num_seqs, int num_q_heads,
+                          const int32_t* block_tables, int max_blocks_per_seq, const int32_t* context_lens,
+                          int max_context_len, float scale, int partition_tokens, void* workspace,
+                          size_t ws_bytes, void* out, void* stream, const int32_t* share_plan) {
+  const pa::NewTokens w{k, v, slot_mapping, num_tokens};
+  if (num_seqs == 0 && num_tokens > 0)
+    return pa_write_kv(pool, layer, k, v, slot_mapping, num_tokens, stream);
+  return pa::decode_call(pool, layer, q, num_seqs, num_q_heads, block_tables, max_blocks_per_seq, context_lens,
+                         max_context_len, scale, partition_tokens, workspace, ws_bytes, out, stream, false, false,
+                         &w, share_plan);
+}
+
+size_t pa_share_plan_words(int num_seqs) {
+  if (num_seqs < 0) return 0;
+  return 1 + 2 * static_cast<size_t>(num_seqs) + 4 * (static_cast<size_t>(num_seqs) / 2 + 1);
+}
+
+int pa_batch_share_plan(const pa_pool* pool, const int* seqs, int num_seqs, int num_q_heads, int32_t* plan_out) {
+  return guarded([&]() -> int {
+    if (!pool || !plan_out || (num_seqs > 0 && !seqs)) return fail(PA_ERR_INVALID_ARG, "NULL argument");
+    if (num_seqs < 0) return fail(PA_ERR_INVALID_ARG, "num_seqs cannot be negative");
+    const pa_pool_desc& d = pool->desc;
+    if (num_q_heads <= 0 || num_q_heads % d.num_kv_heads)
+      return fail(PA_ERR_INVALID_ARG, "num_q_heads must be a positive multiple of num_kv_heads");
+    for (int i = 0; i < num_seqs; ++i) {
+      if (!pool->alloc.live(seqs[i])) return fail(PA_ERR_INVALID_ARG, "unknown or released sequence");
+      if (pool->alloc.swapped(seqs[i])) return fail(PA_ERR_INVALID_ARG, "sequence is swapped out");
+    }
+    const int S = num_seqs, bs = d.block_size, G = num_q_heads / d.num_kv_heads;
+    const int nmax = std::min(4, 16 / G);
+    int32_t* sub = plan_out + 1;
+    int32_t* shared = plan_out + 1 + S;
+    int32_t* members = plan_out + 1 + 2 * static_cast<size_t>(S);
+    std::fill(plan_out, plan_out + pa_share_plan_words(S), 0);
+    std::fill(sub, sub + S, -1);
+    std::fill(members, members + 4 * (static_cast<size_t>(S) / 2 + 1), -1);
+    // groups: rows whose first full block is the same block, in batch order
+    std::vector<int> nfb(S);
+    std::unordered_map<int32_t, std::vector<int>> group_of;
+    std::vector<int32_t> firsts;
+    for (int i = 0; i < S; ++i) {
+      const auto& t = pool->alloc.table(seqs[i]);
+      nfb[i] = pool->alloc.length(seqs[i]) / bs;
+      if (nfb[i] > 0 && !t.empty() && t[0] >= 0 && t[0] < d.num_blocks) {
+        auto it = group_of.find(t[0]);
+        if (it == group_of.end()) {
+          firsts.push_back(t[0]);
+          group_of.emplace(t[0], std::vector<int>{i});
+        } else {
+          it->second.push_back(i);
+        }
+      }
+    }
+    // groups in the order of their leaders (lowest rows), as on the device
+    std::sort(firsts.begin(), firsts.end(),
+              [&](int32_t a, int32_t b) { return group_of[a][0] < group_of[b][0]; });
+    int K = 0;
+    if (nmax >= 2) {
+      for (int32_t f : firsts) {
+        const std::vector<int>& mem = group_of[f];
+        const int gn = static_cast<int>(mem.size());
+        if (gn < 2) continue;
+        const auto& lead = pool->alloc.table(seqs[mem[0]]);
+        const int gsub = gn / nmax + (gn % nmax >= 2 ? 1 : 0);
+        for (int sg = 0; sg < gsub; ++sg) {
+          int common = INT32_MAX;
+          const int r0 = sg * nmax, r1 = std::min(r0 + nmax, gn);
+          for (int r = r0; r < r1; ++r) {
+            const int i = mem[r];
+            int c = nfb[i];
+            if (r > 0) {
+              const auto& t = pool->alloc.table(seqs[i]);
+              const int cap = std::min(nfb[i], nfb[mem[0]]);
+              c = 0;
+              while (c < cap && t[c] == lead[c]) ++c;
+            }
+            common = std::min(common, c);
+          }
+          if (static_cast<int64_t>(common) * bs < 256) continue;
+          for (int r = r0; r < r1; ++r) {
+            sub[mem[r]] = K;
+            shared[mem[r]] = common * bs;
+            members[4 * static_cast<size_t>(K) + (r - r0)] = mem[r];
+          }
+          ++K;
+        }
+      }
+    }
+    plan_out[0] = K;
+    return PA_OK;
+  });
 }
 
 int pa_decode_contiguous(const pa_pool* pool, int layer, const void* q, int num_seqs, int num_q_heads,

@@ -27,9 +27,12 @@ struct NewTokens {
   int num_tokens;
 };
 
+// `share_plan`: device copy of pa_batch_share_plan's words for this batch
+// (NULL: the device finds the sharing groups itself).
 int decode_call(const pa_pool* pool, int layer, const void* q, int num_seqs, int num_q_heads,
                 const int32_t* block_tables, int max_blocks_per_seq, const int32_t* context_lens,
                 int max_context_len, float scale, int partition_tokens, void* workspace, size_t ws_bytes,
-                void* out, void* stream, bool noalloc, bool flat = false, const NewTokens* write = nullptr);
+                void* out, void* stream, bool noalloc, bool flat = false, const NewTokens* write = nullptr,
+                const int32_t* share_plan = nullptr);
 
 }  // namespace pa

@@ -494,122 +494,152 @@ __device__ __forceinline__ void plan_share(const DecodeParams& p) {
   const int c = live ? clamp_ctx(p, t) : 0;
   const int nfb = c / bs;  // full blocks
   const bool keyed = nfb > 0 && b0 >= 0 && b0 < p.N;
-  for (int k = t; k < kShareHash; k += kPlanThreads) {
-    hk[k] = -1;
-    hv[k] = 0x7fffffff;
-  }
-  gcount[t] = 0;
-  cpre[t] = nfb;
-  __syncthreads();
-
-  // 1. Groups: sequences whose first block is the same physical block.
-  int slot = 0;
-  if (keyed) {
-    uint32_t hh = (static_cast<uint32_t>(b0) * 2654435761u) >> (32 - kShareHashBits);
-    for (;;) {  // ends: at most kShareMaxSeqs keys in kShareHash slots
-      const int old = atomicCAS(&hk[hh], -1, b0);
-      if (old == -1 || old == b0) break;
-      hh = (hh + 1) & (kShareHash - 1);
+  int sid = -1, Ls = 0;  // subgroup, shared tokens
+  bool head = false;     // first member of an active subgroup
+  if (p.host_plan) {
+    // Steps 1-4 done on the host from the block manager's tables: row t's
+    // subgroup and shared tokens, each subgroup's members.  Every value is
+    // clamped into range, so a plan that does not fit the batch gives wrong
+    // attention but no access outside the buffers.
+    const int32_t* hp = p.host_plan;
+    const int nsub = p.S / 2;  // at most one subgroup per two rows
+    for (int k = t; k < nsub; k += kPlanThreads) sls[k] = 0x7fffffff;
+    __syncthreads();
+    if (live) {
+      const int s = hp[1 + t];
+      sid = (s >= 0 && s < nsub) ? s : -1;
+      if (sid >= 0) {
+        const int lt = hp[1 + p.S + t];
+        atomicMin(&sls[sid], lt > 0 ? min(lt / bs, nfb) : 0);
+      }
     }
-    slot = static_cast<int>(hh);
-    atomicMin(&hv[slot], t);
-  }
-  __syncthreads();
-  const int L = keyed ? hv[slot] : t;
-  lead[t] = L;
-  if (L != t) atomicAdd(&gcount[L], 1);
-  __syncthreads();
-
-  // 2. Rank in the group by sequence index; subgroups of nmax consecutive
-  //    ranks (a lone last member stays on its own).
-  int rank = 0;
-  if (L != t) {
-    rank = 1;
-    for (int j = L + 1; j < t; ++j) rank += lead[j] == L ? 1 : 0;
-  }
-  const int gn = live ? gcount[L] + 1 : 0;
-  const int gsub = gn >= 2 ? gn / nmax + (gn % nmax >= 2 ? 1 : 0) : 0;
-  // one scan for both: subgroups per leader (low 16 bits), members (high)
-  const bool member = live && L != t;
-  int both = 0;
-  const int sc = block_scan((L == t ? gsub : 0) | (member ? 1 << 16 : 0), wsum, both);
-  const int nsub_total = both & 0xffff, nmem = both >> 16;
-  sbase[t] = sc & 0xffff;
-  if (member) mlist[sc >> 16] = t;
-  for (int k = t; k < nsub_total; k += kPlanThreads) {
-    sls[k] = 0x7fffffff;
+    __syncthreads();
+    if (sid >= 0 && sls[sid] * bs >= kMinSharedTokens) {
+      Ls = sls[sid] * bs;
+      const int32_t* mem = hp + 1 + 2 * static_cast<size_t>(p.S) + 4 * static_cast<size_t>(sid);
+      head = mem[0] == t;
+      if (head) {
+        smem[sid][0] = t;
 #pragma unroll
-    for (int m = 0; m < kShareMaxMembers; ++m) smem[k][m] = -1;
-  }
-  __syncthreads();
-  const int sub = rank / nmax;
-  const int sid = (live && sub < gsub) ? sbase[L] + sub : -1;
-  if (sid >= 0) smem[sid][rank - sub * nmax] = t;
-
-  // 3. Each non-leader's table against its leader's, over the full blocks
-  //    both hold: tasks of 64 entries (one per lane), each task's member
-  //    found in an owner array (the hash arrays are free now), the loads of
-  //    kCmpBatch tasks per wave issued together.  At most kMaxCmpTasks tasks
-  //    are checked; a member whose tasks lie beyond shares only what was
-  //    checked.
-  int ntk = 0, cap = 0;
-  if (t < nmem) {
-    const int m = mlist[t];
-    cap = min(cpre[m], cpre[lead[m]]);
-    ntk = (cap + 63) / 64;
-  }
-  int ntask = 0;
-  const int tb = block_scan(ntk, wsum, ntask);
-  int* towner = hk;
-  if (t < nmem) {
-    const int e = min(tb + ntk, kMaxCmpTasks);
-    for (int k = tb; k < e; ++k) towner[k] = t;
-    cap = min(cap, max(e - tb, 0) * 64);
-    mcap[t] = cap;
-    tbase[t] = tb;
-    cpre[mlist[t]] = cap;
-  }
-  __syncthreads();
-  ntask = min(ntask, kMaxCmpTasks);
-  constexpr int kWavesPlan = kPlanThreads / 64;
-  for (int base = wave; base < ntask; base += kWavesPlan * kCmpBatch) {
-    // Lane r < kCmpBatch looks up task base + r * kWavesPlan (three LDS round
-    // trips for the whole batch); the values are then broadcast by readlane.
-    const int mtk = base + (lane % kCmpBatch) * kWavesPlan;
-    const int own = towner[mtk < ntask ? mtk : 0];
-    const int mm = mlist[own];
-    const int ml = lead[mm];
-    const int mcp = mtk < ntask ? mcap[own] : 0;
-    const int mk0 = (mtk - tbase[own]) * 64;
-    int tm[kCmpBatch], tk0[kCmpBatch], tcap[kCmpBatch], va[kCmpBatch], vb[kCmpBatch];
-#pragma unroll
-    for (int r = 0; r < kCmpBatch; ++r) {
-      tm[r] = __builtin_amdgcn_readlane(mm, r);
-      tk0[r] = __builtin_amdgcn_readlane(mk0, r);
-      tcap[r] = __builtin_amdgcn_readlane(mcp, r);
-      const int tl = __builtin_amdgcn_readlane(ml, r);
-      const int k = tk0[r] + lane;
-      const int kk = k < tcap[r] ? k : 0;  // tcap <= both rows' full blocks <= max_blocks
-      va[r] = p.tables[static_cast<size_t>(tm[r]) * p.max_blocks + kk];
-      vb[r] = p.tables[static_cast<size_t>(tl) * p.max_blocks + kk];
+        for (int m = 1; m < kShareMaxMembers; ++m) smem[sid][m] = (mem[m] >= 0 && mem[m] < p.S) ? mem[m] : -1;
+      }
     }
-#pragma unroll
-    for (int r = 0; r < kCmpBatch; ++r) {
-      const uint64_t bad = __builtin_amdgcn_ballot_w64(tk0[r] + lane < tcap[r] && va[r] != vb[r]);
-      if (lane == 0 && bad != 0) atomicMin(&cpre[tm[r]], tk0[r] + static_cast<int>(__builtin_ctzll(bad)));
+  } else {
+    for (int k = t; k < kShareHash; k += kPlanThreads) {
+      hk[k] = -1;
+      hv[k] = 0x7fffffff;
     }
-  }
-  __syncthreads();
+    gcount[t] = 0;
+    cpre[t] = nfb;
+    __syncthreads();
 
-  // 4. A subgroup shares the full blocks all its members hold in common with
-  //    the leader (the leader's own full blocks when it is a member).
-  if (sid >= 0) atomicMin(&sls[sid], cpre[t]);
-  __syncthreads();
-  int Ls = 0;
-  bool head = false;
-  if (sid >= 0 && sls[sid] * bs >= kMinSharedTokens) {
-    Ls = sls[sid] * bs;
-    head = rank == sub * nmax;
+    // 1. Groups: sequences whose first block is the same physical block.
+    int slot = 0;
+    if (keyed) {
+      uint32_t hh = (static_cast<uint32_t>(b0) * 2654435761u) >> (32 - kShareHashBits);
+      for (;;) {  // ends: at most kShareMaxSeqs keys in kShareHash slots
+        const int old = atomicCAS(&hk[hh], -1, b0);
+        if (old == -1 || old == b0) break;
+        hh = (hh + 1) & (kShareHash - 1);
+      }
+      slot = static_cast<int>(hh);
+      atomicMin(&hv[slot], t);
+    }
+    __syncthreads();
+    const int L = keyed ? hv[slot] : t;
+    lead[t] = L;
+    if (L != t) atomicAdd(&gcount[L], 1);
+    __syncthreads();
+
+    // 2. Rank in the group by sequence index; subgroups of nmax consecutive
+    //    ranks (a lone last member stays on its own).
+    int rank = 0;
+    if (L != t) {
+      rank = 1;
+      for (int j = L + 1; j < t; ++j) rank += lead[j] == L ? 1 : 0;
+    }
+    const int gn = live ? gcount[L] + 1 : 0;
+    const int gsub = gn >= 2 ? gn / nmax + (gn % nmax >= 2 ? 1 : 0) : 0;
+    // one scan for both: subgroups per leader (low 16 bits), members (high)
+    const bool member = live && L != t;
+    int both = 0;
+    const int sc = block_scan((L == t ? gsub : 0) | (member ? 1 << 16 : 0), wsum, both);
+    const int nsub_total = both & 0xffff, nmem = both >> 16;
+    sbase[t] = sc & 0xffff;
+    if (member) mlist[sc >> 16] = t;
+    for (int k = t; k < nsub_total; k += kPlanThreads) {
+      sls[k] = 0x7fffffff;
+#pragma unroll
+      for (int m = 0; m < kShareMaxMembers; ++m) smem[k][m] = -1;
+    }
+    __syncthreads();
+    const int sub = rank / nmax;
+    sid = (live && sub < gsub) ? sbase[L] + sub : -1;
+    if (sid >= 0) smem[sid][rank - sub * nmax] = t;
+
+    // 3. Each non-leader's table against its leader's, over the full blocks
+    //    both hold: tasks of 64 entries (one per lane), each task's member
+    //    found in an owner array (the hash arrays are free now), the loads of
+    //    kCmpBatch tasks per wave issued together.  At most kMaxCmpTasks tasks
+    //    are checked; a member whose tasks lie beyond shares only what was
+    //    checked.
+    int ntk = 0, cap = 0;
+    if (t < nmem) {
+      const int m = mlist[t];
+      cap = min(cpre[m], cpre[lead[m]]);
+      ntk = (cap + 63) / 64;
+    }
+    int ntask = 0;
+    const int tb = block_scan(ntk, wsum, ntask);
+    int* towner = hk;
+    if (t < nmem) {
+      const int e = min(tb + ntk, kMaxCmpTasks);
+      for (int k = tb; k < e; ++k) towner[k] = t;
+      cap = min(cap, max(e - tb, 0) * 64);
+      mcap[t] = cap;
+      tbase[t] = tb;
+      cpre[mlist[t]] = cap;
+    }
+    __syncthreads();
+    ntask = min(ntask, kMaxCmpTasks);
+    constexpr int kWavesPlan = kPlanThreads / 64;
+    for (int base = wave; base < ntask; base += kWavesPlan * kCmpBatch) {
+      // Lane r < kCmpBatch looks up task base + r * kWavesPlan (three LDS round
+      // trips for the whole batch); the values are then broadcast by readlane.
+      const int mtk = base + (lane % kCmpBatch) * kWavesPlan;
+      const int own = towner[mtk < ntask ? mtk : 0];
+      const int mm = mlist[own];
+      const int ml = lead[mm];
+      const int mcp = mtk < ntask ? mcap[own] : 0;
+      const int mk0 = (mtk - tbase[own]) * 64;
+      int tm[kCmpBatch], tk0[kCmpBatch], tcap[kCmpBatch], va[kCmpBatch], vb[kCmpBatch];
+#pragma unroll
+      for (int r = 0; r < kCmpBatch; ++r) {
+        tm[r] = __builtin_amdgcn_readlane(mm, r);
+        tk0[r] = __builtin_amdgcn_readlane(mk0, r);
+        tcap[r] = __builtin_amdgcn_readlane(mcp, r);
+        const int tl = __builtin_amdgcn_readlane(ml, r);
+        const int k = tk0[r] + lane;
+        const int kk = k < tcap[r] ? k : 0;  // tcap <= both rows' full blocks <= max_blocks
+        va[r] = p.tables[static_cast<size_t>(tm[r]) * p.max_blocks + kk];
+        vb[r] = p.tables[static_cast<size_t>(tl) * p.max_blocks + kk];
+      }
+#pragma unroll
+      for (int r = 0; r < kCmpBatch; ++r) {
+        const uint64_t bad = __builtin_amdgcn_ballot_w64(tk0[r] + lane < tcap[r] && va[r] != vb[r]);
+        if (lane == 0 && bad != 0) atomicMin(&cpre[tm[r]], tk0[r] + static_cast<int>(__builtin_ctzll(bad)));
+      }
+    }
+    __syncthreads();
+
+    // 4. A subgroup shares the full blocks all its members hold in common with
+    //    the leader (the leader's own full blocks when it is a member).
+    if (sid >= 0) atomicMin(&sls[sid], cpre[t]);
+    __syncthreads();
+    if (sid >= 0 && sls[sid] * bs >= kMinSharedTokens) {
+      Ls = sls[sid] * bs;
+      head = rank == sub * nmax;
+    }
   }
 
   // 5. Partition size from the work that remains: each sequence's own

@@ -46,6 +46,7 @@ struct DecodeParams {
   int32_t share_nmax;        // sequences per shared work item (their G query heads each: <= 16 columns)
   int32_t* seq_np;           // [S] partition states of each sequence (sharing mode)
   int4* groups;              // [S / 2] member sequences of each shared group (-1 = none)
+  const int32_t* host_plan;  // sharing groups found on the host (pa_batch_share_plan's words), or NULL
   int32_t flat;              // 1: no block table; tables[i] (max_blocks = 1) is sequence i's first
                              //    block and its blocks are consecutive (contiguous-layout comparison)
   // new tokens written before the decode (pa_decode_step; w_tokens = 0: none)

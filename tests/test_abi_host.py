@@ -271,3 +271,104 @@ def test_probe_rejects_unknown_load_forms_without_a_device():
         rc = pa.lib.pa_probe_read_chunks(None, 0, None, 0, form, wg, infl, None, None)
         assert pa.STATUS.get(rc) == "UNSUPPORTED", (form, wg, infl)
     assert pa.lib.pa_probe_read_chunks(None, 0, None, 0, 4, 2, 2, None, None) == 0  # nothing to read
+
+
+def _rule_subgroups(tables, ctx, bs, N, G):
+    """The grouping rule pa_batch_share_plan documents, restated plainly:
+    [(member rows, shared tokens)] in the order of the groups' leaders."""
+    nmax = min(4, 16 // G)
+    if nmax < 2:
+        return []
+    nfb = [int(c) // bs for c in ctx]
+    groups = {}
+    for i in range(len(ctx)):
+        if nfb[i] > 0 and 0 <= tables[i][0] < N:
+            groups.setdefault(int(tables[i][0]), []).append(i)
+    out = []
+    for mem in sorted(groups.values(), key=lambda m: m[0]):
+        lead = mem[0]
+        common = {lead: nfb[lead]}
+        for m in mem[1:]:
+            k = 0
+            while k < min(nfb[m], nfb[lead]) and tables[m][k] == tables[lead][k]:
+                k += 1
+            common[m] = k
+        for s in range(0, len(mem), nmax):
+            sub = mem[s:s + nmax]
+            ls = min(common[m] for m in sub) * bs
+            if len(sub) >= 2 and ls >= 256:
+                out.append((sub, ls))
+    return out
+
+
+def _decode_plan(plan, S):
+    K = int(plan[0])
+    sub, shared = plan[1:1 + S], plan[1 + S:1 + 2 * S]
+    mem = plan[1 + 2 * S:].reshape(-1, 4)
+    got = [([int(x) for x in mem[k] if x >= 0], None) for k in range(K)]
+    for k, (rows, _) in enumerate(got):
+        assert all(sub[r] == k for r in rows)
+        assert len({int(shared[r]) for r in rows}) == 1
+        got[k] = (rows, int(shared[rows[0]]))
+    assert sum(len(r) for r, _ in got) == int((sub >= 0).sum())
+    assert all(shared[i] == 0 for i in range(S) if sub[i] < 0)
+    assert (mem[K:] == -1).all()
+    return got
+
+
+@settings(max_examples=60, deadline=None)
+@given(st.integers(0, 10_000), st.sampled_from([(8, 8), (32, 8), (24, 8), (64, 8), (10, 2), (64, 4)]),
+       st.sampled_from([16, 32]))
+def test_host_share_plan_follows_the_rule(seed, heads, bs):
+    """pa_batch_share_plan on fork / append / copy-on-write scripts of the
+    block manager, against the rule restated in _rule_subgroups, and the
+    property the decode relies on: every member's first Ls tokens lie in the
+    same physical blocks as the other members'."""
+    rng = np.random.default_rng(seed)
+    Hq, Hkv = heads
+    N = 3000
+    pool = pa.Pool(1, N, bs, Hkv, 64, "bf16", free_order=rng.permutation(N).astype(np.int32), device=None)
+    seqs = []
+    for grp in range(int(rng.integers(1, 6))):
+        s0 = pool.seq_create()
+        pool.seq_append(s0, int(rng.integers(0, 1400)))
+        members = [s0]
+        for _ in range(int(rng.integers(0, 9))):
+            child = pool.seq_fork(members[int(rng.integers(0, len(members)))])
+            members.append(child)
+            if rng.random() < 0.5:
+                pool.seq_append(child, int(rng.integers(0, 60)))
+        seqs += members
+    for _ in range(int(rng.integers(0, 3))):
+        s = pool.seq_create()
+        pool.seq_append(s, int(rng.integers(0, 900)))
+        seqs.append(s)
+    for s in rng.permutation(seqs):
+        pool.seq_append(int(s), int(rng.integers(0, 40)))
+    order = [int(x) for x in rng.permutation(seqs)]
+    S = len(order)
+    width = max(1, max(len(pool.seq_block_table(s)[0]) for s in order))
+    tables, ctx = pool.batch_tables(order, width)
+    plan = pool.batch_share_plan(order, Hq)
+    assert plan.shape[0] == pa.lib.pa_share_plan_words(S) == 1 + 2 * S + 4 * (S // 2 + 1)
+    got = _decode_plan(plan, S)
+    assert got == _rule_subgroups(tables, ctx, bs, N, Hq // Hkv)
+    for rows, ls in got:
+        assert 2 <= len(rows) <= min(4, 16 // (Hq // Hkv)) and ls % bs == 0 and ls >= 256
+        for r in rows:
+            assert ctx[r] >= ls and (tables[r][:ls // bs] == tables[rows[0]][:ls // bs]).all()
+
+
+def test_host_share_plan_argument_checks():
+    pool = pa.Pool(1, 64, 16, 2, 64, "bf16", device=None)
+    s = pool.seq_create()
+    pool.seq_append(s, 300)
+    with pytest.raises(pa.PAError) as e:
+        pool.batch_share_plan([s, 7], 4)
+    assert e.value.status == "INVALID_ARG"
+    with pytest.raises(pa.PAError):
+        pool.batch_share_plan([s], 3)  # not a multiple of the kv heads
+    assert pool.batch_share_plan([], 4).tolist() == [0, -1, -1, -1, -1]
+    pool.seq_fork(s)
+    plan = pool.batch_share_plan([s, s + 1], 4)
+    assert _decode_plan(plan, 2) == [([0, 1], 288)]

@@ -186,6 +186,19 @@ def test_forked_branches_match_oracle(case):
     if G <= 8:
         assert nsub == exp
         assert exp > 0
+    # the same groups found on the host (pa_batch_share_plan) and handed to
+    # pa_decode_step_shared: the same items, so the same bits
+    plan = torch.from_numpy(pool.batch_share_plan(order, Hq)).cuda()
+    none_kv = torch.empty(0, Hkv, D, dtype=pa.TORCH_DTYPE[dtype], device="cuda")
+    ws = torch.empty(pool.workspace_bytes(S, Hq, max_ctx, 0), dtype=torch.uint8, device="cuda")
+    out_h = pool.decode_step(0, none_kv, none_kv, torch.empty(0, dtype=torch.int32, device="cuda"),
+                             U.dev_tensor(q, dtype), torch.from_numpy(tables).cuda(), torch.from_numpy(ctx).cuda(),
+                             max_ctx, scale, 0, workspace=ws, share_plan=plan)
+    torch.cuda.synchronize()
+    bits = U.TORCH_BITS[dtype]
+    assert torch.equal(out_h.view(bits), out.view(bits))
+    if G <= 8:
+        assert int(ws[:16].view(torch.int32)[3].item()) == exp
 
 
 # ------------------------------------------------------- hand-built tables ---

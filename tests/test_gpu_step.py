@@ -111,6 +111,15 @@ def test_step_with_sharing_plan_and_skipped_slot():
                            q, t, c, int(ctx.max()), w.scale, 0, workspace=ws)
     torch.cuda.synchronize()
     assert int(ws[:16].view(torch.int32)[3].item()) == w.script["groups"]
+    # the groups found on the host instead (pa_decode_step_shared): same bits
+    # (the step rewrites the same tokens with the same values)
+    plan = torch.from_numpy(pool.batch_share_plan(list(range(w.num_seqs)), w.num_q_heads)).cuda()
+    ws2 = torch.empty_like(ws)
+    out_h = pool.decode_step(0, U.dev_tensor(kn, "bf16"), U.dev_tensor(vn, "bf16"), torch.from_numpy(slots).cuda(),
+                             q, t, c, int(ctx.max()), w.scale, 0, workspace=ws2, share_plan=plan)
+    torch.cuda.synchronize()
+    assert int(ws2[:16].view(torch.int32)[3].item()) == w.script["groups"]
+    assert torch.equal(out_h.view(torch.int16), out.view(torch.int16))
     from oracle import attention as A
     ref = []
     for i in range(w.num_seqs):
