@@ -100,6 +100,14 @@ constexpr int kWorkgroupsPerCU = PA_WG_PER_CU;
 // Work items.
 // ---------------------------------------------------------------------------
 
+#ifndef PA_SHARE_OVERLAP
+#define PA_SHARE_OVERLAP 1
+#endif
+// Sharing plan, shallow schedule: the next item's loads go out before the
+// finished item's states are merged.
+constexpr bool kShareOverlap = PA_SHARE_OVERLAP != 0;
+constexpr int kSlotEmpty = -1;  // an LDS index slot not yet posted (work indices are >= 0)
+
 // Sequences one shared work item covers at most (their G query heads each
 // take a column of the 16-wide score tile).
 constexpr int kShareMaxMembers = 4;
@@ -1120,6 +1128,10 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p, const 
     if constexpr (kShare) Path::load_q_members(qq, p, ii, item_members(ii, groups), lane);
     else Path::load_q(qq, p, ii, lane);
   };
+  if constexpr (kShare && kShareOverlap && !kDeep) {
+    if (threadIdx.x == 0) sm.slot[0] = sm.slot[1] = kSlotEmpty;
+    __syncthreads();
+  }
   Item it = item_at(cur);
   typename Path::Q q;
   load_q(q, it);
@@ -1173,6 +1185,35 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p, const 
       nxt = rfl(sm.slot[k & 1]);
       it = nit;
       q = qn;
+    } else if constexpr (kShare && kShareOverlap) {
+      // The next index goes from thread 0 to the other waves through an LDS
+      // slot that holds kSlotEmpty until it is posted; each wave then reads
+      // the next item's record, query rows and block ids and issues its first
+      // units before this item's states are merged, so the merge runs while
+      // those loads are in flight.  Thread 0 posts before it waits for
+      // anything, so the wait ends.
+      typename Path::State s;
+      run_item(s);
+      if (threadIdx.x == 0) __hip_atomic_store(&sm.slot[k & 1], nn, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      int posted;
+      while ((posted = __hip_atomic_load(&sm.slot[k & 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) ==
+             kSlotEmpty)
+        __builtin_amdgcn_s_sleep(1);
+      cur = rfl(posted);
+      const Item done = it;
+      if (cur < total) {
+        it = item_at(cur);
+        load_q(q, it);
+        st.begin(p, it.trow, it.start, it.u0, it.h);
+        st.ids = st.fetch_ids(lane);
+        prologue<PF, NCH>(st, f, ok, lane);
+      }
+      Path::to_lds(s, sm, wave, lane, done.cols);
+      finish_partition<T, D, Smem::kRows, kShare>(p, sm, done, groups, seq_np);
+      __syncthreads();
+      // Every wave has read the slot (before the barrier): empty it for item k + 2.
+      if (threadIdx.x == 0) sm.slot[k & 1] = kSlotEmpty;
+      if (cur >= total) break;
     } else {
       typename Path::State s;
       run_item(s);
