@@ -100,14 +100,6 @@ constexpr int kWorkgroupsPerCU = PA_WG_PER_CU;
 // Work items.
 // ---------------------------------------------------------------------------
 
-#ifndef PA_SHARE_OVERLAP
-#define PA_SHARE_OVERLAP 1
-#endif
-// Sharing plan, shallow schedule: the next item's loads go out before the
-// finished item's states are merged.
-constexpr bool kShareOverlap = PA_SHARE_OVERLAP != 0;
-constexpr int kSlotEmpty = -1;  // an LDS index slot not yet posted (work indices are >= 0)
-
 // Sequences one shared work item covers at most (their G query heads each
 // take a column of the 16-wide score tile).
 constexpr int kShareMaxMembers = 4;
@@ -449,8 +441,10 @@ constexpr int kShareHash = 1 << kShareHashBits;  // open addressing at load fact
 static_assert(kShareHash >= 2 * kShareMaxSeqs, "hash load factor");
 static_assert(kShareHash >= kPlanBins, "the hash arrays hold the size bins afterwards");
 constexpr int kMinSharedTokens = 256;  // shorter common prefixes are read per sequence
+// Work items per workgroup that size the sharing plan's partitions (two
+// workgroups per CU run its decode, so two items per CU).
 #ifndef PA_SHARE_ITEMS_PER_WG
-#define PA_SHARE_ITEMS_PER_WG 2
+#define PA_SHARE_ITEMS_PER_WG 1
 #endif
 constexpr int kShareItemsPerWorkgroup = PA_SHARE_ITEMS_PER_WG;
 constexpr int kCmpBatch = 8;           // comparison tasks whose loads a wave issues together
@@ -1128,10 +1122,6 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p, const 
     if constexpr (kShare) Path::load_q_members(qq, p, ii, item_members(ii, groups), lane);
     else Path::load_q(qq, p, ii, lane);
   };
-  if constexpr (kShare && kShareOverlap && !kDeep) {
-    if (threadIdx.x == 0) sm.slot[0] = sm.slot[1] = kSlotEmpty;
-    __syncthreads();
-  }
   Item it = item_at(cur);
   typename Path::Q q;
   load_q(q, it);
@@ -1185,35 +1175,6 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p, const 
       nxt = rfl(sm.slot[k & 1]);
       it = nit;
       q = qn;
-    } else if constexpr (kShare && kShareOverlap) {
-      // The next index goes from thread 0 to the other waves through an LDS
-      // slot that holds kSlotEmpty until it is posted; each wave then reads
-      // the next item's record, query rows and block ids and issues its first
-      // units before this item's states are merged, so the merge runs while
-      // those loads are in flight.  Thread 0 posts before it waits for
-      // anything, so the wait ends.
-      typename Path::State s;
-      run_item(s);
-      if (threadIdx.x == 0) __hip_atomic_store(&sm.slot[k & 1], nn, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-      int posted;
-      while ((posted = __hip_atomic_load(&sm.slot[k & 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) ==
-             kSlotEmpty)
-        __builtin_amdgcn_s_sleep(1);
-      cur = rfl(posted);
-      const Item done = it;
-      if (cur < total) {
-        it = item_at(cur);
-        load_q(q, it);
-        st.begin(p, it.trow, it.start, it.u0, it.h);
-        st.ids = st.fetch_ids(lane);
-        prologue<PF, NCH>(st, f, ok, lane);
-      }
-      Path::to_lds(s, sm, wave, lane, done.cols);
-      finish_partition<T, D, Smem::kRows, kShare>(p, sm, done, groups, seq_np);
-      __syncthreads();
-      // Every wave has read the slot (before the barrier): empty it for item k + 2.
-      if (threadIdx.x == 0) sm.slot[k & 1] = kSlotEmpty;
-      if (cur >= total) break;
     } else {
       typename Path::State s;
       run_item(s);
@@ -1412,24 +1373,24 @@ __global__ __launch_bounds__(kMergeThreads) void merge_wide_kernel(DecodeParams 
 
 // Persistent grid: kWorkgroupsPerCU workgroups per CU (never more than the
 // kernel's occupancy allows), cached per device.
-int persistent_grid(const void* kernel) {
+int persistent_grid(const void* kernel, int wg_per_cu = kWorkgroupsPerCU) {
   static std::mutex mu;
   static struct {
     const void* k;
-    int dev, grid;
+    int dev, cap, grid;
   } cache[64];
   static int n = 0;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
   std::lock_guard<std::mutex> lock(mu);
   for (int c = 0; c < n; ++c)
-    if (cache[c].k == kernel && cache[c].dev == dev) return cache[c].grid;
+    if (cache[c].k == kernel && cache[c].dev == dev && cache[c].cap == wg_per_cu) return cache[c].grid;
   int cus = 0, occ = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, kThreads, 0) != hipSuccess) return 0;
-  const int per_cu = occ > 0 && occ < kWorkgroupsPerCU ? occ : kWorkgroupsPerCU;
+  const int per_cu = occ > 0 && occ < wg_per_cu ? occ : wg_per_cu;
   const int grid = (cus > 0 ? cus : 1) * per_cu;
-  if (n < 64) cache[n++] = {kernel, dev, grid};
+  if (n < 64) cache[n++] = {kernel, dev, wg_per_cu, grid};
   return grid;
 }
 
@@ -1498,6 +1459,18 @@ hipError_t launch_decode_kernel(DecodeParams p, hipStream_t stream) {
 #define PA_SHARE_DEEP 0
 #endif
 constexpr bool kShareDeep = PA_SHARE_DEEP != 0;
+// Two workgroups per CU for the sharing plan's decode: its items are short
+// (about 3.5 per CU), and while one workgroup merges an item's wave states
+// and starts the next, the other streams.  Measured on MI355X (64 branches
+// over 16 shared 2,048-token prefixes, groups from the host): 54.3 us per
+// step with one workgroup per CU and two items each, 50.7 us with two
+// workgroups and one item each (copy-on-write batch 53.6 -> 51.8 us); two
+// workgroups with two items each, or with the partition size doubled, were no
+// better than one.  The other instances keep one workgroup per CU.
+#ifndef PA_SHARE_WG_PER_CU
+#define PA_SHARE_WG_PER_CU 2
+#endif
+constexpr int kShareWorkgroupsPerCU = PA_SHARE_WG_PER_CU;
 
 // Sharing plan and decode: the MFMA path with a 16-column tile for every G,
 // so that the query heads of up to four sequences that share a prefix fill
@@ -1506,7 +1479,7 @@ template <typename T, int D>
 hipError_t launch_share(DecodeParams p, hipStream_t stream) {
   using Path = MfmaPath<T, D, 16>;
   const void* k = reinterpret_cast<const void*>(&decode_kernel<Path, T, D, kShareDeep, true>);
-  int grid = persistent_grid(k);
+  int grid = persistent_grid(k, kShareWorkgroupsPerCU);
   if (grid <= 0) return hipErrorInvalidValue;
   const int64_t work_bound = static_cast<int64_t>(p.S) * p.ws_stride * p.H;
   if (grid > work_bound) grid = static_cast<int>(work_bound);
