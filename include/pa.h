@@ -209,9 +209,11 @@ size_t pa_share_plan_words(int num_seqs);
  *   num_q_heads query heads (G = num_q_heads / num_kv_heads)
  *   plan_out    host int32 [pa_share_plan_words(num_seqs)]:
  *                 [0]                number of subgroups K
- *                 [1 + i]            subgroup of batch row i, -1 for none
- *                 [1 + S + i]        tokens row i shares with its subgroup
- *                 [1 + 2S + 4k + m]  member m of subgroup k (batch rows, -1 padded)
+ *                 [1]                S = num_seqs
+ *                 [2]                members per subgroup at most, min(4, 16 / G)
+ *                 [3 + i]            subgroup of batch row i, -1 for none
+ *                 [3 + S + i]        tokens row i shares with its subgroup
+ *                 [3 + 2S + 4k + m]  member m of subgroup k (batch rows, -1 padded)
  * Host only, synchronous.  Errors: INVALID_ARG (unknown, released or
  * swapped-out sequence, num_q_heads not a multiple of num_kv_heads). */
 int pa_batch_share_plan(const pa_pool* pool, const int* seqs, int num_seqs, int num_q_heads,
@@ -221,10 +223,12 @@ int pa_batch_share_plan(const pa_pool* pool, const int* seqs, int num_seqs, int 
  * pa_batch_share_plan (for the same sequences in the same order) instead of
  * on the device: the device then skips the grouping and the id-by-id check
  * and only builds the work list.  share_plan: device copy of those words
- * (NULL: exactly pa_decode_step).  The plan is trusted as the tables are:
- * a plan from another batch gives wrong attention, though every access stays
- * within the pool, q and out (subgroup ids, members and shared lengths are
- * clamped on the device).  The plan is used where pa_decode_step would use
+ * (NULL: exactly pa_decode_step); a plan whose words 1 and 2 do not match
+ * this call (another batch size or group size G) is ignored and the device
+ * finds the groups itself.  Otherwise the plan is trusted as the tables are:
+ * a plan from another batch of the same shape gives wrong attention, though
+ * every access stays within the pool, q, out and the workspace (subgroup
+ * ids, members and shared lengths are clamped on the device).  The plan is used where pa_decode_step would use
  * its own (the pool holds shared blocks, automatic partition size, several
  * partitions possible, num_seqs <= 1024, G <= 8); otherwise the call is
  * pa_decode_step's.  The rest as for pa_decode_step. */

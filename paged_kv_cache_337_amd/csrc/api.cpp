@@ -373,7 +373,7 @@ int pa_decode_step_shared(pa_pool* pool, int layer, const void* k, const void* v
 
 size_t pa_share_plan_words(int num_seqs) {
   if (num_seqs < 0) return 0;
-  return 1 + 2 * static_cast<size_t>(num_seqs) + 4 * (static_cast<size_t>(num_seqs) / 2 + 1);
+  return 3 + 2 * static_cast<size_t>(num_seqs) + 4 * (static_cast<size_t>(num_seqs) / 2 + 1);
 }
 
 int pa_batch_share_plan(const pa_pool* pool, const int* seqs, int num_seqs, int num_q_heads, int32_t* plan_out) {
@@ -389,10 +389,12 @@ int pa_batch_share_plan(const pa_pool* pool, const int* seqs, int num_seqs, int 
     }
     const int S = num_seqs, bs = d.block_size, G = num_q_heads / d.num_kv_heads;
     const int nmax = std::min(4, 16 / G);
-    int32_t* sub = plan_out + 1;
-    int32_t* shared = plan_out + 1 + S;
-    int32_t* members = plan_out + 1 + 2 * static_cast<size_t>(S);
+    int32_t* sub = plan_out + 3;
+    int32_t* shared = plan_out + 3 + S;
+    int32_t* members = plan_out + 3 + 2 * static_cast<size_t>(S);
     std::fill(plan_out, plan_out + pa_share_plan_words(S), 0);
+    plan_out[1] = S;
+    plan_out[2] = nmax;
     std::fill(sub, sub + S, -1);
     std::fill(members, members + 4 * (static_cast<size_t>(S) / 2 + 1), -1);
     // groups: rows whose first full block is the same block, in batch order

@@ -498,12 +498,15 @@ __device__ __forceinline__ void plan_share(const DecodeParams& p) {
   const bool keyed = nfb > 0 && b0 >= 0 && b0 < p.N;
   int sid = -1, Ls = 0;  // subgroup, shared tokens
   bool head = false;     // first member of an active subgroup
-  if (p.host_plan) {
+  // Groups found on the host: used when made for this batch size and group
+  // size (words 1 and 2), else found here.
+  const bool from_host = p.host_plan != nullptr && p.host_plan[1] == p.S && p.host_plan[2] == nmax;
+  if (from_host) {
     // Steps 1-4 done on the host from the block manager's tables: row t's
     // subgroup and shared tokens, each subgroup's members.  Every value is
     // clamped into range, so a plan that does not fit the batch gives wrong
     // attention but no access outside the buffers.
-    const int32_t* hp = p.host_plan;
+    const int32_t* hp = p.host_plan + 2;  // hp[1 + i] is word 3 + i
     const int nsub = p.S / 2;  // at most one subgroup per two rows
     for (int k = t; k < nsub; k += kPlanThreads) sls[k] = 0x7fffffff;
     __syncthreads();
@@ -521,9 +524,11 @@ __device__ __forceinline__ void plan_share(const DecodeParams& p) {
       const int32_t* mem = hp + 1 + 2 * static_cast<size_t>(p.S) + 4 * static_cast<size_t>(sid);
       head = mem[0] == t;
       if (head) {
+        // at most nmax members, so that their query heads fit the score tile
         smem[sid][0] = t;
 #pragma unroll
-        for (int m = 1; m < kShareMaxMembers; ++m) smem[sid][m] = (mem[m] >= 0 && mem[m] < p.S) ? mem[m] : -1;
+        for (int m = 1; m < kShareMaxMembers; ++m)
+          smem[sid][m] = (m < nmax && mem[m] >= 0 && mem[m] < p.S) ? mem[m] : -1;
       }
     }
   } else {

@@ -301,10 +301,13 @@ def _rule_subgroups(tables, ctx, bs, N, G):
     return out
 
 
-def _decode_plan(plan, S):
+def _decode_plan(plan, S, nmax=None):
     K = int(plan[0])
-    sub, shared = plan[1:1 + S], plan[1 + S:1 + 2 * S]
-    mem = plan[1 + 2 * S:].reshape(-1, 4)
+    assert int(plan[1]) == S
+    if nmax is not None:
+        assert int(plan[2]) == nmax
+    sub, shared = plan[3:3 + S], plan[3 + S:3 + 2 * S]
+    mem = plan[3 + 2 * S:].reshape(-1, 4)
     got = [([int(x) for x in mem[k] if x >= 0], None) for k in range(K)]
     for k, (rows, _) in enumerate(got):
         assert all(sub[r] == k for r in rows)
@@ -350,8 +353,8 @@ def test_host_share_plan_follows_the_rule(seed, heads, bs):
     width = max(1, max(len(pool.seq_block_table(s)[0]) for s in order))
     tables, ctx = pool.batch_tables(order, width)
     plan = pool.batch_share_plan(order, Hq)
-    assert plan.shape[0] == pa.lib.pa_share_plan_words(S) == 1 + 2 * S + 4 * (S // 2 + 1)
-    got = _decode_plan(plan, S)
+    assert plan.shape[0] == pa.lib.pa_share_plan_words(S) == 3 + 2 * S + 4 * (S // 2 + 1)
+    got = _decode_plan(plan, S, min(4, 16 // (Hq // Hkv)))
     assert got == _rule_subgroups(tables, ctx, bs, N, Hq // Hkv)
     for rows, ls in got:
         assert 2 <= len(rows) <= min(4, 16 // (Hq // Hkv)) and ls % bs == 0 and ls >= 256
@@ -368,7 +371,7 @@ def test_host_share_plan_argument_checks():
     assert e.value.status == "INVALID_ARG"
     with pytest.raises(pa.PAError):
         pool.batch_share_plan([s], 3)  # not a multiple of the kv heads
-    assert pool.batch_share_plan([], 4).tolist() == [0, -1, -1, -1, -1]
+    assert pool.batch_share_plan([], 4).tolist() == [0, 0, 4, -1, -1, -1, -1]
     pool.seq_fork(s)
     plan = pool.batch_share_plan([s, s + 1], 4)
     assert _decode_plan(plan, 2) == [([0, 1], 288)]

@@ -199,6 +199,20 @@ def test_forked_branches_match_oracle(case):
     assert torch.equal(out_h.view(bits), out.view(bits))
     if G <= 8:
         assert int(ws[:16].view(torch.int32)[3].item()) == exp
+    # a plan made for another group size (members per subgroup) or another
+    # batch size is ignored: the device finds the groups itself
+    wrong_g = pool.batch_share_plan(order, Hkv if G > 1 else 2 * Hkv)
+    wrong_s = pool.batch_share_plan(order[:-1], Hq)
+    for bad in (wrong_g, np.concatenate([wrong_s, np.full(8, -1, np.int32)])):
+        if G <= 8 and (bad[1] == S and bad[2] == min(4, 16 // G)):
+            continue  # the same shape after all (G = 3 and G = 1 both allow four members)
+        ws.zero_()
+        out_b = pool.decode_step(0, none_kv, none_kv, torch.empty(0, dtype=torch.int32, device="cuda"),
+                                 U.dev_tensor(q, dtype), torch.from_numpy(tables).cuda(),
+                                 torch.from_numpy(ctx).cuda(), max_ctx, scale, 0, workspace=ws,
+                                 share_plan=torch.from_numpy(bad).cuda())
+        torch.cuda.synchronize()
+        assert torch.equal(out_b.view(bits), out.view(bits))
 
 
 # ------------------------------------------------------- hand-built tables ---
