@@ -228,10 +228,11 @@ int pa_batch_share_plan(const pa_pool* pool, const int* seqs, int num_seqs, int 
  * finds the groups itself.  Otherwise the plan is trusted as the tables are:
  * a plan from another batch of the same shape gives wrong attention, though
  * every access stays within the pool, q, out and the workspace (subgroup
- * ids, members and shared lengths are clamped on the device).  The plan is used where pa_decode_step would use
- * its own (the pool holds shared blocks, automatic partition size, several
- * partitions possible, num_seqs <= 1024, G <= 8); otherwise the call is
- * pa_decode_step's.  The rest as for pa_decode_step. */
+ * ids, members and shared lengths are clamped on the device).  The plan is
+ * used where pa_decode_step would use its own (the pool holds shared blocks,
+ * automatic partition size, several partitions possible, num_seqs <= 1024,
+ * G <= 8); otherwise the call is pa_decode_step's.  The rest as for
+ * pa_decode_step. */
 int pa_decode_step_shared(pa_pool* pool, int layer, const void* k, const void* v, const int32_t* slot_mapping,
                           int num_tokens, const void* q, int num_seqs, int num_q_heads,
                           const int32_t* block_tables, int max_blocks_per_seq, const int32_t* context_lens,
