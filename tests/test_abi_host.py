@@ -221,6 +221,18 @@ def test_decode_argument_checks_need_no_device():
     assert call(q=(1 << 24) + 8) == "INVALID_ARG"
     assert call(scale=float("inf")) == "INVALID_ARG"
 
+    # pa_decode_step_shared checks the same arguments before any launch
+    def call_shared(layer=0, S=2, Hq=4, wsb=1 << 20, plan=1 << 28):
+        rc = pa.lib.pa_decode_step_shared(pool.handle, layer, None, None, None, 0, vp(1 << 24), S, Hq,
+                                          vp(1 << 25), 4, vp(1 << 26), 64, 0.125, 0, vp(1 << 20), wsb,
+                                          vp(1 << 27), None, vp(plan))
+        return "OK" if rc == 0 else pa.STATUS.get(rc, "?")
+
+    assert call_shared(layer=1) == "INVALID_ARG"
+    assert call_shared(S=0) == "OK"
+    assert call_shared(Hq=3) == "INVALID_ARG"
+    assert call_shared(wsb=16) == "BUFFER_TOO_SMALL"
+
 
 def test_binding_rejects_mismatched_tensors_before_any_launch():
     """The kernels trust shapes, dtypes and strides.  The binding checks every
@@ -364,6 +376,13 @@ def test_host_share_plan_follows_the_rule(seed, heads, bs):
 
 def test_host_share_plan_argument_checks():
     pool = pa.Pool(1, 64, 16, 2, 64, "bf16", device=None)
+    seqs = (ctypes.c_int * 1)(0)
+    out = (ctypes.c_int32 * 16)()
+    assert pa.STATUS[pa.lib.pa_batch_share_plan(None, seqs, 1, 4, out)] == "INVALID_ARG"
+    assert pa.STATUS[pa.lib.pa_batch_share_plan(pool.handle, None, 1, 4, out)] == "INVALID_ARG"
+    assert pa.STATUS[pa.lib.pa_batch_share_plan(pool.handle, seqs, -1, 4, out)] == "INVALID_ARG"
+    assert pa.STATUS[pa.lib.pa_batch_share_plan(pool.handle, seqs, 0, 4, None)] == "INVALID_ARG"
+    assert pa.lib.pa_share_plan_words(-1) == 0
     s = pool.seq_create()
     pool.seq_append(s, 300)
     with pytest.raises(pa.PAError) as e:
