@@ -7,7 +7,9 @@ Three calls in a row on the static scratch, each smaller than the one before
 batch with an automatic partition size, a short batch): every output equals
 pa_decode's on the same inputs bit for bit and matches the oracle within the
 tolerances.  A decode whose workspace would exceed the scratch is refused
-before any launch, leaving the output untouched.
+before any launch, leaving the output untouched.  A batch of forked
+branches runs the sharing plan on the same scratch and matches pa_decode bit
+for bit.
 """
 import numpy as np
 import pytest
@@ -53,6 +55,29 @@ def test_noalloc_equals_decode_on_consecutive_calls():
     for w, pool, q, t, c, ref, out in staged:
         assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), w.name
         U.check_close(U.out_f64(out), U.oracle_rows(w, range(w.num_seqs)), w.dtype, f"noalloc {w.name}")
+
+
+def test_noalloc_with_the_sharing_plan():
+    """Forked branches (the pool's block manager holds shared blocks): the
+    sharing plan's per-sequence state counts and subgroups live in the static
+    scratch too, after the other calls left it dirty."""
+    import paged_kv_cache_337_amd as pa
+    from paged_kv_cache_337_amd import staging as S
+    w = W.shared()
+    pool = pa.Pool(1, w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim, w.dtype,
+                   free_order=w.script["free_order"])
+    U.poison(pool)
+    S.run_shared_script(pool, w, W.shared_prefix_kv, W.private_kv, layers=(0,))
+    width = max(len(pool.seq_block_table(s)[0]) for s in range(w.num_seqs))
+    tables, ctx = pool.batch_tables(list(range(w.num_seqs)), width)
+    q, t, c = U.device_inputs(w, tables=tables, ctx=ctx)
+    max_ctx = int(ctx.max())
+    ref = pool.decode(0, q, t, c, max_ctx, w.scale, 0)
+    out = torch.full_like(q, 7.0)
+    U.log(f"[noalloc] shared: S={w.num_seqs} max_ctx={max_ctx}")
+    pool.decode_noalloc(0, q, t, c, max_ctx, w.scale, out, 0)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
 
 
 def test_noalloc_refuses_a_workspace_beyond_the_scratch():
