@@ -1,0 +1,98 @@
+"""Decode calls captured in a HIP graph (torch.cuda.CUDAGraph) and replayed,
+through the C ABI: the plan resets its work counter on every launch and no
+call records a memset, so each replay must equal the eager call bit for bit.
+
+Each graph is replayed three times with eager work in between (the output
+overwritten, the stream synchronised), and every replay is checked.  Cases:
+pa_decode with a caller workspace (several partitions, the merge kernel),
+pa_decode_noalloc on the static scratch, pa_decode_step (the new tokens'
+write beside the plan; the write is idempotent), and pa_decode_step_shared
+over forked branches with the block manager's sharing groups.
+"""
+import numpy as np
+import pytest
+import torch
+
+pytestmark = pytest.mark.gpu
+
+import workloads as W  # noqa: E402
+from tests import gpu_util as U  # noqa: E402
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU")
+    import paged_kv_cache_337_amd  # noqa: F401
+
+
+def _replay_matches(call, out, ref, bits, name):
+    call()  # warm: the launch shapes are chosen (and cached) outside the capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    torch.cuda.synchronize()
+    for r in range(3):
+        out.fill_(7.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        U.log(f"[graph] {name}: replay {r}")
+        assert torch.equal(out.view(bits), ref.view(bits)), f"{name}: replay {r}"
+
+
+def test_captured_decode_calls_replay_exactly():
+    import paged_kv_cache_337_amd as pa
+    w = W.scaled_down(W.llama3_8b(), 24, 2500, seed_offset=300)
+    pool = U.make_pool(w)
+    U.fill_pool(pool, w)
+    q, t, c = U.device_inputs(w)
+    bits = U.TORCH_BITS[w.dtype]
+    ref = pool.decode(0, q, t, c, w.max_context_len, w.scale)
+    torch.cuda.synchronize()
+
+    out = torch.empty_like(q)
+    ws = torch.empty(pool.workspace_bytes(w.num_seqs, w.num_q_heads, w.max_context_len), dtype=torch.uint8,
+                     device="cuda")
+    _replay_matches(lambda: pool.decode(0, q, t, c, w.max_context_len, w.scale, out=out, workspace=ws),
+                    out, ref, bits, "pa_decode")
+
+    out2 = torch.empty_like(q)
+    _replay_matches(lambda: pool.decode_noalloc(0, q, t, c, w.max_context_len, w.scale, out2),
+                    out2, ref, bits, "pa_decode_noalloc")
+
+    # the step rewrites every sequence's newest token with the values it holds
+    last = w.context_lens - 1
+    kn = np.stack([w.seq_kv(i)[0][last[i]] for i in range(w.num_seqs)])
+    vn = np.stack([w.seq_kv(i)[1][last[i]] for i in range(w.num_seqs)])
+    slots = pa.slots_for_positions(w.block_tables, w.block_size, last, np.ones(w.num_seqs)).astype(np.int32)
+    kd, vd, sd = U.dev_tensor(kn, w.dtype), U.dev_tensor(vn, w.dtype), torch.from_numpy(slots).cuda()
+    out3 = torch.empty_like(q)
+    _replay_matches(lambda: pool.decode_step(0, kd, vd, sd, q, t, c, w.max_context_len, w.scale, out=out3,
+                                             workspace=ws), out3, ref, bits, "pa_decode_step")
+
+
+def test_captured_shared_step_replays_exactly():
+    import paged_kv_cache_337_amd as pa
+    from paged_kv_cache_337_amd import staging as S
+    w = W.shared()
+    pool = pa.Pool(1, w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim, w.dtype,
+                   free_order=w.script["free_order"])
+    U.poison(pool)
+    S.run_shared_script(pool, w, W.shared_prefix_kv, W.private_kv, layers=(0,))
+    seqs = list(range(w.num_seqs))
+    width = max(len(pool.seq_block_table(s)[0]) for s in seqs)
+    tables, ctx = pool.batch_tables(seqs, width)
+    q, t, c = U.device_inputs(w, tables=tables, ctx=ctx)
+    max_ctx = int(ctx.max())
+    ref = pool.decode(0, q, t, c, max_ctx, w.scale)
+    torch.cuda.synchronize()
+    plan = torch.from_numpy(pool.batch_share_plan(seqs, w.num_q_heads)).cuda()
+    empty_kv = torch.empty(0, w.num_kv_heads, w.head_dim, dtype=torch.bfloat16, device="cuda")
+    none = torch.empty(0, dtype=torch.int32, device="cuda")
+    out = torch.empty_like(q)
+    ws = torch.empty(pool.workspace_bytes(w.num_seqs, w.num_q_heads, max_ctx), dtype=torch.uint8, device="cuda")
+    _replay_matches(lambda: pool.decode_step(0, empty_kv, empty_kv, none, q, t, c, max_ctx, w.scale, out=out,
+                                             workspace=ws, share_plan=plan), out, ref, torch.int16,
+                    "pa_decode_step_shared")
