@@ -1,4 +1,4 @@
-"""Decode calls captured in a HIP graph (torch.cuda.CUDAGraph) and replayed,
+"""Decode and prefill calls captured in a HIP graph (torch.cuda.CUDAGraph) and replayed,
 through the C ABI: the plan resets its work counter on every launch and no
 call records a memset, so each replay must equal the eager call bit for bit.
 
@@ -6,8 +6,8 @@ Each graph is replayed three times with eager work in between (the output
 overwritten, the stream synchronised), and every replay is checked.  Cases:
 pa_decode with a caller workspace (several partitions, the merge kernel),
 pa_decode_noalloc on the static scratch, pa_decode_step (the new tokens'
-write beside the plan; the write is idempotent), and pa_decode_step_shared
-over forked branches with the block manager's sharing groups.
+write beside the plan; the write is idempotent), pa_decode_step_shared over
+forked branches with the block manager's sharing groups, and pa_prefill.
 """
 import numpy as np
 import pytest
@@ -96,3 +96,16 @@ def test_captured_shared_step_replays_exactly():
     _replay_matches(lambda: pool.decode_step(0, empty_kv, empty_kv, none, q, t, c, max_ctx, w.scale, out=out,
                                              workspace=ws, share_plan=plan), out, ref, torch.int16,
                     "pa_decode_step_shared")
+
+
+def test_captured_prefill_replays_exactly():
+    from paged_kv_cache_337_amd import staging as S
+    w = W.custom_prefill("graph_prefill", 85, "bf16", [300, 700, 40, 1200], [300, 64, 40, 256], 32, 8, 128, 16)
+    pool = U.make_pool(w)
+    U.fill_pool(pool, w)
+    q, qs, t, c = S.prefill_inputs(w)
+    ref = pool.prefill(0, q, qs, w.max_query_len, t, c, w.max_context_len, w.scale)
+    torch.cuda.synchronize()
+    out = torch.empty_like(q)
+    _replay_matches(lambda: pool.prefill(0, q, qs, w.max_query_len, t, c, w.max_context_len, w.scale, out=out),
+                    out, ref, torch.int16, "pa_prefill")
