@@ -1,6 +1,7 @@
-"""Decode and prefill calls captured in a HIP graph (torch.cuda.CUDAGraph) and replayed,
-through the C ABI: the plan resets its work counter on every launch and no
-call records a memset, so each replay must equal the eager call bit for bit.
+"""Decode and prefill calls captured in a HIP graph (torch.cuda.CUDAGraph)
+and replayed, through the C ABI: the plan resets its work counter on every
+launch and no call records a memset, so each replay must equal the eager call
+bit for bit.
 
 Each graph is replayed three times with eager work in between (the output
 overwritten, the stream synchronised), and every replay is checked.  Cases:
