@@ -34,6 +34,9 @@ SOURCES = [
 # pair (measured on MI355X: 1-1.5% per prefill call).
 EXTRA = {
     "prefill.hip": ["-mno-amdgpu-ieee", "-fno-honor-nans"],
+    # the machine scheduler that favours instruction-level parallelism: the
+    # shared-prefix decode 1-2% faster, the other decode batches unchanged
+    "decode.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"],
 }
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
