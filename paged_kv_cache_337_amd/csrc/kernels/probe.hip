@@ -93,7 +93,7 @@ __global__ __launch_bounds__(kProbeThreads) void probe_lds_kernel(const uint4* _
                                          (__attribute__((address_space(3))) void*)&ring[wl][u][64 * j], 16, 0,
                                          kForm == 4 ? kPolicyNT : 0);
     }
-    __builtin_amdgcn_s_waitcnt(0);  // every load of this round in LDS
+    __builtin_amdgcn_s_waitcnt(0);  // every load of this pass in LDS
 #pragma unroll
     for (int u = 0; u < kInFlight; ++u) acc ^= ring[wl][u][lane].x;
   }
