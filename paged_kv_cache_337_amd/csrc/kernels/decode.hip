@@ -9,10 +9,11 @@
 // FlashAttention) so K/V are read exactly once.
 //
 // Launch sequence of one pa_decode call:
-//   1. plan_kernel (one workgroup) cuts every context into work items of P
-//      tokens (P chosen from the total work when the caller asks for
-//      automatic partitioning; with many small explicit partitions an item is
-//      four consecutive partitions, one per wave) and writes the list of
+//   1. plan_kernel (one workgroup; plan_share_kernel when the pool holds
+//      shared blocks) cuts every context into work items of P tokens (P
+//      chosen from the total work when the caller asks for automatic
+//      partitioning; with many small explicit partitions an item is four
+//      consecutive partitions, one per wave) and writes the list of
 //      (sequence, item, context) records, full items first and the partial
 //      ones by decreasing size, so the tail of the decode consists of the
 //      smallest items.  Small batches whose contexts all fit one partition
@@ -24,7 +25,9 @@
 //      load), query rows and block ids, and it issues the next item's first
 //      K/V loads before merging the current item's four wave states.  For
 //      the few long items of an automatic partition size it takes one index
-//      at a time, which balances the end of the queue better.
+//      at a time, which balances the end of the queue better.  The sharing
+//      plan's items (a prefix several forked sequences share, read once for
+//      all of them) run two workgroups per CU.
 //   3. merge_kernel combines the partition states of multi-partition
 //      sequences by log-sum-exp weighting, one wave per (sequence, query head).
 //      (Merging inside the decode kernel, by the workgroup that finishes a
