@@ -394,3 +394,11 @@ def test_host_share_plan_argument_checks():
     pool.seq_fork(s)
     plan = pool.batch_share_plan([s, s + 1], 4)
     assert _decode_plan(plan, 2) == [([0, 1], 288)]
+    # a swapped-out sequence has no device blocks to share
+    pool.host_tier_init(64)
+    pool.seq_swap_out(s + 1)
+    with pytest.raises(pa.PAError) as e:
+        pool.batch_share_plan([s, s + 1], 4)
+    assert e.value.status == "INVALID_ARG"
+    pool.seq_swap_in(s + 1)  # back in blocks of its own: nothing shared any more
+    assert _decode_plan(pool.batch_share_plan([s, s + 1], 4), 2) == []
